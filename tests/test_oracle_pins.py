@@ -1,0 +1,364 @@
+"""Pins of the fp64 oracle against facts other than itself (CPU only).
+
+Each test ties one oracle step to something the pages or mathematics fix:
+  * SimHash agreement 1 - theta/pi (page "MagicPIG: LSH Sampling for
+    Efficient LLM Generation", background section; page "MagicPIG: don't pick
+    the tallest", section 5) -- Monte Carlo;
+  * u_i, the chance of colliding in at least 2 of L tables (same pages,
+    method details / section 5) -- brute-force enumeration over tables, exact
+    rational binomial tails, closed-form corners, Monte Carlo over seeds;
+  * the estimator reduces to exact softmax attention when every key is sampled
+    with one constant u -- torch float64 softmax;
+  * convergence to exact attention as L grows;
+  * set-inclusion semantics (page "MagicPIG: don't pick the tallest", sec. 5):
+    Horvitz-Thompson unbiasedness of both sums of the ratio;
+  * centering leaves the output unchanged, and without it the sampled set
+    collapses (same page, section 5; method details of the summary page);
+  * the fraction of projections inside the 1e-5 band against its closed form;
+  * integer steps against numpy brute force.
+"""
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+THETAS = [0.0, math.pi / 6, math.pi / 3, math.pi / 2, 2 * math.pi / 3, 5 * math.pi / 6,
+          math.pi - 0.01]
+
+
+# ---------------------------------------------------------------- RNG
+def test_splitmix64_reference_stream():
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "splitmix64_seed1234567.json")))
+    got = [oracle.splitmix64(g["seed"], k) for k in range(1, 6)]
+    assert got == g["outputs"]
+
+
+def test_hyperplanes_standard_normal_and_row_indexed():
+    from scipy import stats
+    W = oracle.hyperplanes(seed=5, R=8192, d=128).astype(np.float64).ravel()
+    N = W.size
+    assert abs(W.mean()) < 5.0 / math.sqrt(N)
+    assert abs(W.var() - 1.0) < 5.0 * math.sqrt(2.0 / N)
+    assert abs(stats.kurtosis(W, fisher=False) - 3.0) < 5.0 * math.sqrt(24.0 / N)
+    assert stats.kstest(W, "norm").pvalue > 1e-4
+    # a row block generated on its own equals the same rows of a longer matrix
+    full = oracle.hyperplanes(seed=9, R=40, d=16)
+    part = oracle.hyperplanes(seed=9, R=10, d=16, row0=25)
+    assert np.array_equal(full[25:35], part)
+    # different seeds give different streams
+    assert not np.array_equal(full, oracle.hyperplanes(seed=10, R=40, d=16))
+
+
+# ---------------------------------------------------------------- SimHash
+@pytest.mark.parametrize("d,R", [(2, 10**6), (16, 10**6), (128, 4 * 10**5)])
+def test_simhash_agreement_is_one_minus_theta_over_pi(d, R):
+    rng = np.random.default_rng(100 + d)
+    Q, _ = np.linalg.qr(rng.standard_normal((d, 2)))
+    e1, e2 = Q[:, 0], Q[:, 1]
+    ys = [math.cos(t) * e1 + math.sin(t) * e2 for t in THETAS]
+    agree = np.zeros(len(THETAS))
+    chunk = 100_000
+    for r0 in range(0, R, chunk):
+        W = oracle.hyperplanes(seed=777 + d, R=min(chunk, R - r0), d=d, row0=r0)
+        bx, _ = oracle.project_signs(1.7 * e1, W)
+        for t, y in enumerate(ys):
+            by, _ = oracle.project_signs(y, W)
+            agree[t] += np.count_nonzero(bx == by)
+    for t, theta in enumerate(THETAS):
+        p = 1.0 - theta / math.pi
+        sigma = math.sqrt(max(p * (1 - p), 1e-12) / R)
+        assert abs(agree[t] / R - p) <= 5 * sigma + 1e-12, (d, theta, agree[t] / R, p)
+
+
+def test_project_signs_on_basis_vectors():
+    """x = e_c projects onto column c of W: bit j is [W[j][c] > 0]."""
+    W = oracle.hyperplanes(seed=3, R=60, d=16)
+    for c in (0, 7, 15):
+        x = np.zeros(16)
+        x[c] = 2.5
+        bits, band = oracle.project_signs(x, W)
+        assert np.array_equal(bits, (W[:, c] > 0).astype(np.uint8))
+        assert not band.any()
+    # a zero vector projects to 0 everywhere: sign(0) = 0 (strict inequality)
+    bits, _ = oracle.project_signs(np.zeros(16), W)
+    assert not bits.any()
+
+
+def test_pack_codes_lsb_first():
+    assert list(oracle.pack_codes([1, 0, 1, 1, 0, 0, 0, 1], 4, 2)) == [13, 8]
+    assert list(oracle.pack_codes([], 0, 3)) == [0, 0, 0]       # K = 0: one bucket
+
+
+# ---------------------------------------------------------------- u_i
+def _brute_u(P, L):
+    """Sum over all 2^L hit patterns of the L tables with >= 2 hits."""
+    pats = np.arange(2 ** L, dtype=np.int64)
+    hits = np.zeros_like(pats)
+    for b in range(L):
+        hits += (pats >> b) & 1
+    probs = np.power(P, hits.astype(np.float64)) * np.power(1.0 - P, (L - hits).astype(np.float64))
+    return math.fsum(probs[hits >= 2].tolist())
+
+
+def test_u_matches_enumeration_over_tables():
+    seen_small = seen_large = False
+    for p in (0.05, 0.2, 0.5, 0.73, 0.9, 0.99):
+        for K in (1, 2, 4, 10):
+            for L in (2, 3, 5, 8, 16):
+                P = p ** K
+                ref = _brute_u(P, L)
+                got = oracle.u(p, K, L)
+                if L * P > 0.05:
+                    seen_large = True
+                else:
+                    seen_small = True
+                assert abs(got - ref) <= 1e-13 * ref, (p, K, L, got, ref)
+    assert seen_small and seen_large       # both arithmetic branches exercised
+
+
+@pytest.mark.parametrize("p,K,L", [(Fraction(3, 10), 10, 150), (Fraction(1, 2), 10, 150),
+                                   (Fraction(7, 10), 9, 120), (Fraction(9, 10), 9, 240),
+                                   (Fraction(1, 10), 4, 16), (Fraction(2, 5), 9, 60),
+                                   (Fraction(99, 100), 10, 150)])
+def test_u_matches_exact_rational_binomial_tail(p, K, L):
+    P = p ** K
+    tail = sum(Fraction(math.comb(L, j)) * P ** j * (1 - P) ** (L - j) for j in range(2, L + 1))
+    ref = float(tail)
+    assert abs(oracle.u(float(p), K, L) - ref) <= 1e-13 * ref
+    assert abs(oracle.log_u(float(p), K, L) - math.log(ref)) <= 1e-12 * max(1.0, abs(math.log(ref)))
+
+
+def test_u_corner_cases():
+    for p in (0.1, 0.5, 0.8):
+        assert oracle.u(p, 1, 2) == pytest.approx(p * p, rel=1e-15)
+        assert oracle.u(p, 3, 2) == pytest.approx(p ** 6, rel=1e-14)
+    assert oracle.u(1.0, 10, 150) == 1.0
+    assert oracle.u(0.3, 0, 16) == 1.0       # K = 0: every table collides
+    assert oracle.u(0.0, 10, 150) == 0.0
+    assert oracle.u(0.5, 4, 100_000) == pytest.approx(1.0, abs=1e-12)
+    # u grows with p and with L
+    ps = np.linspace(0.01, 0.99, 50)
+    us = [oracle.u(p, 10, 150) for p in ps]
+    assert all(a < b or (a == b == 1.0) for a, b in zip(us, us[1:]))   # saturates at 1.0
+    assert oracle.u(0.6, 10, 60) < oracle.u(0.6, 10, 120) < oracle.u(0.6, 10, 240)
+
+
+def test_u_monte_carlo_over_seeds():
+    """A fixed pair at angle pi/3 collides in >= 2 of L tables with frequency u."""
+    d, K, L, R = 16, 3, 6, 20000
+    rng = np.random.default_rng(7)
+    Q, _ = np.linalg.qr(rng.standard_normal((d, 2)))
+    x = Q[:, 0]
+    y = math.cos(math.pi / 3) * Q[:, 0] + math.sin(math.pi / 3) * Q[:, 1]
+    hit = 0
+    for s in range(R):
+        W = oracle.hyperplanes(seed=50_000 + s, R=K * L, d=d)
+        cx, _ = oracle.encode(x, W, K, L)
+        cy, _ = oracle.encode(y, W, K, L)
+        hit += int(np.count_nonzero(cx == cy) >= 2)
+    u = oracle.u(oracle.collision_p(x, y), K, L)
+    assert oracle.collision_p(x, y) == pytest.approx(2.0 / 3.0, rel=1e-12)
+    assert abs(hit / R - u) <= 5 * math.sqrt(u * (1 - u) / R)
+
+
+# ---------------------------------------------------------------- estimator
+def _tiny_inputs(seed):
+    cfg = synth.CONFIGS["tiny"]
+    inp = synth.config_inputs(cfg, layer=seed)
+    k = inp["k"][0, 0].double().numpy()
+    v = inp["v"][0, 0].double().numpy()
+    q = inp["q"][0, 0].double().numpy()
+    return k, v, q
+
+
+def _softmax_attention_torch(q, k, v, rows=None):
+    kt, vt, qt = torch.from_numpy(k), torch.from_numpy(v), torch.from_numpy(q)
+    if rows is not None:
+        kt, vt = kt[rows], vt[rows]
+    w = torch.softmax(kt @ qt / math.sqrt(k.shape[1]), dim=0)
+    return (w @ vt).numpy()
+
+
+def test_all_sampled_with_constant_u_is_exact_softmax():
+    k, v, q = _tiny_inputs(3)
+    ref = _softmax_attention_torch(q, k, v)
+    # K = 0: every key shares the query's (single) bucket in all L tables, so
+    # S = all keys outside T, and u = 1.
+    W = oracle.hyperplanes(seed=3, R=0, d=128)
+    res = oracle.decode_unit(q[None], k, v, W, K=0, L=16, n_sink=1, n_local=16)
+    assert len(res["S"][0]) == 1024 - 17
+    assert np.max(np.abs(res["out"][0] - ref)) <= 1e-12 * np.max(np.abs(ref))
+    # with no exact set and every key in S, any constant log u cancels in the ratio
+    mu = oracle.mean(k)
+    S = np.arange(1024, dtype=np.int32)
+    out = oracle.estimate(q, k, v, mu, S, 4, 16, 0, 0, flags=oracle.CONST_LOG_U,
+                          const_log_u=-3.7)
+    assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))
+    # ...whereas the real, key-dependent u does not cancel
+    out_u = oracle.estimate(q, k, v, mu, S, 4, 16, 0, 0)
+    assert np.max(np.abs(out_u - ref)) > 1e-3 * np.max(np.abs(ref))
+    # only T (S empty) is exact attention over T; nothing at all gives 0
+    T = list(range(1)) + list(range(1024 - 16, 1024))
+    out_t = oracle.estimate(q, k, v, mu, np.zeros(0, np.int32), 4, 16, 1, 16)
+    assert np.allclose(out_t, _softmax_attention_torch(q, k, v, T), rtol=0, atol=1e-13)
+    assert not oracle.estimate(q, k, v, mu, np.zeros(0, np.int32), 4, 16, 0, 0).any()
+
+
+def test_estimator_converges_in_L():
+    Ls = [4, 16, 64, 256]
+    errs = {L: [] for L in Ls}
+    frac = {L: [] for L in Ls}
+    for s in range(12):
+        k, v, q = _tiny_inputs(s)
+        o = _softmax_attention_torch(q, k, v)
+        K, Lm = 4, Ls[-1]
+        W = oracle.hyperplanes(seed=1000 + s, R=K * Lm, d=128)
+        mu = oracle.mean(k)
+        codes, _ = oracle.encode_keys_parallel(k, W, K, Lm, mu)
+        qc, _ = oracle.encode(q, W, K, Lm)
+        prev = None
+        for L in Ls:
+            # W of L tables is the row prefix of W of Lm tables
+            counts = oracle.collision_counts(codes[:L], qc[:L])
+            S = oracle.select(counts, 1, 16)
+            if prev is not None:
+                assert set(prev) <= set(S)          # nested tables => nested sets
+            prev = S
+            oh = oracle.estimate(q, k, v, mu, S, K, L, 1, 16)
+            errs[L].append(np.linalg.norm(oh - o) / np.linalg.norm(o))
+            frac[L].append(len(S) / (1024 - 17))
+    means = [np.mean(errs[L]) for L in Ls]
+    for a, b in zip(means, means[1:]):
+        assert b < 0.6 * a, means
+    assert np.mean(frac[256]) > 0.99
+    assert means[-1] < 0.05
+
+
+def test_horvitz_thompson_inclusion_and_sums():
+    """Set-inclusion semantics: E[1{i in S}] = u_i, and the estimator's two sums
+    sum_S w_i v_i / u_i and sum_S w_i / u_i are unbiased for the sums over all
+    keys outside T (w_i = exp(q.k_i/sqrt(d))).
+
+    The sums are read back out of ``estimate`` itself: the one exact key (the
+    sink, in T) carries value e_0 and every other key has 0 in coordinate 0,
+    so out[0] = w_T / (D_S + w_T) and out[1:] = N_S / (D_S + w_T)."""
+    rng = np.random.default_rng(11)
+    n, d, K, L = 12, 8, 2, 4
+    k = rng.standard_normal((n, d))
+    vals = rng.standard_normal((n, 3))
+    q = rng.standard_normal(d)
+    n_sink, n_local = 1, 0
+    v = np.zeros((n, d))
+    v[0, 0] = 1.0
+    v[1:, 1:4] = vals[1:]
+    mu = oracle.mean(k)
+    x = k - mu
+    uvec = np.array([oracle.u(oracle.collision_p(q, x[i]), K, L) for i in range(n)])
+    wt = np.exp(k @ q / math.sqrt(d))
+    R = 10000
+    inc = np.zeros(n)
+    num = np.zeros((R, 3))
+    den = np.zeros(R)
+    size = np.zeros(R)
+    for s in range(R):
+        W = oracle.hyperplanes(seed=9_000_000 + s, R=K * L, d=d)
+        codes, _ = oracle.encode_keys(k, W, K, L, mu)
+        qc, _ = oracle.encode(q, W, K, L)
+        S = oracle.select(oracle.collision_counts(codes, qc), n_sink, n_local)
+        inc[S] += 1
+        size[s] = len(S)
+        out = oracle.estimate(q, k, v, mu, S, K, L, n_sink, n_local)
+        total = wt[0] / out[0]
+        den[s] = total - wt[0]
+        num[s] = out[1:4] * total
+    mid = np.arange(n_sink, n - n_local)
+    assert inc[0] == 0
+    f = inc[mid] / R
+    sig = np.sqrt(uvec[mid] * (1 - uvec[mid]) / R)
+    assert np.all(np.abs(f - uvec[mid]) <= 4.5 * sig), (f, uvec[mid])
+    assert abs(size.mean() - uvec[mid].sum()) <= 4.5 * size.std() / math.sqrt(R)
+    true_num = (wt[mid, None] * vals[mid]).sum(0)
+    assert np.all(np.abs(num.mean(0) - true_num) <= 4.5 * num.std(0) / math.sqrt(R)), \
+        (num.mean(0), true_num)
+    assert abs(den.mean() - wt[mid].sum()) <= 4.5 * den.std() / math.sqrt(R), \
+        (den.mean(), wt[mid].sum())
+    assert 0.02 < uvec[mid].min() and uvec[mid].max() < 0.98   # probabilities genuinely vary
+
+
+def test_centering_is_score_invariant_and_needed():
+    k, v, q = _tiny_inputs(5)
+    K, L = 4, 16
+    W = oracle.hyperplanes(seed=5, R=K * L, d=128)
+    mu = oracle.mean(k)
+    codes, _ = oracle.encode_keys(k, W, K, L, mu)
+    qc, _ = oracle.encode(q, W, K, L)
+    S = oracle.select(oracle.collision_counts(codes, qc), 1, 16)
+    a = oracle.estimate(q, k, v, mu, S, K, L, 1, 16)
+    b = oracle.estimate(q, k, v, mu, S, K, L, 1, 16, flags=oracle.SCORE_CENTERED)
+    assert np.max(np.abs(a - b)) <= 1e-12 * np.max(np.abs(a))
+    assert len(S) / 1007 > 0.15
+    # without centering the keys sit in a cone facing away from q: almost no
+    # key collides in two tables
+    fr = []
+    for s in range(4):
+        k, v, q = _tiny_inputs(20 + s)
+        W = oracle.hyperplanes(seed=20 + s, R=K * L, d=128)
+        codes, _ = oracle.encode_keys(k, W, K, L, None)
+        qc, _ = oracle.encode(q, W, K, L)
+        fr.append(len(oracle.select(oracle.collision_counts(codes, qc), 1, 16)) / 1007)
+    assert np.mean(fr) < 1e-3
+
+
+def test_mean_matches_exact_column_sums():
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((3000, 7)) * 5 + 1
+    mu = oracle.mean(k)
+    for c in range(7):
+        assert mu[c] == pytest.approx(math.fsum(k[:, c].tolist()) / 3000, rel=1e-14, abs=1e-15)
+
+
+@pytest.mark.slow
+def test_band_fraction_matches_closed_form():
+    """Fraction of |w.x| < 1e-5 |w||x| over random hyperplanes: P(|cos| < eps)
+    for a uniformly random direction in d dimensions = I_{eps^2}(1/2, (d-1)/2)."""
+    from scipy.special import betainc
+    cfg = synth.CONFIGS["llama8b_16k"]
+    inp = synth.cone_inputs(B=1, H_q=4, H_kv=1, n=4096, d=128, dtype=torch.bfloat16, seeds=[42])
+    k = inp["k"][0, 0].double().numpy()
+    W = oracle.hyperplanes(seed=42, R=cfg.K * cfg.L, d=128)
+    mu = oracle.mean(k)
+    _, nb = oracle.encode_keys_parallel(k, W, cfg.K, cfg.L, mu)
+    N = k.shape[0] * cfg.K * cfg.L
+    p = betainc(0.5, 63.5, 1e-10)
+    assert p == pytest.approx(8.97e-5, rel=2e-3)
+    assert abs(nb - N * p) <= 3 * math.sqrt(N * p), (nb, N * p)
+
+
+# ---------------------------------------------------------------- integer steps
+@pytest.mark.parametrize("n_sink,n_local", [(0, 0), (4, 64), (1, 16), (300, 250), (600, 0),
+                                            (0, 900), (10, 10)])
+def test_counts_and_select_brute_force(n_sink, n_local):
+    rng = np.random.default_rng(n_sink * 1000 + n_local)
+    L, n = 7, 500
+    codes = rng.integers(0, 4, size=(L, n)).astype(np.uint16)
+    qc = rng.integers(0, 4, size=L).astype(np.uint16)
+    counts = oracle.collision_counts(codes, qc)
+    ref = np.array([sum(int(codes[l, i] == qc[l]) for l in range(L)) for i in range(n)])
+    assert np.array_equal(counts, ref)
+    S = oracle.select(counts, n_sink, n_local)
+    refS = [i for i in range(n) if ref[i] >= 2 and not (i < n_sink or i >= n - n_local)]
+    assert S.tolist() == refS
+
+
+def test_estimate_rejects_out_of_range_index():
+    k, v, q = _tiny_inputs(1)
+    with pytest.raises(ValueError):
+        oracle.estimate(q, k, v, oracle.mean(k), np.array([5, 4000], np.int32), 4, 16, 1, 16)
