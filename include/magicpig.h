@@ -1,0 +1,168 @@
+/*
+ * magicpig.h -- C ABI of the MI355X (gfx950) MagicPIG decode-attention library.
+ *
+ * What it computes.  MagicPIG estimates one decode step of softmax attention
+ * by locality-sensitive-hash sampling:
+ *   - keys are centered by their mean and SimHash-encoded into L tables of K
+ *     sign bits each (page "MagicPIG: LSH Sampling for Efficient LLM
+ *     Generation", method details: the K x L random projections and the
+ *     centering step; page "MagicPIG: don't pick the tallest", section 5);
+ *   - a query samples every key that shares its bucket in at least two tables;
+ *   - each sampled key i is weighted by exp(q.k_i/sqrt(d) - log u_i), where
+ *     u_i = 1 - (1-p_i^K)^L - L p_i^K (1-p_i^K)^(L-1) and
+ *     p_i = 1 - arccos(cos(q, k_i - mu))/pi (the summary page's quick-read
+ *     equations and its algorithm steps);
+ *   - the sink and local tokens T are attended exactly (u = 1), and one
+ *     softmax over [sampled, exact] gives the output (system co-design
+ *     section: on-device cache of sink/local tokens merged with the sampled
+ *     part).
+ * The two calls follow the pages' problem statement (background section):
+ * build the index once per key cache, then estimate o = softmax(qK^T/sqrt d)V
+ * from a sampled subset per decode step.
+ *
+ * Conventions for every call:
+ *   - every tensor pointer is a DEVICE pointer (HBM of the current HIP device);
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream); all
+ *     work is enqueued on it asynchronously and nothing here synchronises;
+ *   - the library never allocates device memory: the caller owns keys, values,
+ *     queries, outputs, the index workspace and the decode scratch;
+ *   - arguments are validated on the host before anything is enqueued; on any
+ *     status other than MP_OK nothing has been enqueued (except MP_E_HIP, which
+ *     reports a failed launch), and mp_last_error() describes the problem;
+ *   - device faults surface at the caller's next synchronisation of the stream;
+ *   - head dimension d must be 128.
+ *
+ * Fixed readings (where the pages leave a choice open):
+ *   - hyperplanes: W is [R][128] fp32 row-major, R = K*L, row j = l*K + b is
+ *     bit b of table l.  Element e = j*128 + c is the Box-Muller standard normal
+ *     sqrt(-2 ln u1) cos(2 pi u2) (computed in fp64, rounded to fp32) of
+ *     u1 = ((z1 >> 11) + 1) 2^-53 and u2 = (z2 >> 11) 2^-53, where z1, z2 are
+ *     the outputs number 2e+1 and 2e+2 of SplitMix64 (Steele, Lea & Flood 2014)
+ *     started at `seed`.  A smaller L therefore uses a row prefix of W.
+ *   - sign bit = 1 iff projection > 0; code of table l packs bit b at 2^b.
+ *   - queries are hashed raw; keys are hashed after subtracting the mean of
+ *     all n keys of their (sequence, KV head), sink and local tokens included.
+ *   - the cosine in p_i uses the centered key; scores use the raw key.
+ *   - T = [0, n_sink) u [n - n_local, n); sampled sets exclude T.
+ *   - query head h of a sequence uses KV head h / G, G = H_q / H_kv.
+ *   - a zero-length query or centered key has cosine 0.
+ */
+#ifndef MAGICPIG_H
+#define MAGICPIG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mp_status {
+    MP_OK = 0,
+    MP_E_ARG = 1,        /* null pointer, value out of range */
+    MP_E_SHAPE = 2,      /* shapes/strides disagree or are unsupported */
+    MP_E_DTYPE = 3,      /* unsupported dtype */
+    MP_E_WORKSPACE = 4,  /* workspace/scratch too small or misaligned */
+    MP_E_HIP = 5,        /* a HIP call or kernel launch failed */
+    MP_E_HANDLE = 6      /* index handle is NULL or not a live index */
+} mp_status;
+
+typedef enum mp_dtype { MP_F32 = 0, MP_BF16 = 1 } mp_dtype;
+
+/* A [B][H][n][d] key or value tensor.  Strides are in elements; the d axis is
+ * contiguous.  `data` and every row start must be 16-byte aligned. */
+typedef struct mp_kv_view {
+    const void *data;
+    int32_t dtype;               /* mp_dtype */
+    int32_t B, H, n, d;
+    int64_t stride_b, stride_h, stride_n;
+} mp_kv_view;
+
+/* Opaque host handle of a built index; it points into the caller's workspace. */
+typedef struct mp_index mp_index;
+
+/* Keys per chunk of the code layout (see mp_index_views). */
+#define MP_CHUNK 512
+
+/* Bytes of device workspace mp_build_index needs for these sizes; 0 if the
+ * sizes are invalid (B, H_kv, n >= 1; d == 128; 0 <= K <= 16; 2 <= L <= 255). */
+size_t mp_index_workspace_bytes(int32_t B, int32_t H_kv, int32_t n, int32_t d,
+                                int32_t K, int32_t L);
+
+/* Build the index of `keys` ([B][H_kv][n][128], fp32 or bf16): hyperplanes W
+ * from `seed`, per-(sequence, KV head) mean mu, and the codes of every key.
+ * The index holds W, mu and the codes only; keys and values are not copied,
+ * and decode reads them again through its own views.  The workspace
+ * (>= mp_index_workspace_bytes, 256-byte aligned) must stay alive and
+ * unmodified while the index is used.  *out receives a host handle (free it
+ * with mp_index_destroy).  Ownership of `keys` stays with the caller; the
+ * keys must not change until the enqueued build has run. */
+mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t seed,
+                         void *workspace, size_t workspace_bytes, void *stream,
+                         mp_index **out);
+
+/* Bytes of device scratch one mp_decode_attn / mp_decode_debug call needs
+ * for H_q query heads per sequence; 0 if invalid. */
+size_t mp_decode_scratch_bytes(const mp_index *idx, int32_t H_q);
+
+/* One decode step for every (sequence, query head).
+ *   q      [B][H_q][128] fp32, contiguous; H_q = G * H_kv with G in {1,2,4,8}
+ *   k, v   the key and value caches the index was built from: [B][H_kv][n][128],
+ *          same dtype (fp32 or bf16)
+ *   n_sink, n_local >= 0   the exact set T
+ *   scale  score scale; 0 means 1/sqrt(128)
+ *   out    [B][H_q][128] fp32, contiguous
+ *   scratch >= mp_decode_scratch_bytes(idx, H_q), 256-byte aligned; calls that
+ *          share one scratch buffer must be ordered on one stream.
+ * Several decodes may read one index concurrently. */
+mp_status mp_decode_attn(const float *q, int32_t H_q, const mp_index *idx,
+                         const mp_kv_view *k, const mp_kv_view *v,
+                         int32_t n_sink, int32_t n_local, float scale, float *out,
+                         void *scratch, size_t scratch_bytes, void *stream);
+
+/* mp_decode_attn plus the intermediate results, each optional (NULL = skip):
+ *   qcodes [B][H_q][L] uint16     query codes
+ *   counts [B][H_q][n] uint8      tables in which key i shares the query's bucket
+ *   s_idx  [B][H_q][n] int32      sampled set S (ascending; T excluded), padded
+ *   s_len  [B][H_q]    int32      |S|
+ * The output equals what mp_decode_attn computes. */
+mp_status mp_decode_debug(const float *q, int32_t H_q, const mp_index *idx,
+                          const mp_kv_view *k, const mp_kv_view *v,
+                          int32_t n_sink, int32_t n_local, float scale, float *out,
+                          void *scratch, size_t scratch_bytes, void *stream,
+                          uint16_t *qcodes, uint8_t *counts, int32_t *s_idx, int32_t *s_len);
+
+/* mp_decode_attn that also records two caller-created hipEvent_t (passed as
+ * void*, either may be NULL) on `stream` right before and right after the
+ * fused collision-scan + gather kernel, so the caller can time that kernel on
+ * its own.  Used by the benchmark; the output is that of mp_decode_attn. */
+mp_status mp_decode_attn_timed(const float *q, int32_t H_q, const mp_index *idx,
+                               const mp_kv_view *k, const mp_kv_view *v,
+                               int32_t n_sink, int32_t n_local, float scale, float *out,
+                               void *scratch, size_t scratch_bytes, void *stream,
+                               void *ev_scan_begin, void *ev_scan_end);
+
+/* Device pointers into the index workspace (valid while the workspace is):
+ *   W     [R][128] fp32, R = K*L
+ *   mu    [B][H_kv][128] fp32
+ *   codes [B][H_kv][n_pad/MP_CHUNK][L][MP_CHUNK] uint16: the code of table l
+ *         for key i = c*MP_CHUNK + j is at ((bh*nc + c)*L + l)*MP_CHUNK + j;
+ *         keys i >= n are padding and never sampled.
+ * Any output pointer may be NULL. */
+mp_status mp_index_views(const mp_index *idx, const float **W, const float **mu,
+                         const uint16_t **codes, int32_t *n_pad);
+
+/* Free the host handle (not the workspace).  NULL is ignored. */
+void mp_index_destroy(mp_index *idx);
+
+/* Static description of a status code. */
+const char *mp_status_str(mp_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *mp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAGICPIG_H */

@@ -1,0 +1,134 @@
+"""MI355X-native MagicPIG decode attention (LSH-sampled sparse attention).
+
+PyTorch supplies device memory and streams; every step of the path runs in the
+HIP kernels of ``libmagicpig.so`` behind the C ABI in ``include/magicpig.h``.
+This module only marshals tensors into that ABI (see ``capi`` for the
+one-to-one ctypes binding).
+
+    idx = build_index(keys, K=10, L=150, seed=2000)          # keys [B][H_kv][n][128]
+    out = decode_attn(q, idx, keys, values, n_sink=4, n_local=64)   # q [B][H_q][128] fp32
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import capi
+from .capi import MPError, MP_CHUNK
+
+__all__ = ["MagicPIGIndex", "build_index", "decode_attn", "decode_debug", "kv_view", "capi",
+           "MPError", "MP_CHUNK"]
+
+_DTYPES = {torch.float32: capi.MP_F32, torch.bfloat16: capi.MP_BF16}
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def kv_view(t: torch.Tensor) -> capi.mp_kv_view:
+    """mp_kv_view of a [B][H][n][128] device tensor (fp32 or bf16, last dim contiguous)."""
+    if t.dim() != 4:
+        raise ValueError("expected a [B][H][n][d] tensor")
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if t.stride(3) != 1:
+        raise ValueError("the d axis must be contiguous")
+    B, H, n, d = t.shape
+    return capi.mp_kv_view(t.data_ptr(), _DTYPES[t.dtype], B, H, n, d, t.stride(0), t.stride(1),
+                           t.stride(2))
+
+
+class MagicPIGIndex:
+    """A built index: the host handle plus the device workspace that holds
+    W, mu and the key codes."""
+
+    def __init__(self, handle: int, workspace: torch.Tensor, keys_shape, K: int, L: int,
+                 seed: int, dtype):
+        self.handle = handle
+        self.workspace = workspace
+        self.B, self.H_kv, self.n, self.d = keys_shape
+        self.K, self.L, self.seed, self.dtype = K, L, seed, dtype
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            self.handle = None
+            try:
+                capi.mp_index_destroy(h)
+            except Exception:          # interpreter teardown: module globals already gone
+                pass
+
+    def _slice(self, ptr, numel, dtype):
+        base = self.workspace.data_ptr()
+        off = ptr - base
+        esz = torch.empty(0, dtype=dtype).element_size()
+        return self.workspace[off:off + numel * esz].view(dtype)
+
+    def views(self):
+        """Device tensors aliasing the workspace: W [R][128] fp32, mu [B][H_kv][128]
+        fp32 and codes [B][H_kv][n_pad/512][L][512] uint16 (as int16 storage)."""
+        W, mu, codes, n_pad = capi.mp_index_views(self.handle)
+        R = self.K * self.L
+        Wt = self._slice(W, R * 128, torch.float32).view(R, 128)
+        mut = self._slice(mu, self.B * self.H_kv * 128, torch.float32).view(self.B, self.H_kv, 128)
+        nc = n_pad // MP_CHUNK
+        ct = self._slice(codes, self.B * self.H_kv * nc * self.L * MP_CHUNK, torch.int16)
+        return Wt, mut, ct.view(self.B, self.H_kv, nc, self.L, MP_CHUNK)
+
+    def scratch_bytes(self, H_q: int) -> int:
+        return capi.mp_decode_scratch_bytes(self.handle, H_q)
+
+
+def build_index(keys: torch.Tensor, K: int, L: int, seed: int, stream=None) -> MagicPIGIndex:
+    view = kv_view(keys)
+    nbytes = capi.mp_index_workspace_bytes(view.B, view.H, view.n, view.d, K, L)
+    if nbytes == 0:
+        raise ValueError(f"invalid index sizes B={view.B} H={view.H} n={view.n} d={view.d} "
+                         f"K={K} L={L}")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=keys.device)
+    h = capi.mp_build_index(view, K, L, seed, ws.data_ptr(), nbytes, _stream(stream))
+    return MagicPIGIndex(h, ws, tuple(keys.shape), K, L, seed, keys.dtype)
+
+
+def _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, debug):
+    if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3:
+        raise ValueError("q must be a contiguous [B][H_q][128] float32 tensor")
+    B, H_q, d = q.shape
+    if out is None:
+        out = torch.empty(B, H_q, d, dtype=torch.float32, device=q.device)
+    need = index.scratch_bytes(H_q)
+    if need == 0:
+        raise ValueError(f"H_q={H_q} does not fit the index (H_kv={index.H_kv})")
+    if scratch is None:
+        scratch = torch.empty(need, dtype=torch.uint8, device=q.device)
+    kv_k, kv_v = kv_view(k), kv_view(v)
+    s = _stream(stream)
+    if not debug:
+        capi.mp_decode_attn(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local,
+                            float(scale), out.data_ptr(), scratch.data_ptr(), scratch.numel(), s)
+        return out
+    n = index.n
+    qcodes = torch.empty(B, H_q, index.L, dtype=torch.int16, device=q.device)
+    counts = torch.empty(B, H_q, n, dtype=torch.uint8, device=q.device)
+    s_idx = torch.empty(B, H_q, n, dtype=torch.int32, device=q.device)
+    s_len = torch.empty(B, H_q, dtype=torch.int32, device=q.device)
+    capi.mp_decode_debug(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local,
+                         float(scale), out.data_ptr(), scratch.data_ptr(), scratch.numel(), s,
+                         qcodes.data_ptr(), counts.data_ptr(), s_idx.data_ptr(), s_len.data_ptr())
+    return dict(out=out, qcodes=qcodes, counts=counts, s_idx=s_idx, s_len=s_len)
+
+
+def decode_attn(q, index, k, v, n_sink, n_local, scale=0.0, out=None, scratch=None, stream=None):
+    """One decode step: out [B][H_q][128] fp32 (see mp_decode_attn)."""
+    return _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, False)
+
+
+def decode_debug(q, index, k, v, n_sink, n_local, scale=0.0, out=None, scratch=None,
+                 stream=None):
+    """decode_attn plus qcodes, counts, s_idx, s_len (see mp_decode_debug)."""
+    return _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, True)

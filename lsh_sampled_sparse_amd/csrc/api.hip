@@ -1,0 +1,326 @@
+// api.hip -- the C ABI of libmagicpig: argument validation, workspace and
+// scratch layouts, and the launch sequence of index build and decode.
+// Every check runs on the host before anything is enqueued.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "mp_internal.h"
+
+struct mp_index : mp::mp_index_impl {};
+
+namespace mp {
+
+static thread_local char g_err[512] = "";
+
+static mp_status fail(mp_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t L)
+{
+    IndexLayout y{};
+    y.B = B;
+    y.H_kv = H_kv;
+    y.n = n;
+    y.n_chunks = ceil_div(n, kChunk);
+    y.n_pad = y.n_chunks * kChunk;
+    y.n_mean_blocks = ceil_div(n, kMeanRows);
+    y.K = K;
+    y.L = L;
+    y.R = K * L;
+    y.R_pad = y.R > 0 ? ceil_div(y.R, 16) * 16 : 16;
+    const int64_t BH = int64_t(B) * H_kv;
+    int64_t off = 0;
+    y.off_W = off;       off = align256(off + int64_t(y.R_pad) * kD * 4);
+    y.off_Wp = off;      off = align256(off + int64_t(y.R_pad) * kD * 4);
+    y.off_mu = off;      off = align256(off + BH * kD * 4);
+    y.off_mu_part = off; off = align256(off + BH * y.n_mean_blocks * kD * 8);
+    y.off_codes = off;   off = align256(off + BH * y.n_chunks * int64_t(L) * kChunk * 2);
+    y.total = off;
+    return y;
+}
+
+DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q)
+{
+    DecodeLayout y{};
+    y.BHq = lay.B * H_q;
+    y.n_chunks = lay.n_chunks;
+    const int64_t BHq = y.BHq;
+    int64_t off = 0;
+    y.off_qcodes = off;  off = align256(off + BHq * lay.L * 2);
+    y.off_qq = off;      off = align256(off + BHq * lay.L * 4);
+    y.off_qnorm = off;   off = align256(off + BHq * 4);
+    y.off_part = off;    off = align256(off + BHq * lay.n_chunks * int64_t(kD + 2) * 4);
+    y.off_seg_idx = off; off = align256(off + BHq * lay.n_chunks * int64_t(kChunk) * 4);
+    y.off_seg_cnt = off; off = align256(off + BHq * lay.n_chunks * 4);
+    y.total = off;
+    return y;
+}
+
+static bool sizes_ok(int32_t B, int32_t H, int32_t n, int32_t d, int32_t K, int32_t L)
+{
+    return B >= 1 && H >= 1 && n >= 1 && d == kD && K >= 0 && K <= 16 && L >= 2 && L <= 255 &&
+           int64_t(B) * H <= 65535;
+}
+
+static mp_status check_view(const mp_kv_view *v, const char *name)
+{
+    if (!v) return fail(MP_E_ARG, "%s: view is NULL", name);
+    if (!v->data) return fail(MP_E_ARG, "%s: data is NULL", name);
+    if (v->dtype != MP_F32 && v->dtype != MP_BF16)
+        return fail(MP_E_DTYPE, "%s: dtype %d is not MP_F32 or MP_BF16", name, v->dtype);
+    if (v->d != kD) return fail(MP_E_SHAPE, "%s: d = %d, only 128 is supported", name, v->d);
+    if (v->B < 1 || v->H < 1 || v->n < 1)
+        return fail(MP_E_SHAPE, "%s: B, H, n must be >= 1 (got %d, %d, %d)", name, v->B, v->H, v->n);
+    if (v->stride_b < 0 || v->stride_h < 0 || v->stride_n < kD)
+        return fail(MP_E_SHAPE, "%s: strides must be >= 0 and stride_n >= 128", name);
+    const int64_t elt = v->dtype == MP_F32 ? 4 : 2;
+    if ((reinterpret_cast<uintptr_t>(v->data) & 15) || (v->stride_b * elt) % 16 ||
+        (v->stride_h * elt) % 16 || (v->stride_n * elt) % 16)
+        return fail(MP_E_SHAPE, "%s: data and row strides must be 16-byte aligned", name);
+    return MP_OK;
+}
+
+static const mp_index *live(const mp_index *idx)
+{
+    return (idx && idx->magic == kMagic) ? idx : nullptr;
+}
+
+static mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx,
+                               const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
+                               int32_t n_local, float scale, float *out, void *scratch,
+                               size_t scratch_bytes, void *stream, bool debug, uint16_t *qcodes,
+                               uint8_t *counts, int32_t *s_idx, int32_t *s_len,
+                               void *ev_begin = nullptr, void *ev_end = nullptr)
+{
+    g_err[0] = 0;
+    if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
+    const IndexLayout &lay = idx->lay;
+    if (!q || !out) return fail(MP_E_ARG, "q and out must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(out) & 15))
+        return fail(MP_E_ARG, "q and out must be 16-byte aligned");
+    if (H_q < 1 || H_q % lay.H_kv)
+        return fail(MP_E_SHAPE, "H_q = %d is not a positive multiple of H_kv = %d", H_q, lay.H_kv);
+    const int32_t G = H_q / lay.H_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(MP_E_SHAPE, "GQA group size H_q/H_kv = %d; supported: 1, 2, 4, 8", G);
+    if (int64_t(lay.B) * H_q > 65535 * 16)
+        return fail(MP_E_SHAPE, "B*H_q = %lld is too large", (long long)lay.B * H_q);
+    mp_status st = check_view(k, "k");
+    if (st != MP_OK) return st;
+    st = check_view(v, "v");
+    if (st != MP_OK) return st;
+    if (k->dtype != v->dtype) return fail(MP_E_DTYPE, "k and v must have the same dtype");
+    if (k->dtype != idx->key_dtype)
+        return fail(MP_E_DTYPE, "k dtype differs from the keys the index was built from");
+    if (k->B != lay.B || k->H != lay.H_kv || k->n != lay.n || v->B != lay.B ||
+        v->H != lay.H_kv || v->n != lay.n)
+        return fail(MP_E_SHAPE, "k/v shape [%d][%d][%d] / [%d][%d][%d] differs from the index [%d][%d][%d]",
+                    k->B, k->H, k->n, v->B, v->H, v->n, lay.B, lay.H_kv, lay.n);
+    if (n_sink < 0 || n_local < 0) return fail(MP_E_ARG, "n_sink and n_local must be >= 0");
+    if (!isfinite(scale) || scale < 0.0f) return fail(MP_E_ARG, "scale must be finite and >= 0");
+    const DecodeLayout dl = decode_layout(lay, H_q);
+    if (!scratch) return fail(MP_E_WORKSPACE, "scratch is NULL");
+    if (reinterpret_cast<uintptr_t>(scratch) & 255)
+        return fail(MP_E_WORKSPACE, "scratch must be 256-byte aligned");
+    if (scratch_bytes < size_t(dl.total))
+        return fail(MP_E_WORKSPACE, "scratch holds %zu bytes, %lld needed", scratch_bytes,
+                    (long long)dl.total);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != idx->device)
+        return fail(MP_E_ARG, "current device %d is not the device %d the index lives on", dev,
+                    idx->device);
+
+    char *sp = static_cast<char *>(scratch);
+    DecodeArgs a{};
+    a.q = q;
+    a.B = lay.B;
+    a.H_q = H_q;
+    a.H_kv = lay.H_kv;
+    a.G = G;
+    a.n = lay.n;
+    a.n_chunks = lay.n_chunks;
+    a.K = lay.K;
+    a.L = lay.L;
+    a.n_sink = n_sink;
+    a.n_local = n_local;
+    a.scale = scale > 0.0f ? scale : 1.0f / sqrtf(float(kD));
+    a.W = idx->W;
+    a.mu = idx->mu;
+    a.codes = idx->codes;
+    a.k = KVRows{k->data, k->stride_b, k->stride_h, k->stride_n, k->H};
+    a.v = KVRows{v->data, v->stride_b, v->stride_h, v->stride_n, v->H};
+    a.dtype = k->dtype;
+    a.qcodes = reinterpret_cast<uint16_t *>(sp + dl.off_qcodes);
+    a.qq = reinterpret_cast<uint32_t *>(sp + dl.off_qq);
+    a.qnorm = reinterpret_cast<float *>(sp + dl.off_qnorm);
+    a.part = reinterpret_cast<float *>(sp + dl.off_part);
+    a.seg_idx = reinterpret_cast<int32_t *>(sp + dl.off_seg_idx);
+    a.seg_cnt = reinterpret_cast<int32_t *>(sp + dl.off_seg_cnt);
+    a.out = out;
+    a.counts = counts;
+    a.s_idx = s_idx;
+    a.s_len = s_len;
+    a.debug = debug;
+    a.ev_begin = static_cast<hipEvent_t>(ev_begin);
+    a.ev_end = static_cast<hipEvent_t>(ev_end);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_decode(a, s);
+    if (e != hipSuccess) return fail(MP_E_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    if (debug && qcodes) {
+        e = hipMemcpyAsync(qcodes, a.qcodes, size_t(dl.BHq) * lay.L * 2, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return fail(MP_E_HIP, "qcodes copy failed: %s", hipGetErrorString(e));
+    }
+    return MP_OK;
+}
+
+}  // namespace mp
+
+using namespace mp;
+
+extern "C" {
+
+size_t mp_index_workspace_bytes(int32_t B, int32_t H_kv, int32_t n, int32_t d, int32_t K, int32_t L)
+{
+    if (!sizes_ok(B, H_kv, n, d, K, L)) return 0;
+    return size_t(index_layout(B, H_kv, n, K, L).total);
+}
+
+mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t seed,
+                         void *workspace, size_t workspace_bytes, void *stream, mp_index **out)
+{
+    g_err[0] = 0;
+    if (!out) return fail(MP_E_ARG, "out is NULL");
+    *out = nullptr;
+    mp_status st = check_view(keys, "keys");
+    if (st != MP_OK) return st;
+    if (K < 0 || K > 16) return fail(MP_E_ARG, "K = %d outside [0, 16]", K);
+    if (L < 2 || L > 255) return fail(MP_E_ARG, "L = %d outside [2, 255]", L);
+    if (int64_t(keys->B) * keys->H > 65535)
+        return fail(MP_E_SHAPE, "B*H_kv = %lld is too large", (long long)keys->B * keys->H);
+    const IndexLayout lay = index_layout(keys->B, keys->H, keys->n, K, L);
+    if (!workspace) return fail(MP_E_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255)
+        return fail(MP_E_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < size_t(lay.total))
+        return fail(MP_E_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
+                    (long long)lay.total);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MP_E_HIP, "no current HIP device");
+
+    mp_index *idx = new (std::nothrow) mp_index();
+    if (!idx) return fail(MP_E_ARG, "host allocation of the handle failed");
+    char *wp = static_cast<char *>(workspace);
+    idx->magic = kMagic;
+    idx->lay = lay;
+    idx->seed = seed;
+    idx->key_dtype = keys->dtype;
+    idx->device = dev;
+    idx->W = reinterpret_cast<float *>(wp + lay.off_W);
+    idx->Wp = reinterpret_cast<float *>(wp + lay.off_Wp);
+    idx->mu = reinterpret_cast<float *>(wp + lay.off_mu);
+    idx->mu_part = reinterpret_cast<double *>(wp + lay.off_mu_part);
+    idx->codes = reinterpret_cast<uint16_t *>(wp + lay.off_codes);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const KVRows rows{keys->data, keys->stride_b, keys->stride_h, keys->stride_n, keys->H};
+    hipError_t e = launch_wgen(seed, lay.R, lay.R_pad, idx->W, idx->Wp, s);
+    if (e == hipSuccess)
+        e = launch_mean(rows, keys->dtype, lay.B, lay.H_kv, lay.n, lay.n_mean_blocks, idx->mu_part,
+                        idx->mu, s);
+    if (e == hipSuccess) {
+        const int64_t ncodes = int64_t(lay.B) * lay.H_kv * lay.n_chunks * int64_t(L) * kChunk;
+        if (K == 0)
+            e = launch_fill_u16(idx->codes, ncodes, s);
+        else
+            e = launch_encode_keys(rows, keys->dtype, lay.B, lay.H_kv, lay.n, lay.n_chunks, idx->mu,
+                                   idx->Wp, K, L, lay.R_pad, idx->codes, s);
+    }
+    if (e != hipSuccess) {
+        idx->magic = 0;
+        delete idx;
+        return fail(MP_E_HIP, "index build launch failed: %s", hipGetErrorString(e));
+    }
+    *out = idx;
+    return MP_OK;
+}
+
+size_t mp_decode_scratch_bytes(const mp_index *idx, int32_t H_q)
+{
+    if (!live(idx) || H_q < 1 || H_q % idx->lay.H_kv) return 0;
+    return size_t(decode_layout(idx->lay, H_q).total);
+}
+
+mp_status mp_decode_attn(const float *q, int32_t H_q, const mp_index *idx, const mp_kv_view *k,
+                         const mp_kv_view *v, int32_t n_sink, int32_t n_local, float scale,
+                         float *out, void *scratch, size_t scratch_bytes, void *stream)
+{
+    return decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
+                         stream, false, nullptr, nullptr, nullptr, nullptr);
+}
+
+mp_status mp_decode_attn_timed(const float *q, int32_t H_q, const mp_index *idx,
+                               const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
+                               int32_t n_local, float scale, float *out, void *scratch,
+                               size_t scratch_bytes, void *stream, void *ev_scan_begin,
+                               void *ev_scan_end)
+{
+    return decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
+                         stream, false, nullptr, nullptr, nullptr, nullptr, ev_scan_begin,
+                         ev_scan_end);
+}
+
+mp_status mp_decode_debug(const float *q, int32_t H_q, const mp_index *idx, const mp_kv_view *k,
+                          const mp_kv_view *v, int32_t n_sink, int32_t n_local, float scale,
+                          float *out, void *scratch, size_t scratch_bytes, void *stream,
+                          uint16_t *qcodes, uint8_t *counts, int32_t *s_idx, int32_t *s_len)
+{
+    return decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
+                         stream, true, qcodes, counts, s_idx, s_len);
+}
+
+mp_status mp_index_views(const mp_index *idx, const float **W, const float **mu,
+                         const uint16_t **codes, int32_t *n_pad)
+{
+    g_err[0] = 0;
+    if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
+    if (W) *W = idx->W;
+    if (mu) *mu = idx->mu;
+    if (codes) *codes = idx->codes;
+    if (n_pad) *n_pad = idx->lay.n_pad;
+    return MP_OK;
+}
+
+void mp_index_destroy(mp_index *idx)
+{
+    if (!live(idx)) return;
+    idx->magic = 0;
+    delete idx;
+}
+
+const char *mp_status_str(mp_status s)
+{
+    switch (s) {
+    case MP_OK: return "MP_OK";
+    case MP_E_ARG: return "MP_E_ARG: invalid argument";
+    case MP_E_SHAPE: return "MP_E_SHAPE: unsupported or mismatched shape";
+    case MP_E_DTYPE: return "MP_E_DTYPE: unsupported dtype";
+    case MP_E_WORKSPACE: return "MP_E_WORKSPACE: workspace or scratch too small or misaligned";
+    case MP_E_HIP: return "MP_E_HIP: HIP call or kernel launch failed";
+    case MP_E_HANDLE: return "MP_E_HANDLE: not a live index";
+    }
+    return "unknown mp_status";
+}
+
+const char *mp_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,614 @@
+// decode.hip -- one MagicPIG decode step on gfx950: three launches.
+//
+//   encode_query   SimHash codes of the raw queries (page "MagicPIG: LSH
+//                  Sampling for Efficient LLM Generation", algorithm steps:
+//                  the query's code from the shared projector).
+//   scan_gather    per 512-key chunk of one KV head and its G query heads:
+//                  (a) stream the chunk's codes (16-byte lane loads) and count,
+//                      per key and query head, the tables where the key shares
+//                      the query's bucket;
+//                  (b) a key is sampled for a head iff that count is >= 2 and
+//                      the key is not in the exact set T (method details and
+//                      page "MagicPIG: don't pick the tallest", section 5);
+//                      ballot/prefix-sum compaction of the union of sampled
+//                      and exact keys into an ascending LDS list;
+//                  (c) gather the listed K/V rows, recompute q.k and the cosine
+//                      to the centered key, u_i = P[Binomial(L, p^K) >= 2],
+//                      z = q.k*scale - log u (z = q.k*scale on T), and run an
+//                      online softmax per query head (algorithm steps: one
+//                      softmax over [w_S, w_T]/sqrt(d) - log[u, 1]); the
+//                      chunk's partial softmax (max, sum, unnormalised
+//                      accumulator) per head goes to scratch.
+//   merge          log-sum-exp merge of the chunk partials of every query head
+//                  (system co-design: partial attention outputs are merged
+//                  recursively).  A kernel of its own: its launch boundary is
+//                  what makes the partials of blocks on other XCDs visible,
+//                  which an in-kernel device-scope fence would buy with an L2
+//                  write-back per block.
+#include <math.h>
+
+#include "mp_internal.h"
+
+namespace mp {
+namespace {
+
+constexpr int kPart = kD + 2;     // partial softmax: m, l, acc[128]
+constexpr int kRowsPerGroup = 2;  // listed rows a 16-lane group holds per round
+constexpr int kRound = 16 * kRowsPerGroup;
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// 8 consecutive elements of a K or V row: raw load, then conversion to fp32.
+template <typename T> struct Row8;
+template <> struct Row8<float> {
+    struct raw { float4 a, b; };
+    static __device__ __forceinline__ raw load_raw(const float *p)
+    {
+        return raw{*reinterpret_cast<const float4 *>(p), *reinterpret_cast<const float4 *>(p + 4)};
+    }
+    static __device__ __forceinline__ void convert(const raw &r, float (&o)[8])
+    {
+        o[0] = r.a.x; o[1] = r.a.y; o[2] = r.a.z; o[3] = r.a.w;
+        o[4] = r.b.x; o[5] = r.b.y; o[6] = r.b.z; o[7] = r.b.w;
+    }
+};
+template <> struct Row8<uint16_t> {
+    using raw = uint4;
+    static __device__ __forceinline__ raw load_raw(const uint16_t *p)
+    {
+        return *reinterpret_cast<const uint4 *>(p);
+    }
+    static __device__ __forceinline__ void convert(const raw &a, float (&o)[8])
+    {
+        o[0] = bf16_to_f32(a.x & 0xFFFFu); o[1] = bf16_to_f32(a.x >> 16);
+        o[2] = bf16_to_f32(a.y & 0xFFFFu); o[3] = bf16_to_f32(a.y >> 16);
+        o[4] = bf16_to_f32(a.z & 0xFFFFu); o[5] = bf16_to_f32(a.z >> 16);
+        o[6] = bf16_to_f32(a.w & 0xFFFFu); o[7] = bf16_to_f32(a.w >> 16);
+    }
+};
+
+// Per 16-bit half: min(a, b).  Written out because the compiler turns the
+// vector-extension form into compares and selects.
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b)
+{
+    uint32_t d;
+    asm("v_pk_min_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// log u for u = P[at least 2 of L tables collide], P = p^K (fp32).
+// Closed form 1 - (1-P)^L - L P (1-P)^(L-1) where L*P > 0.05; below that the
+// two subtractions cancel, so u is the binomial tail
+//   C(L,2) P^2 (1-P)^(L-2) * (1 + sum_{j>=3} prod_{i=2}^{j-1} (L-i)/(i+1) P/(1-P))
+// taken in logs.  p is floored at 1e-30: p = 0 only for an exactly
+// anti-parallel centered key, which cannot collide in exact arithmetic.
+__device__ __forceinline__ float log_u_f32(float p, int K, int L)
+{
+    if (K == 0) return 0.0f;
+    p = fminf(fmaxf(p, 1e-30f), 1.0f);
+    const float logP = float(K) * logf(p);
+    const float P = expf(logP);
+    if (P >= 1.0f) return 0.0f;
+    const float a = log1pf(-P);
+    const float LP = float(L) * P;
+    if (LP > 0.05f) {
+        const float u = -expm1f(float(L) * a) - LP * expf(float(L - 1) * a);
+        return logf(u);
+    }
+    const float r = P / (1.0f - P);
+    float term = 1.0f, rest = 0.0f;
+    for (int j = 2; j < L; ++j) {
+        term *= float(L - j) / float(j + 1) * r;
+        rest += term;
+        if (term < 1e-9f * (1.0f + rest)) break;
+    }
+    return logf(0.5f * float(L) * float(L - 1)) + 2.0f * logP + float(L - 2) * a + log1pf(rest);
+}
+
+// ---------------------------------------------------------------- query codes
+// Block: TB = 64/K whole tables (<= 64 hyperplanes) x 4 query heads.  Lane =
+// hyperplane, wave = query head: the lane keeps its W row in registers and
+// reads the head's query from LDS (a broadcast).  Sign bits meet in LDS and
+// are packed per (head, table).
+__global__ __launch_bounds__(256) void encode_query_kernel(const float *__restrict__ q,
+                                                           int32_t BHq,
+                                                           const float *__restrict__ W, int32_t K,
+                                                           int32_t L,
+                                                           uint16_t *__restrict__ qcodes,
+                                                           uint32_t *__restrict__ qq,
+                                                           float *__restrict__ qnorm)
+{
+    __shared__ float4 sQ[4][kD / 4];
+    __shared__ uint8_t sbit[4][64];
+    const int t = threadIdx.x;
+    const int TB = K > 0 ? 64 / K : 64;
+    const int l0 = blockIdx.x * TB;
+    const int nt = min(TB, L - l0);
+    const int nh = nt * K;
+    const int q0 = blockIdx.y * 4;
+    const int nq = min(4, BHq - q0);
+    const float4 *q4 = reinterpret_cast<const float4 *>(q + int64_t(q0) * kD);
+    if (t < nq * (kD / 4)) sQ[t / (kD / 4)][t % (kD / 4)] = q4[t];
+    const int hp = t & 63, qi = uniform(t >> 6);
+    float4 wr[kD / 4];
+    if (hp < nh) {
+        const float4 *w4 = reinterpret_cast<const float4 *>(W + (int64_t(l0) * K + hp) * kD);
+#pragma unroll
+        for (int c = 0; c < kD / 4; ++c) wr[c] = w4[c];
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && qi < nq) {       // |q| of this wave's head, for the cosines
+        const float4 v = sQ[qi][hp & 31];
+        float s2 = hp < 32 ? v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w : 0.0f;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) s2 += __shfl_xor(s2, off);
+        if (hp == 0) qnorm[q0 + qi] = sqrtf(s2);
+    }
+    if (hp < nh && qi < nq) {
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;   // four chains, dims c mod 4
+#pragma unroll
+        for (int c = 0; c < kD / 4; ++c) {
+            const float4 qv = sQ[qi][c];
+            a0 = fmaf(wr[c].x, qv.x, a0);
+            a1 = fmaf(wr[c].y, qv.y, a1);
+            a2 = fmaf(wr[c].z, qv.z, a2);
+            a3 = fmaf(wr[c].w, qv.w, a3);
+        }
+        sbit[qi][hp] = ((a0 + a1) + (a2 + a3)) > 0.0f ? 1 : 0;
+    }
+    __syncthreads();
+    if (t < nq * nt) {
+        const int qj = t / nt, tl = t % nt;
+        uint32_t code = 0;
+        for (int bb = 0; bb < K; ++bb) code |= uint32_t(sbit[qj][tl * K + bb]) << bb;
+        const int64_t o = int64_t(q0 + qj) * L + l0 + tl;
+        qcodes[o] = uint16_t(code);
+        qq[o] = code | (code << 16);
+    }
+}
+
+// ---------------------------------------------------------------- scan + gather
+// Waves per SIMD the register budget is cut for: 4 up to G = 4 (fp32 rows at
+// G = 4 would spill there), 2 for G = 8.
+template <int G, typename T>
+constexpr int scan_occupancy() { return G <= 2 || (G == 4 && sizeof(T) == 2) ? 4 : (G == 4 ? 3 : 2); }
+
+template <int G, typename T>
+__global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_kernel(DecodeArgs a)
+{
+    __shared__ uint32_t red[G][256];         // packed mismatch counts, word = 2 keys
+    __shared__ uint32_t ulist[kChunk];       // key | headmask << 16 | exact << 24
+    __shared__ int wsum[4];
+    __shared__ float st[4][G][kPart];
+    __shared__ __align__(16) float sq[G][kD];   // the group's queries
+    __shared__ float sqn[G];                 // their norms
+    __shared__ __align__(16) float smu[kD];  // mean of the head's keys
+    __shared__ float srow[kRound][2 * G + 1];   // per listed row: q.k, q.(k-mu), |k-mu|^2
+    __shared__ float sz[kRound][G];          // per (row, head): z, or -inf if not taken
+
+    const int chunk = blockIdx.x;
+    const int bkv = blockIdx.y;
+    const int b = bkv / a.H_kv, h = bkv % a.H_kv;
+    const int bhq0 = b * a.H_q + h * G;
+    const int t = threadIdx.x, lane = t & 63, w = uniform(t >> 6);
+    const int L = a.L;
+    const int n = a.n;
+
+    // Queries, their norms and mu go to LDS now; the loads land during the scan.
+    for (int i = t; i < G * kD; i += 256) sq[i / kD][i % kD] = a.q[int64_t(bhq0) * kD + i];
+    if (t < G) sqn[t] = a.qnorm[bhq0 + t];
+    if (t < kD) smu[t] = a.mu[int64_t(bkv) * kD + t];
+
+    // ---- (a) collision counts: wave w scans tables [w L/4, (w+1) L/4) ----
+    for (int i = t; i < G * 256; i += 256) (&red[0][0])[i] = 0u;
+    {
+        const uint4 *cp = reinterpret_cast<const uint4 *>(
+                              a.codes + (int64_t(bkv) * a.n_chunks + chunk) * int64_t(L) * kChunk) +
+                          lane;
+        const uint32_t *qqp = a.qq + int64_t(bhq0) * L;
+        const uint32_t one2 = 0x00010001u;
+        uint32_t mism[4][G];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int g = 0; g < G; ++g) mism[k][g] = 0u;
+        const int lb = uniform((w * L) / 4), le = uniform(((w + 1) * L) / 4);
+        // Batches of 8 tables, the next batch in flight while this one is
+        // counted; a short last batch re-reads table le-1 and skips it.
+        uint4 cur[8], nxt[8];
+        if (lb < le) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) cur[u] = cp[int64_t(min(lb + u, le - 1)) * (kChunk / 8)];
+        }
+        for (int l0 = lb; l0 < le; l0 += 8) {
+            if (l0 + 8 < le) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    nxt[u] = cp[int64_t(min(l0 + 8 + u, le - 1)) * (kChunk / 8)];
+            }
+            const int nv = min(8, le - l0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                // a re-read table (u >= nv) adds min(x, 0) = 0 mismatches
+                const uint32_t lim = u < nv ? one2 : 0u;
+                const int lu = min(l0 + u, le - 1);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const uint32_t qv = qqp[g * L + lu];
+                    mism[0][g] += pk_min_u16(cur[u].x ^ qv, lim);
+                    mism[1][g] += pk_min_u16(cur[u].y ^ qv, lim);
+                    mism[2][g] += pk_min_u16(cur[u].z ^ qv, lim);
+                    mism[3][g] += pk_min_u16(cur[u].w ^ qv, lim);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
+        }
+        __syncthreads();   // red zeroed
+        // Each half counts at most 255 tables, so a 32-bit add of the packed
+        // pair never carries between keys.
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int g = 0; g < G; ++g) atomicAdd(&red[g][lane * 4 + k], mism[k][g]);
+        __syncthreads();
+    }
+
+    // ---- (b) sampled / exact sets and ascending compaction ----
+    // Thread t owns keys 2t and 2t+1 of the chunk.
+    const int64_t key0 = int64_t(chunk) * kChunk + 2 * t;
+    uint32_t hm[2] = {0u, 0u};
+    bool ex[2], fl[2];
+    uint32_t cnt[2][G];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int64_t i = key0 + e;
+        const bool valid = i < n;
+        ex[e] = valid && (i < a.n_sink || i >= int64_t(n) - a.n_local);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const uint32_t mm = (red[g][t] >> (16 * e)) & 0xFFFFu;
+            cnt[e][g] = uint32_t(L) - mm;
+            if (valid && !ex[e] && cnt[e][g] >= 2u) hm[e] |= 1u << g;
+        }
+        fl[e] = ex[e] || hm[e] != 0u;
+    }
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    {
+        const unsigned long long b0 = __ballot(fl[0]), b1 = __ballot(fl[1]);
+        const int pre = __popcll(b0 & lt) + __popcll(b1 & lt);
+        if (lane == 0) wsum[w] = __popcll(b0) + __popcll(b1);
+        __syncthreads();
+        int woff = 0;
+        for (int j = 0; j < w; ++j) woff += wsum[j];
+        const int pos = woff + pre;
+        if (fl[0]) ulist[pos] = uint32_t(2 * t) | (hm[0] << 16) | (uint32_t(ex[0]) << 24);
+        if (fl[1])
+            ulist[pos + (fl[0] ? 1 : 0)] =
+                uint32_t(2 * t + 1) | (hm[1] << 16) | (uint32_t(ex[1]) << 24);
+    }
+    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+
+    if (a.debug) {
+        if (a.counts) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                if (key0 + e < n)
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        a.counts[int64_t(bhq0 + g) * n + key0 + e] = uint8_t(cnt[e][g]);
+        }
+        // Per-head sampled lists of this chunk (ascending), for the S view.
+        for (int g = 0; g < G; ++g) {
+            const bool s0 = (hm[0] >> g) & 1u, s1 = (hm[1] >> g) & 1u;
+            const unsigned long long b0 = __ballot(s0), b1 = __ballot(s1);
+            const int pre = __popcll(b0 & lt) + __popcll(b1 & lt);
+            __syncthreads();
+            if (lane == 0) wsum[w] = __popcll(b0) + __popcll(b1);
+            __syncthreads();
+            int woff = 0;
+            for (int j = 0; j < w; ++j) woff += wsum[j];
+            int32_t *seg = a.seg_idx + (int64_t(bhq0 + g) * a.n_chunks + chunk) * kChunk;
+            if (s0) seg[woff + pre] = int32_t(key0);
+            if (s1) seg[woff + pre + (s0 ? 1 : 0)] = int32_t(key0 + 1);
+            if (t == 0)
+                a.seg_cnt[int64_t(bhq0 + g) * a.n_chunks + chunk] =
+                    wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        }
+    }
+    __syncthreads();   // ulist complete
+
+    // ---- (c) gather + online softmax, in rounds of up to 64 listed rows ----
+    // c1: 16 groups of 16 lanes, lane = 8 dims; group gi loads rows
+    //     gi, gi+16, gi+32, gi+48 of the round (all loads issued first) and
+    //     reduces q_g.k, q_g.(k - mu) and |k - mu|^2 into LDS;
+    // c2: one thread per (row, head) evaluates z once;
+    // c3: each group folds its rows' z and V rows into its running softmax.
+    const int gi = t >> 4, li = t & 15;
+    float mu8[8];
+    {
+        const float4 m0 = reinterpret_cast<const float4 *>(smu)[2 * li];
+        const float4 m1 = reinterpret_cast<const float4 *>(smu)[2 * li + 1];
+        mu8[0] = m0.x; mu8[1] = m0.y; mu8[2] = m0.z; mu8[3] = m0.w;
+        mu8[4] = m1.x; mu8[5] = m1.y; mu8[6] = m1.z; mu8[7] = m1.w;
+    }
+    float m_run[G], l_run[G], acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m_run[g] = -INFINITY;
+        l_run[g] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[g][j] = 0.0f;
+    }
+    const T *kb = static_cast<const T *>(a.k.data) + b * a.k.sb + h * a.k.sh + 8 * li;
+    const T *vb = static_cast<const T *>(a.v.data) + b * a.v.sb + h * a.v.sh + 8 * li;
+    const float inv_pi = 0.31830988618379067f;
+    for (int base = 0; base < total; base += kRound) {
+        const int ne = min(kRound, total - base);
+        typename Row8<T>::raw kraw[kRowsPerGroup], vraw[kRowsPerGroup];
+#pragma unroll
+        for (int r = 0; r < kRowsPerGroup; ++r) {
+            const int e = gi + 16 * r;
+            if (e < ne) {
+                const int64_t i = int64_t(chunk) * kChunk + (ulist[base + e] & 0xFFFFu);
+                kraw[r] = Row8<T>::load_raw(kb + i * a.k.sn);
+                vraw[r] = Row8<T>::load_raw(vb + i * a.v.sn);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kRowsPerGroup; ++r) {
+            const int e = gi + 16 * r;
+            if (e >= ne) continue;            // uniform over the 16-lane group
+            float kr[8], x[8];
+            Row8<T>::convert(kraw[r], kr);
+            float xx = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                x[j] = kr[j] - mu8[j];
+                xx = fmaf(x[j], x[j], xx);
+            }
+            float sd[G], td[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float4 q0 = *reinterpret_cast<const float4 *>(&sq[g][8 * li]);
+                const float4 q1 = *reinterpret_cast<const float4 *>(&sq[g][8 * li + 4]);
+                const float qg[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                float s0 = 0.0f, t0 = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    s0 = fmaf(qg[j], kr[j], s0);
+                    t0 = fmaf(qg[j], x[j], t0);
+                }
+                sd[g] = s0;
+                td[g] = t0;
+            }
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) {
+                xx += __shfl_xor(xx, off, 16);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    sd[g] += __shfl_xor(sd[g], off, 16);
+                    td[g] += __shfl_xor(td[g], off, 16);
+                }
+            }
+            if (li == 0) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    srow[e][g] = sd[g];
+                    srow[e][G + g] = td[g];
+                }
+                srow[e][2 * G] = xx;
+            }
+        }
+        __syncthreads();
+        for (int pidx = t; pidx < ne * G; pidx += 256) {
+            const int e = pidx / G, g = pidx % G;
+            const uint32_t ent = ulist[base + e];
+            const bool exact = (ent >> 24) & 1u;
+            float z = -INFINITY;
+            if (exact || ((ent >> (16 + g)) & 1u)) {
+                z = srow[e][g] * a.scale;
+                if (!exact) {
+                    const float den = sqn[g] * sqrtf(srow[e][2 * G]);
+                    float cs = den > 0.0f ? srow[e][G + g] / den : 0.0f;
+                    cs = fminf(fmaxf(cs, -1.0f), 1.0f);
+                    const float p = 1.0f - acosf(cs) * inv_pi;
+                    z -= log_u_f32(p, a.K, L);
+                }
+            }
+            sz[e][g] = z;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kRowsPerGroup; ++r) {
+            const int e = gi + 16 * r;
+            if (e >= ne) continue;
+            float vr[8];
+            Row8<T>::convert(vraw[r], vr);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float z = sz[e][g];
+                if (z == -INFINITY) continue;
+                const float mn = fmaxf(m_run[g], z);
+                const float al = __expf(m_run[g] - mn);
+                const float be = __expf(z - mn);
+                l_run[g] = l_run[g] * al + be;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(acc[g][j], al, be * vr[j]);
+                m_run[g] = mn;
+            }
+        }
+        __syncthreads();   // srow/sz are rewritten by the next round
+    }
+
+    // ---- combine the 4 groups of a wave (lanes l, l^16, l^32) ----
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float mo = __shfl_xor(m_run[g], off);
+            const float lo = __shfl_xor(l_run[g], off);
+            float ao[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ao[j] = __shfl_xor(acc[g][j], off);
+            const float mn = fmaxf(m_run[g], mo);
+            if (mn != -INFINITY) {
+                const float al = __expf(m_run[g] - mn), be = __expf(mo - mn);
+                l_run[g] = l_run[g] * al + lo * be;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[g][j] = acc[g][j] * al + ao[j] * be;
+                m_run[g] = mn;
+            }
+        }
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) st[w][g][2 + 8 * li + j] = acc[g][j];
+            if (li == 0) {
+                st[w][g][0] = m_run[g];
+                st[w][g][1] = l_run[g];
+            }
+        }
+    }
+    __syncthreads();
+    // ---- combine the 4 waves into this chunk's partial ----
+    float *part0 = a.part + (int64_t(bkv) * a.n_chunks + chunk) * (G * kPart);
+    for (int idx = t; idx < G * kD; idx += 256) {
+        const int g = idx / kD, c = idx % kD;
+        float M = st[0][g][0];
+        for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, st[ww][g][0]);
+        float lsum = 0.0f, av = 0.0f;
+        if (M != -INFINITY) {
+            for (int ww = 0; ww < 4; ++ww) {
+                const float f = __expf(st[ww][g][0] - M);
+                lsum += st[ww][g][1] * f;
+                av += st[ww][g][2 + c] * f;
+            }
+        }
+        part0[g * kPart + 2 + c] = av;
+        if (c == 0) {
+            part0[g * kPart] = M;
+            part0[g * kPart + 1] = lsum;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- merge
+// Block = one (KV head unit, query head g of its group, quarter of the dims);
+// thread = (dim c of 32, chunk lane j of 32).  Lane j folds chunks j, j+32,
+// ... into a running (max, sum, acc) in one pass; the 32 lanes are then
+// combined in lane order, so the result is deterministic.
+template <int G>
+__global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ part,
+                                                    int32_t n_chunks, int32_t H_kv, int32_t H_q,
+                                                    float *__restrict__ out)
+{
+    __shared__ float sm[32][33], sl[32][33], sa[32][33];
+    const int bkv = blockIdx.x / G, g = blockIdx.x % G;
+    const int t = threadIdx.x, cl = t & 31, j = t >> 5;
+    const int c = 32 * blockIdx.y + cl;
+    const float *p = part + int64_t(bkv) * n_chunks * (G * kPart) + g * kPart;
+    float m = -INFINITY, l = 0.0f, acc = 0.0f;
+#pragma unroll 2
+    for (int ch = j; ch < n_chunks; ch += 32) {
+        const float *pc = p + int64_t(ch) * (G * kPart);
+        const float mc = pc[0], lc = pc[1], ac = pc[2 + c];
+        if (mc > m) {
+            const float f = __expf(m - mc);      // 0 while m = -inf
+            l = fmaf(l, f, lc);
+            acc = fmaf(acc, f, ac);
+            m = mc;
+        } else if (mc != -INFINITY) {
+            const float f = __expf(mc - m);
+            l = fmaf(lc, f, l);
+            acc = fmaf(ac, f, acc);
+        }
+    }
+    sm[j][cl] = m;
+    sl[j][cl] = l;
+    sa[j][cl] = acc;
+    __syncthreads();
+    if (t < 32) {
+        float M = -INFINITY;
+        for (int r = 0; r < 32; ++r) M = fmaxf(M, sm[r][t]);
+        float ls = 0.0f, as = 0.0f;
+        if (M != -INFINITY) {
+            for (int r = 0; r < 32; ++r) {
+                const float f = __expf(sm[r][t] - M);
+                ls = fmaf(sl[r][t], f, ls);
+                as = fmaf(sa[r][t], f, as);
+            }
+        }
+        const int b = bkv / H_kv, h = bkv % H_kv;
+        out[(int64_t(b) * H_q + h * G + g) * kD + c] = ls > 0.0f ? as / ls : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------- debug S view
+__global__ __launch_bounds__(256) void seg_compact_kernel(const int32_t *__restrict__ seg_idx,
+                                                          const int32_t *__restrict__ seg_cnt,
+                                                          int32_t n_chunks, int32_t n,
+                                                          int32_t *__restrict__ s_idx,
+                                                          int32_t *__restrict__ s_len)
+{
+    const int bhq = blockIdx.x, t = threadIdx.x;
+    int64_t off = 0;
+    for (int ch = 0; ch < n_chunks; ++ch) {
+        const int cnt = seg_cnt[int64_t(bhq) * n_chunks + ch];
+        const int32_t *src = seg_idx + (int64_t(bhq) * n_chunks + ch) * kChunk;
+        if (s_idx)
+            for (int r = t; r < cnt; r += 256) s_idx[int64_t(bhq) * n + off + r] = src[r];
+        off += cnt;
+    }
+    if (t == 0 && s_len) s_len[bhq] = int32_t(off);
+}
+
+template <int G>
+hipError_t launch_scan_gather(const DecodeArgs &a, hipStream_t s)
+{
+    const dim3 grid(a.n_chunks, a.B * a.H_kv);
+    if (a.dtype == MP_BF16)
+        scan_gather_kernel<G, uint16_t><<<grid, 256, 0, s>>>(a);
+    else
+        scan_gather_kernel<G, float><<<grid, 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.ev_end && (e = hipEventRecord(a.ev_end, s)) != hipSuccess) return e;
+    merge_kernel<G><<<dim3(a.B * a.H_kv * G, kD / 32), 1024, 0, s>>>(a.part, a.n_chunks, a.H_kv,
+                                                                   a.H_q, a.out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
+{
+    const int BHq = a.B * a.H_q;
+    const int TB = a.K > 0 ? 64 / a.K : 64;
+    encode_query_kernel<<<dim3(ceil_div(a.L, TB), ceil_div(BHq, 4)), 256, 0, s>>>(
+        a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.ev_begin && (e = hipEventRecord(a.ev_begin, s)) != hipSuccess) return e;
+    switch (a.G) {
+    case 1: e = launch_scan_gather<1>(a, s); break;
+    case 2: e = launch_scan_gather<2>(a, s); break;
+    case 4: e = launch_scan_gather<4>(a, s); break;
+    case 8: e = launch_scan_gather<8>(a, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    if (a.debug && (a.s_idx || a.s_len)) {
+        seg_compact_kernel<<<dim3(BHq), 256, 0, s>>>(a.seg_idx, a.seg_cnt, a.n_chunks, a.n,
+                                                     a.s_idx, a.s_len);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace mp

@@ -1,0 +1,304 @@
+// index_build.hip -- index build for MagicPIG decode on gfx950.
+//
+//   wgen          hyperplanes W ~ N(0,1), one shared matrix for all heads
+//                 (page "MagicPIG: LSH Sampling for Efficient LLM Generation",
+//                 system co-design item 2: one random projector serves every head)
+//   mean          mu = mean of all n keys of each (sequence, KV head), fp64 sums
+//                 (same page, method details: centering before hashing)
+//   encode_keys   SimHash codes of x_i = k_i - mu on fp32 MFMA: bit j = [W_j.x_i > 0],
+//                 K bits per table packed LSB-first into uint16 (same page,
+//                 background: SimHash sign(w^T x); method details: K x L vectors)
+#include "mp_internal.h"
+
+namespace mp {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- W
+// SplitMix64 (Steele, Lea & Flood 2014): output number k of the generator
+// started at `seed` is the finaliser applied to seed + k * golden-gamma.
+__device__ __forceinline__ uint64_t splitmix_output(uint64_t seed, uint64_t k)
+{
+    uint64_t z = seed + k * 0x9E3779B97F4A7C15ULL;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+// Element e of W is the cosine branch of the Box-Muller transform of the
+// uniforms made from outputs 2e+1 and 2e+2.  Also writes the MFMA B-fragment
+// copy: for column tile t (16 hyperplanes), lane = (j % 16) + 16 * (c / 32)
+// and k-step s = c % 32 live at Wp[((t*8 + s/4)*64 + lane)*4 + s%4], so one
+// float4 per lane per 4 k-steps is a contiguous 1 KB wave load.
+__global__ __launch_bounds__(256) void wgen_kernel(uint64_t seed, int32_t R, int32_t R_pad,
+                                                   float *__restrict__ W, float *__restrict__ Wp)
+{
+    const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (e >= int64_t(R_pad) * kD) return;
+    const int32_t j = int32_t(e / kD), c = int32_t(e % kD);
+    float g = 0.0f;
+    if (j < R) {
+        const uint64_t z1 = splitmix_output(seed, 2 * uint64_t(e) + 1);
+        const uint64_t z2 = splitmix_output(seed, 2 * uint64_t(e) + 2);
+        const double u1 = (double(z1 >> 11) + 1.0) * 0x1.0p-53;
+        const double u2 = double(z2 >> 11) * 0x1.0p-53;
+        g = float(sqrt(-2.0 * log(u1)) * cos(2.0 * 3.141592653589793 * u2));
+    }
+    W[e] = g;
+    const int32_t t = j >> 4, lane = (j & 15) + 16 * (c >> 5), s = c & 31;
+    Wp[((int64_t(t) * 8 + (s >> 2)) * 64 + lane) * 4 + (s & 3)] = g;
+}
+
+// ---------------------------------------------------------------- loads
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// 8 consecutive elements of a row, as fp32.
+template <typename T> struct Row8;
+template <> struct Row8<float> {
+    static __device__ __forceinline__ void load(const float *p, float (&o)[8])
+    {
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+};
+template <> struct Row8<uint16_t> {
+    static __device__ __forceinline__ void load(const uint16_t *p, float (&o)[8])
+    {
+        const uint4 a = *reinterpret_cast<const uint4 *>(p);
+        o[0] = bf16_to_f32(a.x & 0xFFFFu); o[1] = bf16_to_f32(a.x >> 16);
+        o[2] = bf16_to_f32(a.y & 0xFFFFu); o[3] = bf16_to_f32(a.y >> 16);
+        o[4] = bf16_to_f32(a.z & 0xFFFFu); o[5] = bf16_to_f32(a.z >> 16);
+        o[6] = bf16_to_f32(a.w & 0xFFFFu); o[7] = bf16_to_f32(a.w >> 16);
+    }
+};
+
+// ---------------------------------------------------------------- mean
+// Block (kMeanRows keys of one head): thread t sums dims 8*(t%16)..+7 over
+// rows r0 + t/16 + 16k in fp64; the 16 row lanes are added in LDS in a fixed
+// order, so the result does not depend on scheduling.
+template <typename T>
+__global__ __launch_bounds__(256) void mean_partial_kernel(const T *__restrict__ keys, int64_t sb,
+                                                           int64_t sh, int64_t sn, int32_t H,
+                                                           int32_t n, int32_t nmb,
+                                                           double *__restrict__ mu_part)
+{
+    __shared__ double red[16][kD];
+    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int t = threadIdx.x, dg = t & 15, ro = t >> 4;
+    const int64_t r0 = int64_t(blockIdx.x) * kMeanRows;
+    const int64_t r1 = r0 + kMeanRows < n ? r0 + kMeanRows : n;
+    const T *base = keys + b * sb + h * sh + 8 * dg;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int64_t i = r0 + ro; i < r1; i += 16) {
+        float v[8];
+        Row8<T>::load(base + i * sn, v);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] += double(v[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) red[ro][8 * dg + k] = acc[k];
+    __syncthreads();
+    if (t < kD) {
+        double s = 0.0;
+        for (int r = 0; r < 16; ++r) s += red[r][t];
+        mu_part[(int64_t(bh) * nmb + blockIdx.x) * kD + t] = s;
+    }
+}
+
+__global__ __launch_bounds__(kD) void mean_final_kernel(const double *__restrict__ mu_part,
+                                                        int32_t nmb, int32_t n,
+                                                        float *__restrict__ mu)
+{
+    const int bh = blockIdx.x, t = threadIdx.x;
+    double s = 0.0;
+    for (int c = 0; c < nmb; ++c) s += mu_part[(int64_t(bh) * nmb + c) * kD + t];
+    mu[int64_t(bh) * kD + t] = float(s / double(n));
+}
+
+// ---------------------------------------------------------------- encode
+// One block = 4 waves = 256 consecutive keys of one head; wave w owns keys
+// k0 = 256*blockIdx.x + 64*w .. +63 as 4 row tiles of 16.
+//
+// Contraction P[i][j] = sum_c x_i[c] W_j[c] on v_mfma_f32_16x16x4_f32
+// (A 16x4, B 4x16, 16x16 fp32 accumulate).  The 128-long contraction is split
+// in 32 k-steps; in k-step s, lane l feeds dim c = 32*(l/16) + s of row l%16
+// (A = keys) and of column l%16 (B = hyperplanes), so a lane reads 32
+// contiguous dims of one key row.  The result lane l holds rows
+// 4*(l/16) + r, column l%16 of the tile, so a ballot of register r gives
+// 16 sign bits of each of 4 rows: they go to LDS as 16-bit pieces and the
+// codes are cut out of the bit rows once every column tile is done.
+//
+// W tiles (8 KB each, fragment order) are staged through a double-buffered LDS
+// slot shared by the 4 waves.
+template <typename T>
+__global__ __launch_bounds__(256) void encode_keys_kernel(
+    const T *__restrict__ keys, int64_t sb, int64_t sh, int64_t sn, int32_t H, int32_t n,
+    int32_t n_chunks, const float *__restrict__ mu, const float *__restrict__ Wp, int32_t K,
+    int32_t L, int32_t NT, int32_t pstride, uint16_t *__restrict__ codes)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    float4 *wbuf = reinterpret_cast<float4 *>(smem);                       // [2][512] float4
+    uint16_t *bits = reinterpret_cast<uint16_t *>(smem + 2 * 512 * 16);    // [4][64][pstride]
+
+    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int il = lane & 15, g = lane >> 4;
+    const int64_t k0 = int64_t(blockIdx.x) * 256 + 64 * w;
+
+    // A fragments: x = k - mu for 4 row tiles, dims 32g .. 32g+31.
+    float a[4][32];
+    {
+        float m[32];
+        const float *mp = mu + int64_t(bh) * kD + 32 * g;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float4 v = *reinterpret_cast<const float4 *>(mp + 4 * q);
+            m[4 * q] = v.x; m[4 * q + 1] = v.y; m[4 * q + 2] = v.z; m[4 * q + 3] = v.w;
+        }
+        const T *base = keys + b * sb + h * sh + 32 * g;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int64_t row = k0 + 16 * rt + il;
+            if (row < n) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float v[8];
+                    Row8<T>::load(base + row * sn + 8 * q, v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a[rt][8 * q + e] = v[e] - m[8 * q + e];
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 32; ++s) a[rt][s] = 0.0f;
+            }
+        }
+    }
+
+    const float4 *wp4 = reinterpret_cast<const float4 *>(Wp);
+    float4 pre0 = wp4[t], pre1 = wp4[256 + t];
+    wbuf[t] = pre0;
+    wbuf[256 + t] = pre1;
+    __syncthreads();
+
+    uint16_t *mybits = bits + int64_t(w) * 64 * pstride;
+    for (int ct = 0; ct < NT; ++ct) {
+        if (ct + 1 < NT) {
+            pre0 = wp4[int64_t(ct + 1) * 512 + t];
+            pre1 = wp4[int64_t(ct + 1) * 512 + 256 + t];
+        }
+        const float4 *cur = wbuf + (ct & 1) * 512;
+        float bf[32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float4 v = cur[q * 64 + lane];
+            bf[4 * q] = v.x; bf[4 * q + 1] = v.y; bf[4 * q + 2] = v.z; bf[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 32; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt][s], bf[s], acc, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const unsigned long long m = __ballot(acc[r] > 0.0f);
+                if (lane < 4)
+                    mybits[(16 * rt + 4 * lane + r) * pstride + ct] =
+                        uint16_t((m >> (16 * lane)) & 0xFFFFu);
+            }
+        }
+        if (ct + 1 < NT) {
+            wbuf[((ct + 1) & 1) * 512 + t] = pre0;
+            wbuf[((ct + 1) & 1) * 512 + 256 + t] = pre1;
+        }
+        __syncthreads();
+    }
+
+    // Cut table codes out of the bit rows: lane = key.
+    const int64_t key = k0 + lane;
+    const int chunk = int(key / kChunk), within = int(key % kChunk);
+    uint16_t *cout = codes + (int64_t(bh) * n_chunks + chunk) * int64_t(L) * kChunk + within;
+    const uint16_t *row = mybits + lane * pstride;
+    const uint32_t kmask = (1u << K) - 1u;
+    for (int l = 0; l < L; ++l) {
+        const int pos = l * K, t0 = pos >> 4, o = pos & 15;
+        const uint32_t lo = row[t0];
+        const uint32_t hi = (t0 + 1 < NT) ? uint32_t(row[t0 + 1]) : 0u;
+        cout[int64_t(l) * kChunk] = uint16_t(((lo | (hi << 16)) >> o) & kmask);
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_u16_kernel(uint16_t *p, int64_t count)
+{
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+         i += int64_t(gridDim.x) * blockDim.x)
+        p[i] = 0;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_wgen(uint64_t seed, int32_t R, int32_t R_pad, float *W, float *Wp, hipStream_t s)
+{
+    const int64_t total = int64_t(R_pad) * kD;
+    wgen_kernel<<<dim3(ceil_div(total, 256)), dim3(256), 0, s>>>(seed, R, R_pad, W, Wp);
+    return hipGetLastError();
+}
+
+hipError_t launch_mean(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
+                       int32_t nmb, double *mu_part, float *mu, hipStream_t s)
+{
+    const dim3 grid(nmb, B * H);
+    if (dtype == MP_BF16)
+        mean_partial_kernel<uint16_t><<<grid, 256, 0, s>>>(
+            static_cast<const uint16_t *>(keys.data), keys.sb, keys.sh, keys.sn, H, n, nmb, mu_part);
+    else
+        mean_partial_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(keys.data),
+                                                        keys.sb, keys.sh, keys.sn, H, n, nmb,
+                                                        mu_part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    mean_final_kernel<<<dim3(B * H), dim3(kD), 0, s>>>(mu_part, nmb, n, mu);
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
+                              int32_t n_chunks, const float *mu, const float *Wp, int32_t K,
+                              int32_t L, int32_t R_pad, uint16_t *codes, hipStream_t s)
+{
+    const int32_t NT = R_pad / 16;
+    const int32_t pstride = NT + ((6 - NT % 4) % 4);   // pstride % 4 == 2: odd dword stride
+    const size_t shmem = size_t(2) * 512 * 16 + size_t(4) * 64 * pstride * 2;
+    const dim3 grid(n_chunks * (kChunk / 256), B * H);
+    hipError_t e;
+    if (dtype == MP_BF16) {
+        auto fn = encode_keys_kernel<uint16_t>;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
+        if (e != hipSuccess) return e;
+        fn<<<grid, 256, shmem, s>>>(static_cast<const uint16_t *>(keys.data), keys.sb, keys.sh,
+                                    keys.sn, H, n, n_chunks, mu, Wp, K, L, NT, pstride, codes);
+    } else {
+        auto fn = encode_keys_kernel<float>;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
+        if (e != hipSuccess) return e;
+        fn<<<grid, 256, shmem, s>>>(static_cast<const float *>(keys.data), keys.sb, keys.sh,
+                                    keys.sn, H, n, n_chunks, mu, Wp, K, L, NT, pstride, codes);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u16(uint16_t *p, int64_t count, hipStream_t s)
+{
+    int64_t blocks = (count + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    fill_u16_kernel<<<dim3(uint32_t(blocks)), 256, 0, s>>>(p, count);
+    return hipGetLastError();
+}
+
+}  // namespace mp

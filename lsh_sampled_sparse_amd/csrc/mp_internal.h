@@ -1,0 +1,87 @@
+// mp_internal.h -- types and launchers shared by the HIP sources of libmagicpig.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/magicpig.h"
+
+namespace mp {
+
+constexpr int kD = 128;            // head dimension
+constexpr int kChunk = MP_CHUNK;   // keys per scan chunk: 64 lanes x 8 keys
+constexpr int kMeanRows = 1024;    // keys per partial-sum block of the mean pass
+constexpr uint64_t kMagic = 0x4D50494458303031ULL;  // "MPIDX001"
+
+inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+inline int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
+
+// Workspace layout of an index (all offsets 256-byte aligned).
+struct IndexLayout {
+    int32_t B, H_kv, n, n_pad, n_chunks, n_mean_blocks, K, L, R, R_pad;
+    int64_t off_W, off_Wp, off_mu, off_mu_part, off_codes, total;
+};
+IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t L);
+
+struct mp_index_impl {
+    uint64_t magic;
+    IndexLayout lay;
+    uint64_t seed;
+    int32_t key_dtype;
+    int device;
+    float *W;        // [R_pad][128] canonical (rows >= R are zero)
+    float *Wp;       // [R_pad/16][8][64][4] MFMA B-fragment order
+    float *mu;       // [B*H_kv][128]
+    double *mu_part; // [B*H_kv][n_mean_blocks][128]
+    uint16_t *codes; // [B*H_kv][n_chunks][L][kChunk]
+};
+
+// Decode scratch layout.
+struct DecodeLayout {
+    int32_t BHq, n_chunks;
+    int64_t off_qcodes, off_qq, off_qnorm, off_part, off_seg_idx, off_seg_cnt, total;
+};
+DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q);
+
+// Row addressing of a [B][H][n][128] view.
+struct KVRows {
+    const void *data;
+    int64_t sb, sh, sn;   // element strides
+    int32_t H;
+};
+
+// ---- launchers (return hipSuccess or the launch error) ----
+hipError_t launch_wgen(uint64_t seed, int32_t R, int32_t R_pad, float *W, float *Wp, hipStream_t s);
+hipError_t launch_mean(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
+                       int32_t n_mean_blocks, double *mu_part, float *mu, hipStream_t s);
+hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
+                              int32_t n_chunks, const float *mu, const float *Wp, int32_t K,
+                              int32_t L, int32_t R_pad, uint16_t *codes, hipStream_t s);
+hipError_t launch_fill_u16(uint16_t *p, int64_t count, hipStream_t s);
+
+struct DecodeArgs {
+    const float *q;          // [BHq][128]
+    int32_t B, H_q, H_kv, G, n, n_chunks, K, L;
+    int32_t n_sink, n_local;
+    float scale;
+    const float *W;          // [R][128]
+    const float *mu;         // [B*H_kv][128]
+    const uint16_t *codes;   // index codes
+    KVRows k, v;
+    int32_t dtype;
+    uint16_t *qcodes;        // scratch [BHq][L]
+    uint32_t *qq;            // scratch [BHq][L], code | code << 16
+    float *qnorm;            // scratch [BHq], |q|
+    float *part;             // scratch [B*H_kv][n_chunks][G][kD + 2] chunk partials
+    int32_t *seg_idx;        // scratch [BHq][n_chunks * kChunk] (debug only)
+    int32_t *seg_cnt;        // scratch [BHq][n_chunks] (debug only)
+    float *out;              // [BHq][128]
+    uint8_t *counts;         // optional [BHq][n]
+    int32_t *s_idx;          // optional [BHq][n]
+    int32_t *s_len;          // optional [BHq]
+    bool debug;
+    hipEvent_t ev_begin, ev_end;   // optional, recorded around scan_gather
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+}  // namespace mp

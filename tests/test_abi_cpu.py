@@ -1,0 +1,113 @@
+"""The C ABI library loads, exports every function include/magicpig.h declares,
+and rejects bad arguments on the host before touching the GPU (CPU only: no
+compute call is made)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from lsh_sampled_sparse_amd import capi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "magicpig.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mp_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = capi.lib()
+    names = _declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(capi.EXPORTED)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert capi.mp_status_str(s).startswith("MP_")
+    assert "unknown" in capi.mp_status_str(99)
+
+
+def test_workspace_bytes_rejects_bad_sizes_and_covers_codes():
+    f = capi.mp_index_workspace_bytes
+    assert f(1, 8, 98304, 64, 10, 150) == 0       # d != 128
+    assert f(1, 8, 98304, 128, 17, 150) == 0      # K > 16
+    assert f(1, 8, 98304, 128, 10, 1) == 0        # L < 2
+    assert f(1, 8, 98304, 128, 10, 256) == 0      # L > 255
+    assert f(0, 8, 98304, 128, 10, 150) == 0
+    assert f(1, 8, 0, 128, 10, 150) == 0
+    a = f(1, 8, 98304, 128, 10, 150)
+    assert a >= 8 * 98304 * 150 * 2 and a % 256 == 0
+    assert f(1, 8, 98305, 128, 10, 150) > a                 # ragged tail pads a chunk
+    assert f(1, 8, 1, 128, 0, 2) > 0                         # K = 0 is allowed
+
+
+def _view(**kw):
+    v = dict(data=0x10000, dtype=capi.MP_BF16, B=1, H=2, n=1000, d=128, stride_b=2 * 1000 * 128,
+             stride_h=1000 * 128, stride_n=128)
+    v.update(kw)
+    return capi.mp_kv_view(**v)
+
+
+@pytest.mark.parametrize("kw,K,L,status", [
+    (dict(data=None), 10, 150, capi.MP_E_ARG),
+    (dict(dtype=7), 10, 150, capi.MP_E_DTYPE),
+    (dict(d=64), 10, 150, capi.MP_E_SHAPE),
+    (dict(n=0), 10, 150, capi.MP_E_SHAPE),
+    (dict(stride_n=100), 10, 150, capi.MP_E_SHAPE),
+    (dict(data=0x10002), 10, 150, capi.MP_E_SHAPE),      # misaligned rows
+    (dict(stride_n=129), 10, 150, capi.MP_E_SHAPE),      # 258-byte bf16 rows
+    (dict(), 17, 150, capi.MP_E_ARG),
+    (dict(), -1, 150, capi.MP_E_ARG),
+    (dict(), 10, 1, capi.MP_E_ARG),
+    (dict(), 10, 300, capi.MP_E_ARG),
+])
+def test_build_index_rejects_bad_arguments(kw, K, L, status):
+    out = C.c_void_p(123)
+    st = capi.lib().mp_build_index(C.byref(_view(**kw)), K, L, 0, 0x100000, 1 << 40, None,
+                                   C.byref(out))
+    assert st == status, capi.mp_last_error()
+    assert out.value is None
+    assert capi.mp_last_error() != ""
+
+
+def test_build_index_rejects_bad_workspace():
+    out = C.c_void_p()
+    v = _view()
+    need = capi.mp_index_workspace_bytes(1, 2, 1000, 128, 10, 150)
+    L = capi.lib()
+    assert L.mp_build_index(C.byref(v), 10, 150, 0, None, need, None, C.byref(out)) == capi.MP_E_WORKSPACE
+    assert L.mp_build_index(C.byref(v), 10, 150, 0, 0x100010, need, None, C.byref(out)) == capi.MP_E_WORKSPACE
+    assert L.mp_build_index(C.byref(v), 10, 150, 0, 0x100000, need - 1, None, C.byref(out)) == capi.MP_E_WORKSPACE
+    assert "needed" in capi.mp_last_error()
+    assert L.mp_build_index(C.byref(v), 10, 150, 0, 0x100000, need, None, None) == capi.MP_E_ARG
+
+
+def test_decode_rejects_dead_handles():
+    L = capi.lib()
+    fake = (C.c_uint8 * 4096)()          # zeroed host memory: no magic number
+    v = _view()
+    for h in (None, C.addressof(fake)):
+        st = L.mp_decode_attn(0x1000, 8, h, C.byref(v), C.byref(v), 4, 64, 0.0, 0x2000, 0x3000,
+                              1 << 30, None)
+        assert st == capi.MP_E_HANDLE
+    assert capi.mp_decode_scratch_bytes(None, 8) == 0
+    assert capi.mp_decode_scratch_bytes(C.addressof(fake), 8) == 0
+    W, mu, codes, n_pad = C.c_void_p(), C.c_void_p(), C.c_void_p(), C.c_int32()
+    assert L.mp_index_views(None, C.byref(W), C.byref(mu), C.byref(codes), C.byref(n_pad)) == capi.MP_E_HANDLE
+    L.mp_index_destroy(None)            # ignored
+
+
+def test_python_layer_fails_loudly_without_library(tmp_path, monkeypatch):
+    import importlib
+    monkeypatch.setattr(capi, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(capi, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        capi.lib()
