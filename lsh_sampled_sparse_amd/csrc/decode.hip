@@ -33,7 +33,7 @@ namespace mp {
 namespace {
 
 constexpr int kPart = kD + 2;     // partial softmax: m, l, acc[128]
-constexpr int kRowsPerGroup = 2;  // listed rows a 16-lane group holds per round
+constexpr int kRowsPerGroup = 4;  // listed rows a 16-lane group holds per round
 constexpr int kRound = 16 * kRowsPerGroup;
 
 // ---------------------------------------------------------------- helpers
@@ -52,6 +52,17 @@ template <> struct Row8<float> {
         o[0] = r.a.x; o[1] = r.a.y; o[2] = r.a.z; o[3] = r.a.w;
         o[4] = r.b.x; o[5] = r.b.y; o[6] = r.b.z; o[7] = r.b.w;
     }
+    static __device__ __forceinline__ void store_raw(float *p, const raw &r)
+    {
+        reinterpret_cast<float4 *>(p)[0] = r.a;
+        reinterpret_cast<float4 *>(p)[1] = r.b;
+    }
+    static __device__ __forceinline__ void load_pair(const float *p, float &v0, float &v1)
+    {
+        const float2 v = *reinterpret_cast<const float2 *>(p);
+        v0 = v.x;
+        v1 = v.y;
+    }
 };
 template <> struct Row8<uint16_t> {
     using raw = uint4;
@@ -65,6 +76,16 @@ template <> struct Row8<uint16_t> {
         o[2] = bf16_to_f32(a.y & 0xFFFFu); o[3] = bf16_to_f32(a.y >> 16);
         o[4] = bf16_to_f32(a.z & 0xFFFFu); o[5] = bf16_to_f32(a.z >> 16);
         o[6] = bf16_to_f32(a.w & 0xFFFFu); o[7] = bf16_to_f32(a.w >> 16);
+    }
+    static __device__ __forceinline__ void store_raw(uint16_t *p, const raw &r)
+    {
+        *reinterpret_cast<uint4 *>(p) = r;
+    }
+    static __device__ __forceinline__ void load_pair(const uint16_t *p, float &v0, float &v1)
+    {
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+        v0 = bf16_to_f32(v & 0xFFFFu);
+        v1 = bf16_to_f32(v >> 16);
     }
 };
 
@@ -182,12 +203,13 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     __shared__ uint32_t red[G][256];         // packed mismatch counts, word = 2 keys
     __shared__ uint32_t ulist[kChunk];       // key | headmask << 16 | exact << 24
     __shared__ int wsum[4];
-    __shared__ float st[4][G][kPart];
     __shared__ __align__(16) float sq[G][kD];   // the group's queries
     __shared__ float sqn[G];                 // their norms
     __shared__ __align__(16) float smu[kD];  // mean of the head's keys
     __shared__ float srow[kRound][2 * G + 1];   // per listed row: q.k, q.(k-mu), |k-mu|^2
-    __shared__ float sz[kRound][G];          // per (row, head): z, or -inf if not taken
+    __shared__ float sw[kRound][G];          // per (row, head): exp(z - running max) or 0
+    __shared__ __align__(16) T sv[kRound][kD];  // the round's V rows
+    __shared__ float smax[G], slsum[G], sscale[G];   // running max / sum, last rescale
 
     const int chunk = blockIdx.x;
     const int bkv = blockIdx.y;
@@ -201,6 +223,10 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     for (int i = t; i < G * kD; i += 256) sq[i / kD][i % kD] = a.q[int64_t(bhq0) * kD + i];
     if (t < G) sqn[t] = a.qnorm[bhq0 + t];
     if (t < kD) smu[t] = a.mu[int64_t(bkv) * kD + t];
+    if (t < G) {
+        smax[t] = -INFINITY;
+        slsum[t] = 0.0f;
+    }
 
     // ---- (a) collision counts: wave w scans tables [w L/4, (w+1) L/4) ----
     for (int i = t; i < G * 256; i += 256) (&red[0][0])[i] = 0u;
@@ -321,28 +347,20 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     }
     __syncthreads();   // ulist complete
 
-    // ---- (c) gather + online softmax, in rounds of up to 64 listed rows ----
-    // c1: 16 groups of 16 lanes, lane = 8 dims; group gi loads rows
-    //     gi, gi+16, gi+32, gi+48 of the round (all loads issued first) and
-    //     reduces q_g.k, q_g.(k - mu) and |k - mu|^2 into LDS;
-    // c2: one thread per (row, head) evaluates z once;
-    // c3: each group folds its rows' z and V rows into its running softmax.
+    // ---- (c) gather + online softmax, in rounds of up to kRound listed rows ----
+    // c1: 16 groups of 16 lanes, lane = 8 dims; group gi takes rows gi, gi+16,
+    //     ... of the round (all loads issued first), reduces q_g.k,
+    //     q_g.(k - mu) and |k - mu|^2 into srow and stages the V row in LDS;
+    // c2: wave w takes heads w, w+4, ...; lane e evaluates z of row e once,
+    //     and the wave forms the round's max, the weights exp(z - M) and their
+    //     sum (running max / sum per head live in LDS);
+    // c3: thread = (head, pair of dims): it rescales its accumulator and adds
+    //     the round's weighted V rows.
     const int gi = t >> 4, li = t & 15;
-    float mu8[8];
-    {
-        const float4 m0 = reinterpret_cast<const float4 *>(smu)[2 * li];
-        const float4 m1 = reinterpret_cast<const float4 *>(smu)[2 * li + 1];
-        mu8[0] = m0.x; mu8[1] = m0.y; mu8[2] = m0.z; mu8[3] = m0.w;
-        mu8[4] = m1.x; mu8[5] = m1.y; mu8[6] = m1.z; mu8[7] = m1.w;
-    }
-    float m_run[G], l_run[G], acc[G][8];
+    constexpr int kPairs = (G * (kD / 2) + 255) / 256;
+    float acc0[kPairs], acc1[kPairs];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m_run[g] = -INFINITY;
-        l_run[g] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[g][j] = 0.0f;
-    }
+    for (int p = 0; p < kPairs; ++p) acc0[p] = acc1[p] = 0.0f;
     const T *kb = static_cast<const T *>(a.k.data) + b * a.k.sb + h * a.k.sh + 8 * li;
     const T *vb = static_cast<const T *>(a.v.data) + b * a.v.sb + h * a.v.sh + 8 * li;
     const float inv_pi = 0.31830988618379067f;
@@ -358,10 +376,14 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
                 vraw[r] = Row8<T>::load_raw(vb + i * a.v.sn);
             }
         }
+        const float4 m0 = reinterpret_cast<const float4 *>(smu)[2 * li];
+        const float4 m1 = reinterpret_cast<const float4 *>(smu)[2 * li + 1];
+        const float mu8[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
         for (int r = 0; r < kRowsPerGroup; ++r) {
             const int e = gi + 16 * r;
             if (e >= ne) continue;            // uniform over the 16-lane group
+            Row8<T>::store_raw(&sv[e][8 * li], vraw[r]);
             float kr[8], x[8];
             Row8<T>::convert(kraw[r], kr);
             float xx = 0.0f;
@@ -404,96 +426,74 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
             }
         }
         __syncthreads();
-        for (int pidx = t; pidx < ne * G; pidx += 256) {
-            const int e = pidx / G, g = pidx % G;
-            const uint32_t ent = ulist[base + e];
-            const bool exact = (ent >> 24) & 1u;
+        for (int g = w; g < G; g += 4) {
             float z = -INFINITY;
-            if (exact || ((ent >> (16 + g)) & 1u)) {
-                z = srow[e][g] * a.scale;
-                if (!exact) {
-                    const float den = sqn[g] * sqrtf(srow[e][2 * G]);
-                    float cs = den > 0.0f ? srow[e][G + g] / den : 0.0f;
-                    cs = fminf(fmaxf(cs, -1.0f), 1.0f);
-                    const float p = 1.0f - acosf(cs) * inv_pi;
-                    z -= log_u_f32(p, a.K, L);
+            if (lane < ne) {
+                const uint32_t ent = ulist[base + lane];
+                const bool exact = (ent >> 24) & 1u;
+                if (exact || ((ent >> (16 + g)) & 1u)) {
+                    z = srow[lane][g] * a.scale;
+                    if (!exact) {
+                        const float den = sqn[g] * sqrtf(srow[lane][2 * G]);
+                        float cs = den > 0.0f ? srow[lane][G + g] / den : 0.0f;
+                        cs = fminf(fmaxf(cs, -1.0f), 1.0f);
+                        const float p = 1.0f - acosf(cs) * inv_pi;
+                        z -= log_u_f32(p, a.K, L);
+                    }
                 }
             }
-            sz[e][g] = z;
+            float M = z;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+            const float m_old = smax[g];
+            const float m_new = fmaxf(m_old, M);
+            const float wgt = z == -INFINITY ? 0.0f : __expf(z - m_new);
+            float ls = wgt;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) ls += __shfl_xor(ls, off);
+            if (lane < ne) sw[lane][g] = wgt;
+            if (lane == 0) {
+                const float sc = m_new == -INFINITY ? 1.0f : __expf(m_old - m_new);
+                sscale[g] = sc;
+                slsum[g] = slsum[g] * sc + ls;
+                smax[g] = m_new;
+            }
         }
         __syncthreads();
 #pragma unroll
-        for (int r = 0; r < kRowsPerGroup; ++r) {
-            const int e = gi + 16 * r;
-            if (e >= ne) continue;
-            float vr[8];
-            Row8<T>::convert(vraw[r], vr);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float z = sz[e][g];
-                if (z == -INFINITY) continue;
-                const float mn = fmaxf(m_run[g], z);
-                const float al = __expf(m_run[g] - mn);
-                const float be = __expf(z - mn);
-                l_run[g] = l_run[g] * al + be;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[g][j] = fmaf(acc[g][j], al, be * vr[j]);
-                m_run[g] = mn;
+        for (int p = 0; p < kPairs; ++p) {
+            const int idx = t + 256 * p;
+            if (idx < G * (kD / 2)) {
+                const int g = idx / (kD / 2), dp = idx % (kD / 2);
+                const float sc = sscale[g];
+                float x0 = acc0[p] * sc, x1 = acc1[p] * sc;
+                for (int e = 0; e < ne; ++e) {
+                    const float wg = sw[e][g];
+                    float v0, v1;
+                    Row8<T>::load_pair(&sv[e][2 * dp], v0, v1);
+                    x0 = fmaf(wg, v0, x0);
+                    x1 = fmaf(wg, v1, x1);
+                }
+                acc0[p] = x0;
+                acc1[p] = x1;
             }
         }
-        __syncthreads();   // srow/sz are rewritten by the next round
+        __syncthreads();   // srow, sw, sv are rewritten by the next round
     }
 
-    // ---- combine the 4 groups of a wave (lanes l, l^16, l^32) ----
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mo = __shfl_xor(m_run[g], off);
-            const float lo = __shfl_xor(l_run[g], off);
-            float ao[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) ao[j] = __shfl_xor(acc[g][j], off);
-            const float mn = fmaxf(m_run[g], mo);
-            if (mn != -INFINITY) {
-                const float al = __expf(m_run[g] - mn), be = __expf(mo - mn);
-                l_run[g] = l_run[g] * al + lo * be;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[g][j] = acc[g][j] * al + ao[j] * be;
-                m_run[g] = mn;
-            }
-        }
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) st[w][g][2 + 8 * li + j] = acc[g][j];
-            if (li == 0) {
-                st[w][g][0] = m_run[g];
-                st[w][g][1] = l_run[g];
-            }
-        }
-    }
-    __syncthreads();
-    // ---- combine the 4 waves into this chunk's partial ----
+    // ---- this chunk's partial: (max, sum, unnormalised accumulator) per head ----
     float *part0 = a.part + (int64_t(bkv) * a.n_chunks + chunk) * (G * kPart);
-    for (int idx = t; idx < G * kD; idx += 256) {
-        const int g = idx / kD, c = idx % kD;
-        float M = st[0][g][0];
-        for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, st[ww][g][0]);
-        float lsum = 0.0f, av = 0.0f;
-        if (M != -INFINITY) {
-            for (int ww = 0; ww < 4; ++ww) {
-                const float f = __expf(st[ww][g][0] - M);
-                lsum += st[ww][g][1] * f;
-                av += st[ww][g][2 + c] * f;
+#pragma unroll
+    for (int p = 0; p < kPairs; ++p) {
+        const int idx = t + 256 * p;
+        if (idx < G * (kD / 2)) {
+            const int g = idx / (kD / 2), dp = idx % (kD / 2);
+            part0[g * kPart + 2 + 2 * dp] = acc0[p];
+            part0[g * kPart + 3 + 2 * dp] = acc1[p];
+            if (dp == 0) {
+                part0[g * kPart] = smax[g];
+                part0[g * kPart + 1] = slsum[g];
             }
-        }
-        part0[g * kPart + 2 + c] = av;
-        if (c == 0) {
-            part0[g * kPart] = M;
-            part0[g * kPart + 1] = lsum;
         }
     }
 }
