@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a device copy of 256 MiB (read + write), the known-size "
+                         "reference for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -168,6 +171,14 @@ def main():
             capi.mp_decode_attn_timed(q.data_ptr(), cfg.H_q, idx.handle, kv_k, kv_v,
                                       cfg.n_sink, cfg.n_local, 0.0, out.data_ptr(),
                                       scratch.data_ptr(), scratch.numel(), sh, eb, ee)
+
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         step(i)

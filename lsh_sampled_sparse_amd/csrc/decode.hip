@@ -35,6 +35,10 @@ namespace {
 constexpr int kPart = kD + 2;     // partial softmax: m, l, acc[128]
 constexpr int kRowsPerGroup = 4;  // listed rows a 16-lane group holds per round
 constexpr int kRound = 16 * kRowsPerGroup;
+#ifndef MP_SCAN_BATCH
+#define MP_SCAN_BATCH 4
+#endif
+constexpr int kScanBatch = MP_SCAN_BATCH;   // tables per code batch in the scan
 
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -195,12 +199,16 @@ __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restri
 // Waves per SIMD the register budget is cut for: 4 up to G = 4 (fp32 rows at
 // G = 4 would spill there), 2 for G = 8.
 template <int G, typename T>
-constexpr int scan_occupancy() { return G <= 2 || (G == 4 && sizeof(T) == 2) ? 4 : (G == 4 ? 3 : 2); }
+#ifndef MP_SCAN_OCC4
+#define MP_SCAN_OCC4 4
+#endif
+constexpr int scan_occupancy() { return G <= 2 || (G == 4 && sizeof(T) == 2) ? MP_SCAN_OCC4 : (G == 4 ? 3 : 2); }
 
 template <int G, typename T>
 __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_kernel(DecodeArgs a)
 {
     __shared__ uint32_t red[G][256];         // packed mismatch counts, word = 2 keys
+    __shared__ __align__(16) uint32_t sqq[256][G];   // query codes, code | code << 16
     __shared__ uint32_t ulist[kChunk];       // key | headmask << 16 | exact << 24
     __shared__ int wsum[4];
     __shared__ __align__(16) float sq[G][kD];   // the group's queries
@@ -227,6 +235,11 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         smax[t] = -INFINITY;
         slsum[t] = 0.0f;
     }
+    // The group's query codes, [table][head], read back as one broadcast per
+    // table.  (Read from global memory inside the scan, these loads would
+    // queue behind the prefetched code batch and stall on it.)
+    for (int i = t; i < G * L; i += 256) sqq[i % L][i / L] = a.qq[int64_t(bhq0) * L + i];
+    __syncthreads();
 
     // ---- (a) collision counts: wave w scans tables [w L/4, (w+1) L/4) ----
     for (int i = t; i < G * 256; i += 256) (&red[0][0])[i] = 0u;
@@ -234,7 +247,6 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         const uint4 *cp = reinterpret_cast<const uint4 *>(
                               a.codes + (int64_t(bkv) * a.n_chunks + chunk) * int64_t(L) * kChunk) +
                           lane;
-        const uint32_t *qqp = a.qq + int64_t(bhq0) * L;
         const uint32_t one2 = 0x00010001u;
         uint32_t mism[4][G];
 #pragma unroll
@@ -242,36 +254,40 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
 #pragma unroll
             for (int g = 0; g < G; ++g) mism[k][g] = 0u;
         const int lb = uniform((w * L) / 4), le = uniform(((w + 1) * L) / 4);
-        // Batches of 8 tables, the next batch in flight while this one is
-        // counted; a short last batch re-reads table le-1 and skips it.
-        uint4 cur[8], nxt[8];
-        if (lb < le) {
+        // Batches of kScanBatch tables in two alternating register buffers: while one
+        // batch is counted the next is in flight.  (A copy from a prefetch
+        // buffer into a "current" one would make every batch wait for its
+        // successor's loads.)  A short last batch re-reads table le-1; its
+        // extra entries are masked out of the count.
+        uint4 bufA[kScanBatch], bufB[kScanBatch];
+        auto load_batch = [&](uint4 (&buf)[kScanBatch], int l0) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) cur[u] = cp[int64_t(min(lb + u, le - 1)) * (kChunk / 8)];
-        }
-        for (int l0 = lb; l0 < le; l0 += 8) {
-            if (l0 + 8 < le) {
+            for (int u = 0; u < kScanBatch; ++u)
+                buf[u] = cp[int64_t(min(l0 + u, le - 1)) * (kChunk / 8)];
+        };
+        auto count_batch = [&](const uint4 (&buf)[kScanBatch], int l0) {
+            const int nv = min(kScanBatch, le - l0);
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    nxt[u] = cp[int64_t(min(l0 + 8 + u, le - 1)) * (kChunk / 8)];
-            }
-            const int nv = min(8, le - l0);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < kScanBatch; ++u) {
                 // a re-read table (u >= nv) adds min(x, 0) = 0 mismatches
                 const uint32_t lim = u < nv ? one2 : 0u;
                 const int lu = min(l0 + u, le - 1);
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const uint32_t qv = qqp[g * L + lu];
-                    mism[0][g] += pk_min_u16(cur[u].x ^ qv, lim);
-                    mism[1][g] += pk_min_u16(cur[u].y ^ qv, lim);
-                    mism[2][g] += pk_min_u16(cur[u].z ^ qv, lim);
-                    mism[3][g] += pk_min_u16(cur[u].w ^ qv, lim);
+                    const uint32_t qv = sqq[lu][g];
+                    mism[0][g] += pk_min_u16(buf[u].x ^ qv, lim);
+                    mism[1][g] += pk_min_u16(buf[u].y ^ qv, lim);
+                    mism[2][g] += pk_min_u16(buf[u].z ^ qv, lim);
+                    mism[3][g] += pk_min_u16(buf[u].w ^ qv, lim);
                 }
             }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
+        };
+        if (lb < le) load_batch(bufA, lb);
+        for (int l0 = lb; l0 < le; l0 += 2 * kScanBatch) {
+            if (l0 + kScanBatch < le) load_batch(bufB, l0 + kScanBatch);
+            count_batch(bufA, l0);
+            if (l0 + 2 * kScanBatch < le) load_batch(bufA, l0 + 2 * kScanBatch);
+            if (l0 + kScanBatch < le) count_batch(bufB, l0 + kScanBatch);
         }
         __syncthreads();   // red zeroed
         // Each half counts at most 255 tables, so a 32-bit add of the packed
