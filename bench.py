@@ -28,6 +28,20 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, published
 METRIC = "decode attn steps/s + achieved HBM GB/s (% peak), 1 layer, 96K ctx, K=10 L=150"
+DECODE_SRC = os.path.join(ROOT, "lsh_sampled_sparse_amd", "csrc", "decode.hip")
+
+# HBM bytes per scan_gather launch read from hardware counters with rocprofv3
+# (FETCH_SIZE and WRITE_SIZE in two separate --pmc runs of this script with
+# --calib-copy), each counter scaled by the factor that makes it read the
+# known bytes of the 256 MiB fp32 negation that --calib-copy runs in the same
+# process.  Valid only for the kernel source they were taken on: reported as
+# null once decode.hip no longer hashes to decode_hip_sha256.
+MEASURED_TRAFFIC = {
+    "decode_hip_sha256": "6140eeeb73ff2c81a1bce0019015afd2b9f7ff07e9cafd9e22fabf85cc8908b9",
+    "fetch_kib": 126719.7, "fetch_scale": 1.9999,
+    "write_kib": 3316.7, "write_scale": 1.0000,
+    "bytes_per_launch": 262904585,
+}
 
 
 def scan_bytes_per_launch(cfg, union_rows: int) -> int:
@@ -173,10 +187,13 @@ def main():
                                       scratch.data_ptr(), scratch.numel(), sh, eb, ee)
 
     if args.calib_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        # A kernel of known traffic for scaling hardware byte counters: an fp32
+        # negation reads 256 MiB and writes 256 MiB (a kernel name of its own,
+        # unlike a plain copy, which shares the runtime's copy kernel).
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(4):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -215,6 +232,13 @@ def main():
     flops_build = 2.0 * cfg.B * cfg.H_kv * cfg.n * cfg.d * cfg.K * cfg.L
     build_avg = sum(build_ms[1:]) / max(1, len(build_ms) - 1) if len(build_ms) > 1 else build_ms[0]
 
+    traffic = None
+    if MEASURED_TRAFFIC is not None:
+        import hashlib
+        with open(DECODE_SRC, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() == MEASURED_TRAFFIC["decode_hip_sha256"]:
+                traffic = MEASURED_TRAFFIC["bytes_per_launch"]
+
     cpu = None
     if not args.no_cpu_baseline:
         k, v, q = state[0][0], state[0][1], state[0][2]
@@ -246,7 +270,7 @@ def main():
         "mean_union_rows_per_layer": round(sum(union_rows) / len(union_rows), 1),
         "roofline": {"kernel": "scan_gather", "bound": "hbm", "achieved": round(scan_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(scan_avg_ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": round(scan_bytes / args.steps)},
         "index_build": {"ms_per_layer": round(build_avg, 3),
