@@ -132,10 +132,12 @@ mp_status mp_decode_debug(const float *q, int32_t H_q, const mp_index *idx,
                           void *scratch, size_t scratch_bytes, void *stream,
                           uint16_t *qcodes, uint8_t *counts, int32_t *s_idx, int32_t *s_len);
 
-/* mp_decode_attn that also records two caller-created hipEvent_t (passed as
- * void*, either may be NULL) on `stream` right before and right after the
- * fused collision-scan + gather kernel, so the caller can time that kernel on
- * its own.  Used by the benchmark; the output is that of mp_decode_attn. */
+/* mp_decode_attn that also stamps two caller-created hipEvent_t (passed as
+ * void*, either may be NULL) with the start and the end of the fused
+ * collision-scan + gather kernel (they are handed to the kernel's launch, so
+ * no other command sits between them and the kernel), so the caller can time
+ * that kernel on its own.  Used by the benchmark; the output is that of
+ * mp_decode_attn. */
 mp_status mp_decode_attn_timed(const float *q, int32_t H_q, const mp_index *idx,
                                const mp_kv_view *k, const mp_kv_view *v,
                                int32_t n_sink, int32_t n_local, float scale, float *out,

@@ -30,6 +30,7 @@
 //                  what makes the partials of blocks on other XCDs visible,
 //                  which an in-kernel device-scope fence would buy with an L2
 //                  write-back per block.
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "mp_internal.h"
@@ -768,7 +769,16 @@ hipError_t launch_scan_gather_t(const DecodeArgs &a, hipStream_t s)
     const int slots = resident_workgroups<G, T>();
     if (slots <= 0) return hipErrorInvalidDevice;
     const int32_t cpb = ceil_div(chunks, slots);
-    scan_gather_kernel<G, T><<<dim3(ceil_div(chunks, cpb)), 256, 0, s>>>(a, cpb);
+    const dim3 grid(ceil_div(chunks, cpb));
+    if (a.ev_begin || a.ev_end) {
+        // timed entry point: the runtime stamps the events at this kernel's
+        // own start and end
+        hipExtLaunchKernelGGL(scan_gather_kernel<G, T>, grid, dim3(256), 0, s,
+                              static_cast<hipEvent_t>(a.ev_begin),
+                              static_cast<hipEvent_t>(a.ev_end), 0, a, cpb);
+    } else {
+        scan_gather_kernel<G, T><<<grid, 256, 0, s>>>(a, cpb);
+    }
     return hipGetLastError();
 }
 
@@ -778,7 +788,6 @@ hipError_t launch_scan_gather(const DecodeArgs &a, hipStream_t s)
     hipError_t e = a.dtype == MP_BF16 ? launch_scan_gather_t<G, uint16_t>(a, s)
                                       : launch_scan_gather_t<G, float>(a, s);
     if (e != hipSuccess) return e;
-    if (a.ev_end && (e = hipEventRecord(a.ev_end, s)) != hipSuccess) return e;
     merge_kernel<G><<<dim3(a.B * a.H_kv * G, kD / 32), 1024, 0, s>>>(a.part, a.n_chunks, a.H_kv,
                                                                    a.H_q, a.out);
     return hipGetLastError();
@@ -794,7 +803,6 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
         a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.ev_begin && (e = hipEventRecord(a.ev_begin, s)) != hipSuccess) return e;
     switch (a.G) {
     case 1: e = launch_scan_gather<1>(a, s); break;
     case 2: e = launch_scan_gather<2>(a, s); break;
