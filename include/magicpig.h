@@ -144,6 +144,61 @@ mp_status mp_decode_attn_timed(const float *q, int32_t H_q, const mp_index *idx,
                                void *scratch, size_t scratch_bytes, void *stream,
                                void *ev_scan_begin, void *ev_scan_end);
 
+/* ---- Bucketed hash tables (the retrieval of the summary page's algorithm
+ * steps: the query's code selects one bucket per table, and the keys found in
+ * at least two buckets are sampled; page "MagicPIG: don't pick the tallest",
+ * section 6: one 32-bit token index per key and table).  They give the same
+ * sampled sets and outputs as mp_decode_attn, reading the query's L buckets
+ * instead of every key's codes.  Supported for K <= 12 and n <= 622,592. ---- */
+
+/* Bytes of the table workspace of an index (256-byte aligned):
+ *   offsets [B*H_kv][L][2^K + 1] uint32: bucket b of table l of unit u holds
+ *           entries [offsets[u][l][b], offsets[u][l][b+1]) of that table;
+ *   entries [B*H_kv][L][n] uint32: key indices grouped by bucket (their order
+ *           within a bucket is not fixed; nothing depends on it).
+ * 0 if the index cannot have tables (K > 12, n too large, not a live index). */
+size_t mp_tables_workspace_bytes(const mp_index *idx);
+
+/* Builds the tables of `idx` from its codes into `workspace` (caller-owned,
+ * at least mp_tables_workspace_bytes, 256-byte aligned, kept alive and
+ * unchanged while the index is used with the calls below) and attaches them
+ * to the index.  A later call rebuilds them into the new workspace.
+ * MP_E_SHAPE if the index cannot have tables. */
+mp_status mp_build_tables(mp_index *idx, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Scratch bytes of mp_decode_attn_tables / _timed / _debug for H_q query
+ * heads (0 if invalid).  Larger than mp_decode_scratch_bytes by the per-head
+ * collision bitmaps, 2 bits per key. */
+size_t mp_decode_tables_scratch_bytes(const mp_index *idx, int32_t H_q);
+
+/* mp_decode_attn through the tables built by mp_build_tables (MP_E_ARG if
+ * none); arguments, layouts and errors as for mp_decode_attn. */
+mp_status mp_decode_attn_tables(const float *q, int32_t H_q, const mp_index *idx,
+                                const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
+                                int32_t n_local, float scale, float *out, void *scratch,
+                                size_t scratch_bytes, void *stream);
+
+/* mp_decode_attn_tables that also stamps two caller-created hipEvent_t with
+ * the start and end of the gather kernel (as mp_decode_attn_timed does for
+ * the scan kernel).  Used by the benchmark. */
+mp_status mp_decode_attn_tables_timed(const float *q, int32_t H_q, const mp_index *idx,
+                                      const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
+                                      int32_t n_local, float scale, float *out, void *scratch,
+                                      size_t scratch_bytes, void *stream, void *ev_gather_begin,
+                                      void *ev_gather_end);
+
+/* mp_decode_tables with the debug views of mp_decode_debug, except that
+ * counts2[b][h][i] = min(collision count, 2): the tables only tell whether a
+ * key was seen once or at least twice. */
+mp_status mp_decode_tables_debug(const float *q, int32_t H_q, const mp_index *idx,
+                                 const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
+                                 int32_t n_local, float scale, float *out, void *scratch,
+                                 size_t scratch_bytes, void *stream, uint16_t *qcodes,
+                                 uint8_t *counts2, int32_t *s_idx, int32_t *s_len);
+
+/* Device pointers to the attached tables (layout above); MP_E_ARG if none. */
+mp_status mp_tables_views(const mp_index *idx, const uint32_t **offsets, const uint32_t **entries);
+
 /* Device pointers into the index workspace (valid while the workspace is):
  *   W     [R][128] fp32, R = K*L
  *   mu    [B][H_kv][128] fp32

@@ -16,8 +16,8 @@ import torch
 from . import capi
 from .capi import MPError, MP_CHUNK
 
-__all__ = ["MagicPIGIndex", "build_index", "decode_attn", "decode_debug", "kv_view", "capi",
-           "MPError", "MP_CHUNK"]
+__all__ = ["MagicPIGIndex", "build_index", "build_tables", "decode_attn", "decode_debug",
+           "decode_attn_tables", "decode_tables_debug", "kv_view", "capi", "MPError", "MP_CHUNK"]
 
 _DTYPES = {torch.float32: capi.MP_F32, torch.bfloat16: capi.MP_BF16}
 
@@ -53,6 +53,7 @@ class MagicPIGIndex:
         self.workspace = workspace
         self.B, self.H_kv, self.n, self.d = keys_shape
         self.K, self.L, self.seed, self.dtype = K, L, seed, dtype
+        self.tables = None      # table workspace, once build_tables ran
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -80,8 +81,25 @@ class MagicPIGIndex:
         ct = self._slice(codes, self.B * self.H_kv * nc * self.L * MP_CHUNK, torch.int16)
         return Wt, mut, ct.view(self.B, self.H_kv, nc, self.L, MP_CHUNK)
 
-    def scratch_bytes(self, H_q: int) -> int:
+    def scratch_bytes(self, H_q: int, tables: bool = False) -> int:
+        if tables:
+            return capi.mp_decode_tables_scratch_bytes(self.handle, H_q)
         return capi.mp_decode_scratch_bytes(self.handle, H_q)
+
+    def table_views(self):
+        """Device tensors aliasing the table workspace: offsets
+        [B][H_kv][L][2^K + 1] and entries [B][H_kv][L][n] (uint32 as int32)."""
+        off, ent = capi.mp_tables_views(self.handle)
+        nb = (1 << self.K) + 1
+        o = self._slice_of(self.tables, off, self.B * self.H_kv * self.L * nb, torch.int32)
+        e = self._slice_of(self.tables, ent, self.B * self.H_kv * self.L * self.n, torch.int32)
+        return (o.view(self.B, self.H_kv, self.L, nb), e.view(self.B, self.H_kv, self.L, self.n))
+
+    @staticmethod
+    def _slice_of(buf, ptr, numel, dtype):
+        off = ptr - buf.data_ptr()
+        esz = torch.empty(0, dtype=dtype).element_size()
+        return buf[off:off + numel * esz].view(dtype)
 
 
 def build_index(keys: torch.Tensor, K: int, L: int, seed: int, stream=None) -> MagicPIGIndex:
@@ -95,13 +113,25 @@ def build_index(keys: torch.Tensor, K: int, L: int, seed: int, stream=None) -> M
     return MagicPIGIndex(h, ws, tuple(keys.shape), K, L, seed, keys.dtype)
 
 
-def _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, debug):
+def build_tables(index: MagicPIGIndex, stream=None) -> MagicPIGIndex:
+    """Build the bucketed hash tables of `index` (see mp_build_tables); the
+    table workspace is kept on the index object."""
+    nbytes = capi.mp_tables_workspace_bytes(index.handle)
+    if nbytes == 0:
+        raise ValueError(f"this index cannot have tables (K={index.K}, n={index.n})")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=index.workspace.device)
+    capi.mp_build_tables(index.handle, ws.data_ptr(), nbytes, _stream(stream))
+    index.tables = ws
+    return index
+
+
+def _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, debug, tables=False):
     if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3:
         raise ValueError("q must be a contiguous [B][H_q][128] float32 tensor")
     B, H_q, d = q.shape
     if out is None:
         out = torch.empty(B, H_q, d, dtype=torch.float32, device=q.device)
-    need = index.scratch_bytes(H_q)
+    need = index.scratch_bytes(H_q, tables)
     if need == 0:
         raise ValueError(f"H_q={H_q} does not fit the index (H_kv={index.H_kv})")
     if scratch is None:
@@ -109,17 +139,19 @@ def _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, debug)
     kv_k, kv_v = kv_view(k), kv_view(v)
     s = _stream(stream)
     if not debug:
-        capi.mp_decode_attn(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local,
-                            float(scale), out.data_ptr(), scratch.data_ptr(), scratch.numel(), s)
+        f = capi.mp_decode_attn_tables if tables else capi.mp_decode_attn
+        f(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local, float(scale),
+          out.data_ptr(), scratch.data_ptr(), scratch.numel(), s)
         return out
     n = index.n
     qcodes = torch.empty(B, H_q, index.L, dtype=torch.int16, device=q.device)
     counts = torch.empty(B, H_q, n, dtype=torch.uint8, device=q.device)
     s_idx = torch.empty(B, H_q, n, dtype=torch.int32, device=q.device)
     s_len = torch.empty(B, H_q, dtype=torch.int32, device=q.device)
-    capi.mp_decode_debug(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local,
-                         float(scale), out.data_ptr(), scratch.data_ptr(), scratch.numel(), s,
-                         qcodes.data_ptr(), counts.data_ptr(), s_idx.data_ptr(), s_len.data_ptr())
+    f = capi.mp_decode_tables_debug if tables else capi.mp_decode_debug
+    f(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local, float(scale), out.data_ptr(),
+      scratch.data_ptr(), scratch.numel(), s, qcodes.data_ptr(), counts.data_ptr(),
+      s_idx.data_ptr(), s_len.data_ptr())
     return dict(out=out, qcodes=qcodes, counts=counts, s_idx=s_idx, s_len=s_len)
 
 
@@ -132,3 +164,15 @@ def decode_debug(q, index, k, v, n_sink, n_local, scale=0.0, out=None, scratch=N
                  stream=None):
     """decode_attn plus qcodes, counts, s_idx, s_len (see mp_decode_debug)."""
     return _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, True)
+
+
+def decode_attn_tables(q, index, k, v, n_sink, n_local, scale=0.0, out=None, scratch=None,
+                       stream=None):
+    """decode_attn through the bucketed tables (see mp_decode_attn_tables)."""
+    return _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, False, True)
+
+
+def decode_tables_debug(q, index, k, v, n_sink, n_local, scale=0.0, out=None, scratch=None,
+                        stream=None):
+    """decode_attn_tables plus qcodes, counts (min(count, 2)), s_idx, s_len."""
+    return _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, True, True)

@@ -20,6 +20,9 @@ MP_CHUNK = 512
 EXPORTED = [
     "mp_index_workspace_bytes", "mp_build_index", "mp_decode_scratch_bytes", "mp_decode_attn",
     "mp_decode_attn_timed", "mp_decode_debug", "mp_index_views", "mp_index_destroy", "mp_status_str", "mp_last_error",
+    "mp_tables_workspace_bytes", "mp_build_tables", "mp_decode_tables_scratch_bytes",
+    "mp_decode_attn_tables", "mp_decode_attn_tables_timed", "mp_decode_tables_debug",
+    "mp_tables_views",
 ]
 
 
@@ -65,6 +68,20 @@ def lib():
         L.mp_decode_attn_timed.argtypes = dec + [vp, vp]
         L.mp_decode_debug.restype = C.c_int
         L.mp_decode_debug.argtypes = dec + [vp, vp, vp, vp]
+        L.mp_tables_workspace_bytes.restype = sz
+        L.mp_tables_workspace_bytes.argtypes = [vp]
+        L.mp_build_tables.restype = C.c_int
+        L.mp_build_tables.argtypes = [vp, vp, sz, vp]
+        L.mp_decode_tables_scratch_bytes.restype = sz
+        L.mp_decode_tables_scratch_bytes.argtypes = [vp, i32]
+        L.mp_decode_attn_tables.restype = C.c_int
+        L.mp_decode_attn_tables.argtypes = dec
+        L.mp_decode_attn_tables_timed.restype = C.c_int
+        L.mp_decode_attn_tables_timed.argtypes = dec + [vp, vp]
+        L.mp_decode_tables_debug.restype = C.c_int
+        L.mp_decode_tables_debug.argtypes = dec + [vp, vp, vp, vp]
+        L.mp_tables_views.restype = C.c_int
+        L.mp_tables_views.argtypes = [vp, C.POINTER(vp), C.POINTER(vp)]
         L.mp_index_views.restype = C.c_int
         L.mp_index_views.argtypes = [vp, C.POINTER(vp), C.POINTER(vp), C.POINTER(vp),
                                      C.POINTER(i32)]
@@ -130,6 +147,47 @@ def mp_decode_debug(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scr
     st = lib().mp_decode_debug(q, H_q, idx, C.byref(k), C.byref(v), n_sink, n_local, scale, out,
                                scratch, scratch_bytes, stream, qcodes, counts, s_idx, s_len)
     _check(st, "mp_decode_debug")
+
+
+def mp_tables_workspace_bytes(idx: int) -> int:
+    return int(lib().mp_tables_workspace_bytes(idx))
+
+
+def mp_build_tables(idx: int, workspace: int, workspace_bytes: int, stream: int) -> None:
+    _check(lib().mp_build_tables(idx, workspace, workspace_bytes, stream), "mp_build_tables")
+
+
+def mp_decode_tables_scratch_bytes(idx: int, H_q: int) -> int:
+    return int(lib().mp_decode_tables_scratch_bytes(idx, H_q))
+
+
+def mp_decode_attn_tables(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
+                          stream) -> None:
+    st = lib().mp_decode_attn_tables(q, H_q, idx, C.byref(k), C.byref(v), n_sink, n_local, scale,
+                                     out, scratch, scratch_bytes, stream)
+    _check(st, "mp_decode_attn_tables")
+
+
+def mp_decode_attn_tables_timed(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch,
+                                scratch_bytes, stream, ev_gather_begin, ev_gather_end) -> None:
+    st = lib().mp_decode_attn_tables_timed(q, H_q, idx, C.byref(k), C.byref(v), n_sink, n_local,
+                                           scale, out, scratch, scratch_bytes, stream,
+                                           ev_gather_begin, ev_gather_end)
+    _check(st, "mp_decode_attn_tables_timed")
+
+
+def mp_decode_tables_debug(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch,
+                           scratch_bytes, stream, qcodes, counts2, s_idx, s_len) -> None:
+    st = lib().mp_decode_tables_debug(q, H_q, idx, C.byref(k), C.byref(v), n_sink, n_local,
+                                      scale, out, scratch, scratch_bytes, stream, qcodes, counts2,
+                                      s_idx, s_len)
+    _check(st, "mp_decode_tables_debug")
+
+
+def mp_tables_views(idx: int):
+    off, ent = C.c_void_p(), C.c_void_p()
+    _check(lib().mp_tables_views(idx, C.byref(off), C.byref(ent)), "mp_tables_views")
+    return off.value, ent.value
 
 
 def mp_index_views(idx: int):

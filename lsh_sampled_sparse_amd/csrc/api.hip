@@ -49,7 +49,7 @@ IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t 
     return y;
 }
 
-DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q)
+DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables)
 {
     DecodeLayout y{};
     y.BHq = lay.B * H_q;
@@ -62,8 +62,21 @@ DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q)
     y.off_part = off;    off = align256(off + BHq * lay.n_chunks * int64_t(kD + 2) * 4);
     y.off_seg_idx = off; off = align256(off + BHq * lay.n_chunks * int64_t(kChunk) * 4);
     y.off_seg_cnt = off; off = align256(off + BHq * lay.n_chunks * 4);
+    y.off_bits = off;
+    if (tables) off = align256(off + BHq * (lay.n_pad / 16) * 4);
     y.total = off;
     return y;
+}
+
+size_t collide_lds_bytes(const IndexLayout &lay);   // tables.hip
+constexpr size_t kLdsLimit = 160 * 1024 - 1024;     // per workgroup, less the static part
+
+// Why the bucketed tables of an index cannot be used, or NULL.
+static const char *tables_unsupported(const IndexLayout &lay)
+{
+    if (lay.K > kMaxTableK) return "tables need K <= 12 (2^K bucket counters in LDS)";
+    if (collide_lds_bytes(lay) > kLdsLimit) return "tables need n <= 622,592 (2 bits per key in LDS)";
+    return nullptr;
 }
 
 static bool sizes_ok(int32_t B, int32_t H, int32_t n, int32_t d, int32_t K, int32_t L)
@@ -100,11 +113,14 @@ static mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx,
                                int32_t n_local, float scale, float *out, void *scratch,
                                size_t scratch_bytes, void *stream, bool debug, uint16_t *qcodes,
                                uint8_t *counts, int32_t *s_idx, int32_t *s_len,
-                               void *ev_begin = nullptr, void *ev_end = nullptr)
+                               void *ev_begin = nullptr, void *ev_end = nullptr,
+                               bool tables = false)
 {
     g_err[0] = 0;
     if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
     const IndexLayout &lay = idx->lay;
+    if (tables && !idx->tab_off)
+        return fail(MP_E_ARG, "the index has no bucketed tables: call mp_build_tables first");
     if (!q || !out) return fail(MP_E_ARG, "q and out must be non-NULL");
     if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(out) & 15))
         return fail(MP_E_ARG, "q and out must be 16-byte aligned");
@@ -128,7 +144,7 @@ static mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx,
                     k->B, k->H, k->n, v->B, v->H, v->n, lay.B, lay.H_kv, lay.n);
     if (n_sink < 0 || n_local < 0) return fail(MP_E_ARG, "n_sink and n_local must be >= 0");
     if (!isfinite(scale) || scale < 0.0f) return fail(MP_E_ARG, "scale must be finite and >= 0");
-    const DecodeLayout dl = decode_layout(lay, H_q);
+    const DecodeLayout dl = decode_layout(lay, H_q, tables);
     if (!scratch) return fail(MP_E_WORKSPACE, "scratch is NULL");
     if (reinterpret_cast<uintptr_t>(scratch) & 255)
         return fail(MP_E_WORKSPACE, "scratch must be 256-byte aligned");
@@ -166,6 +182,9 @@ static mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx,
     a.part = reinterpret_cast<float *>(sp + dl.off_part);
     a.seg_idx = reinterpret_cast<int32_t *>(sp + dl.off_seg_idx);
     a.seg_cnt = reinterpret_cast<int32_t *>(sp + dl.off_seg_cnt);
+    a.tab_off = idx->tab_off;
+    a.tab_ent = idx->tab_ent;
+    a.bits = tables ? reinterpret_cast<uint32_t *>(sp + dl.off_bits) : nullptr;
     a.out = out;
     a.counts = counts;
     a.s_idx = s_idx;
@@ -174,7 +193,7 @@ static mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx,
     a.ev_begin = static_cast<hipEvent_t>(ev_begin);
     a.ev_end = static_cast<hipEvent_t>(ev_end);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_decode(a, s);
+    hipError_t e = tables ? launch_decode_tables(a, s) : launch_decode(a, s);
     if (e != hipSuccess) return fail(MP_E_HIP, "decode launch failed: %s", hipGetErrorString(e));
     if (debug && qcodes) {
         e = hipMemcpyAsync(qcodes, a.qcodes, size_t(dl.BHq) * lay.L * 2, hipMemcpyDeviceToDevice, s);
@@ -286,6 +305,85 @@ mp_status mp_decode_debug(const float *q, int32_t H_q, const mp_index *idx, cons
 {
     return decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
                          stream, true, qcodes, counts, s_idx, s_len);
+}
+
+size_t mp_tables_workspace_bytes(const mp_index *idx)
+{
+    if (!live(idx) || tables_unsupported(idx->lay)) return 0;
+    return size_t(tables_layout(idx->lay).total);
+}
+
+mp_status mp_build_tables(mp_index *idx, void *workspace, size_t workspace_bytes, void *stream)
+{
+    g_err[0] = 0;
+    if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
+    if (const char *why = tables_unsupported(idx->lay)) return fail(MP_E_SHAPE, "%s", why);
+    const TablesLayout tl = tables_layout(idx->lay);
+    if (!workspace) return fail(MP_E_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255)
+        return fail(MP_E_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < size_t(tl.total))
+        return fail(MP_E_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
+                    (long long)tl.total);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != idx->device)
+        return fail(MP_E_ARG, "current device %d is not the device %d the index lives on", dev,
+                    idx->device);
+    char *wp = static_cast<char *>(workspace);
+    idx->tab_off = reinterpret_cast<uint32_t *>(wp + tl.off_offsets);
+    idx->tab_ent = reinterpret_cast<uint32_t *>(wp + tl.off_entries);
+    const hipError_t e = launch_build_tables(*idx, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        idx->tab_off = idx->tab_ent = nullptr;
+        return fail(MP_E_HIP, "table build launch failed: %s", hipGetErrorString(e));
+    }
+    return MP_OK;
+}
+
+size_t mp_decode_tables_scratch_bytes(const mp_index *idx, int32_t H_q)
+{
+    if (!live(idx) || H_q < 1 || H_q % idx->lay.H_kv || tables_unsupported(idx->lay)) return 0;
+    return size_t(decode_layout(idx->lay, H_q, true).total);
+}
+
+mp_status mp_decode_attn_tables(const float *q, int32_t H_q, const mp_index *idx,
+                                const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
+                                int32_t n_local, float scale, float *out, void *scratch,
+                                size_t scratch_bytes, void *stream)
+{
+    return decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
+                         stream, false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, true);
+}
+
+mp_status mp_decode_attn_tables_timed(const float *q, int32_t H_q, const mp_index *idx,
+                                      const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
+                                      int32_t n_local, float scale, float *out, void *scratch,
+                                      size_t scratch_bytes, void *stream, void *ev_gather_begin,
+                                      void *ev_gather_end)
+{
+    return decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
+                         stream, false, nullptr, nullptr, nullptr, nullptr, ev_gather_begin,
+                         ev_gather_end, true);
+}
+
+mp_status mp_decode_tables_debug(const float *q, int32_t H_q, const mp_index *idx,
+                                 const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
+                                 int32_t n_local, float scale, float *out, void *scratch,
+                                 size_t scratch_bytes, void *stream, uint16_t *qcodes,
+                                 uint8_t *counts2, int32_t *s_idx, int32_t *s_len)
+{
+    return decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
+                         stream, true, qcodes, counts2, s_idx, s_len, nullptr, nullptr, true);
+}
+
+mp_status mp_tables_views(const mp_index *idx, const uint32_t **offsets, const uint32_t **entries)
+{
+    g_err[0] = 0;
+    if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
+    if (!idx->tab_off) return fail(MP_E_ARG, "the index has no bucketed tables");
+    if (offsets) *offsets = idx->tab_off;
+    if (entries) *entries = idx->tab_ent;
+    return MP_OK;
 }
 
 mp_status mp_index_views(const mp_index *idx, const float **W, const float **mu,

@@ -33,82 +33,15 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
-#include "mp_internal.h"
+#include "gather_common.h"
 
 namespace mp {
 namespace {
 
-constexpr int kPart = kD + 2;     // partial softmax: m, l, acc[128]
-#ifndef MP_ROWS_PER_GROUP
-#define MP_ROWS_PER_GROUP 4
-#endif
-constexpr int kRowsPerGroup = MP_ROWS_PER_GROUP;  // listed rows a 16-lane group holds per round
-constexpr int kRound = 16 * kRowsPerGroup;
 #ifndef MP_SCAN_BATCH
 #define MP_SCAN_BATCH 4
 #endif
 constexpr int kScanBatch = MP_SCAN_BATCH;   // tables per code batch in the scan
-
-// ---------------------------------------------------------------- helpers
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// 8 consecutive elements of a K or V row: raw 16-byte words, then fp32.
-template <typename T> struct Row8;
-template <> struct Row8<float> {
-    static constexpr int kLoads = 2;
-    struct raw { u32x4 w[2]; };
-    static __device__ __forceinline__ raw load_raw(const float *p)
-    {
-        return raw{{*reinterpret_cast<const u32x4 *>(p), *reinterpret_cast<const u32x4 *>(p + 4)}};
-    }
-    static __device__ __forceinline__ void convert(const raw &r, float (&o)[8])
-    {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            o[j] = __uint_as_float(r.w[0][j]);
-            o[4 + j] = __uint_as_float(r.w[1][j]);
-        }
-    }
-    static __device__ __forceinline__ void store_raw(float *p, const raw &r)
-    {
-        reinterpret_cast<u32x4 *>(p)[0] = r.w[0];
-        reinterpret_cast<u32x4 *>(p)[1] = r.w[1];
-    }
-    static __device__ __forceinline__ void load_pair(const float *p, float &v0, float &v1)
-    {
-        const float2 v = *reinterpret_cast<const float2 *>(p);
-        v0 = v.x;
-        v1 = v.y;
-    }
-};
-template <> struct Row8<uint16_t> {
-    static constexpr int kLoads = 1;
-    struct raw { u32x4 w[1]; };
-    static __device__ __forceinline__ raw load_raw(const uint16_t *p)
-    {
-        return raw{{*reinterpret_cast<const u32x4 *>(p)}};
-    }
-    static __device__ __forceinline__ void convert(const raw &r, float (&o)[8])
-    {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            o[2 * j] = bf16_to_f32(r.w[0][j] & 0xFFFFu);
-            o[2 * j + 1] = bf16_to_f32(r.w[0][j] >> 16);
-        }
-    }
-    static __device__ __forceinline__ void store_raw(uint16_t *p, const raw &r)
-    {
-        *reinterpret_cast<u32x4 *>(p) = r.w[0];
-    }
-    static __device__ __forceinline__ void load_pair(const uint16_t *p, float &v0, float &v1)
-    {
-        const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
-        v0 = bf16_to_f32(v & 0xFFFFu);
-        v1 = bf16_to_f32(v >> 16);
-    }
-};
 
 // Per 16-bit half: min(a, b).  Written out because the compiler turns the
 // vector-extension form into compares and selects.
@@ -117,37 +50,6 @@ __device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b)
     uint32_t d;
     asm("v_pk_min_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
     return d;
-}
-
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// log u for u = P[at least 2 of L tables collide], P = p^K (fp32).
-// Closed form 1 - (1-P)^L - L P (1-P)^(L-1) where L*P > 0.05; below that the
-// two subtractions cancel, so u is the binomial tail
-//   C(L,2) P^2 (1-P)^(L-2) * (1 + sum_{j>=3} prod_{i=2}^{j-1} (L-i)/(i+1) P/(1-P))
-// taken in logs.  p is floored at 1e-30: p = 0 only for an exactly
-// anti-parallel centered key, which cannot collide in exact arithmetic.
-__device__ __forceinline__ float log_u_f32(float p, int K, int L)
-{
-    if (K == 0) return 0.0f;
-    p = fminf(fmaxf(p, 1e-30f), 1.0f);
-    const float logP = float(K) * logf(p);
-    const float P = expf(logP);
-    if (P >= 1.0f) return 0.0f;
-    const float a = log1pf(-P);
-    const float LP = float(L) * P;
-    if (LP > 0.05f) {
-        const float u = -expm1f(float(L) * a) - LP * expf(float(L - 1) * a);
-        return logf(u);
-    }
-    const float r = P / (1.0f - P);
-    float term = 1.0f, rest = 0.0f;
-    for (int j = 2; j < L; ++j) {
-        term *= float(L - j) / float(j + 1) * r;
-        rest += term;
-        if (term < 1e-9f * (1.0f + rest)) break;
-    }
-    return logf(0.5f * float(L) * float(L - 1)) + 2.0f * logP + float(L - 2) * a + log1pf(rest);
 }
 
 // ---------------------------------------------------------------- query codes
@@ -222,49 +124,6 @@ __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restri
 template <int G, typename T>
 constexpr int scan_occupancy() { return G <= 2 || (G == 4 && sizeof(T) == 2) ? MP_SCAN_OCC : 2; }
 
-// Full-rate cross-lane move inside a DPP row of 16 lanes.
-template <int kCtrl>
-__device__ __forceinline__ float dpp_mov(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
-
-// Sum over each aligned group of 16 lanes; every lane of the group gets it.
-// Butterfly over lane ^ 1, lane ^ 2 (quad permutes), then the half-row and
-// row mirrors, which pair the two quads of each half and the two halves.
-__device__ __forceinline__ float row16_sum(float v)
-{
-    v += dpp_mov<0xB1>(v);    // quad_perm [1, 0, 3, 2]
-    v += dpp_mov<0x4E>(v);    // quad_perm [2, 3, 0, 1]
-    v += dpp_mov<0x141>(v);   // row_half_mirror
-    v += dpp_mov<0x140>(v);   // row_mirror
-    return v;
-}
-
-// Max / sum over the wave (64 lanes), the same value in every lane: DPP
-// inside each row of 16 lanes, then the four row results in lane order.
-__device__ __forceinline__ float wave_max(float v)
-{
-    v = fmaxf(v, dpp_mov<0xB1>(v));
-    v = fmaxf(v, dpp_mov<0x4E>(v));
-    v = fmaxf(v, dpp_mov<0x141>(v));
-    v = fmaxf(v, dpp_mov<0x140>(v));
-    const int b = __float_as_int(v);
-    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)),
-                       __int_as_float(__builtin_amdgcn_readlane(b, 16))),
-                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)),
-                       __int_as_float(__builtin_amdgcn_readlane(b, 48))));
-}
-__device__ __forceinline__ float wave_sum(float v)
-{
-    v = row16_sum(v);
-    const int b = __float_as_int(v);
-    return ((__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
-             __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
-            __int_as_float(__builtin_amdgcn_readlane(b, 32))) +
-           __int_as_float(__builtin_amdgcn_readlane(b, 48));
-}
-
 // One workgroup takes a run of `cpb` consecutive 512-key chunks (numbered
 // over (sequence, KV head) units, then chunks); runs are as equal as the
 // chunk count allows and the grid is no larger than what is resident at
@@ -292,10 +151,7 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     __shared__ __align__(16) float sq[2][G][kD];   // per staged unit: the group's queries
     __shared__ float sqn[2][G];              // their norms
     __shared__ __align__(16) float smu[2][kD];   // mean of the unit's keys
-    __shared__ float srow[kRound][2 * G + 1];   // per listed row: q.k, q.(k-mu), |k-mu|^2
-    __shared__ float sz[kRound][G];          // per (row, head): z, or -inf if not sampled
-    __shared__ float sw[kRound][G];          // per (row, head): exp(z - running max) or 0
-    __shared__ __align__(16) T sv[kRound][kD];  // the round's V rows
+    __shared__ GatherLds<G, T> gl;           // one gather round
 
     const int w = uniform(threadIdx.x >> 6);
     const int L = a.L;
@@ -425,157 +281,10 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
                     asm volatile("" ::"v"(kraw[r].w[j]), "v"(vraw[r].w[j]));
         }
         if (pend) {
-            // ---- (c) gather-SNIS of the pending chunk, in rounds of up to
-            // kRound listed rows (round 0's rows are already loaded) ----
-            // c1: 16 groups of 16 lanes, lane = 8 dims; group gi takes rows
-            //     gi, gi+16, ... of the round, stages its V rows in LDS and
-            //     reduces q_g.k, q_g.(k - mu) and |k - mu|^2 over its lanes;
-            //     the group's lanes then share out its (row, head) pairs and
-            //     evaluate z for each;
-            // c2: wave w owns heads w, w+4, ... (their running max and sum live
-            //     in its registers): it forms the round's max, the weights
-            //     exp(z - max) and their sum, and each thread = (head, pair of
-            //     dims) rescales its accumulator and adds the weighted V rows.
-            const int pb = p_bkv / a.H_kv, ph = p_bkv % a.H_kv;
-            const T *kb = static_cast<const T *>(a.k.data) + pb * a.k.sb + ph * a.k.sh + 8 * li;
-            const T *vb = static_cast<const T *>(a.v.data) + pb * a.v.sb + ph * a.v.sh + 8 * li;
-            constexpr int kPairs = (G * (kD / 2) + 255) / 256;   // (head, dim pair)s per thread
-            constexpr int kZ = kRowsPerGroup * G;                 // (row, head)s per group
-            float acc0[kPairs], acc1[kPairs], m_run[kPairs], l_run[kPairs];
-#pragma unroll
-            for (int p = 0; p < kPairs; ++p) {
-                acc0[p] = acc1[p] = 0.0f;
-                m_run[p] = -INFINITY;
-                l_run[p] = 0.0f;
-            }
-            const float inv_pi = 0.31830988618379067f;
-            using Raw = typename Row8<T>::raw;
-            // One round: rows [base, base + ne) of the list, their K/V words in kr_/vr_.
-            auto round = [&](int base, const Raw(&kr_)[kRowsPerGroup], const Raw(&vr_)[kRowsPerGroup]) {
-                const int ne = min(kRound, p_total - base);
-                const float4 m0 = reinterpret_cast<const float4 *>(smu[p_slot])[2 * li];
-                const float4 m1 = reinterpret_cast<const float4 *>(smu[p_slot])[2 * li + 1];
-                const float mu8[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-#pragma unroll
-                for (int r = 0; r < kRowsPerGroup; ++r) {
-                    const int e = gi + 16 * r;
-                    if (e >= ne) continue;            // uniform over the 16-lane group
-                    Row8<T>::store_raw(&sv[e][8 * li], vr_[r]);
-                    float kr[8], x[8];
-                    Row8<T>::convert(kr_[r], kr);
-                    float xx = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        x[j] = kr[j] - mu8[j];
-                        xx = fmaf(x[j], x[j], xx);
-                    }
-                    float sd[G], td[G];
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const float4 q0 = *reinterpret_cast<const float4 *>(&sq[p_slot][g][8 * li]);
-                        const float4 q1 =
-                            *reinterpret_cast<const float4 *>(&sq[p_slot][g][8 * li + 4]);
-                        const float qg[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-                        float s0 = 0.0f, t0 = 0.0f;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            s0 = fmaf(qg[j], kr[j], s0);
-                            t0 = fmaf(qg[j], x[j], t0);
-                        }
-                        sd[g] = row16_sum(s0);
-                        td[g] = row16_sum(t0);
-                    }
-                    xx = row16_sum(xx);
-                    if (li == 0) {
-#pragma unroll
-                        for (int g = 0; g < G; ++g) {
-                            srow[e][g] = sd[g];
-                            srow[e][G + g] = td[g];
-                        }
-                        srow[e][2 * G] = xx;
-                    }
-                }
-                // z of the group's (row, head) pairs, one per lane (srow was
-                // written by this wave: LDS keeps a wave's accesses in order)
-#pragma unroll
-                for (int k = 0; k < (kZ + 15) / 16; ++k) {
-                    const int zp = li + 16 * k;
-                    const int r = zp / G, g = zp % G;
-                    const int e = gi + 16 * r;
-                    if (zp < kZ && e < ne) {
-                        const uint32_t ent = ulist[base + e];
-                        const bool exact = (ent >> 24) & 1u;
-                        float z = -INFINITY;
-                        if (exact || ((ent >> (16 + g)) & 1u)) {
-                            z = srow[e][g] * a.scale;
-                            if (!exact) {
-                                const float den = sqn[p_slot][g] * sqrtf(srow[e][2 * G]);
-                                float cs = den > 0.0f ? srow[e][G + g] / den : 0.0f;
-                                cs = fminf(fmaxf(cs, -1.0f), 1.0f);
-                                const float pc = 1.0f - acosf(cs) * inv_pi;
-                                z -= log_u_f32(pc, a.K, L);
-                            }
-                        }
-                        sz[e][g] = z;
-                    }
-                }
-                __syncthreads();
-#pragma unroll
-                for (int p = 0; p < kPairs; ++p) {
-                    const int g = uniform((t + 256 * p) / (kD / 2)), dp = lane;
-                    if (g < G) {
-                        const float z = lane < ne ? sz[lane][g] : -INFINITY;
-                        const float m_new = fmaxf(m_run[p], wave_max(z));
-                        const float wgt = z == -INFINITY ? 0.0f : __expf(z - m_new);
-                        if (lane < ne) sw[lane][g] = wgt;
-                        const float sc = m_new == -INFINITY ? 1.0f : __expf(m_run[p] - m_new);
-                        l_run[p] = fmaf(l_run[p], sc, wave_sum(wgt));
-                        m_run[p] = m_new;
-                        // the weights were written by this wave: in order in LDS
-                        float x0 = acc0[p] * sc, x1 = acc1[p] * sc;
-                        for (int e = 0; e < ne; ++e) {
-                            const float wg = sw[e][g];
-                            float v0, v1;
-                            Row8<T>::load_pair(&sv[e][2 * dp], v0, v1);
-                            x0 = fmaf(wg, v0, x0);
-                            x1 = fmaf(wg, v1, x1);
-                        }
-                        acc0[p] = x0;
-                        acc1[p] = x1;
-                    }
-                }
-                __syncthreads();   // srow, sz, sw, sv are rewritten by the next round
-            };
-            // Round 0 with the rows loaded before the scan (older than the
-            // batches in flight); later rounds load theirs here.
-            if (p_total > 0) round(0, kraw, vraw);
-            for (int base = kRound; base < p_total; base += kRound) {
-                const int ne = min(kRound, p_total - base);
-                Raw kr2[kRowsPerGroup], vr2[kRowsPerGroup];
-#pragma unroll
-                for (int r = 0; r < kRowsPerGroup; ++r) {
-                    const int e = gi + 16 * r;
-                    const int64_t i = int64_t(p_chunk) * kChunk +
-                                      (e < ne ? (ulist[base + e] & 0xFFFFu) : 0u);
-                    kr2[r] = Row8<T>::load_raw(kb + i * a.k.sn);
-                    vr2[r] = Row8<T>::load_raw(vb + i * a.v.sn);
-                }
-                round(base, kr2, vr2);
-            }
-            // the chunk's partial: (max, sum, unnormalised accumulator) per head
-            float *part0 = a.part + (int64_t(p_bkv) * a.n_chunks + p_chunk) * (G * kPart);
-#pragma unroll
-            for (int p = 0; p < kPairs; ++p) {
-                const int g = uniform((t + 256 * p) / (kD / 2)), dp = lane;
-                if (g < G) {
-                    part0[g * kPart + 2 + 2 * dp] = acc0[p];
-                    part0[g * kPart + 3 + 2 * dp] = acc1[p];
-                    if (dp == 0) {
-                        part0[g * kPart] = m_run[p];
-                        part0[g * kPart + 1] = l_run[p];
-                    }
-                }
-            }
+            // ---- (c) gather-SNIS of the pending chunk (its round-0 rows were
+            // loaded before this scan)
+            gather_chunk<G, T>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot], sqn[p_slot],
+                               smu[p_slot], kraw, vraw, t, gi, li);
         }
         // counts in red are complete; the pending chunk's list is no longer
         // read
@@ -603,22 +312,9 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
             }
             fl[e] = ex[e] || hm[e] != 0u;
         }
-        const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        {
-            const unsigned long long b0 = __ballot(fl[0]), b1 = __ballot(fl[1]);
-            const int pre = __popcll(b0 & lt) + __popcll(b1 & lt);
-            if (lane == 0) wsum[w] = __popcll(b0) + __popcll(b1);
-            __syncthreads();
-            int woff = 0;
-            for (int j = 0; j < w; ++j) woff += wsum[j];
-            const int pos = woff + pre;
-            if (fl[0]) ulist[pos] = uint32_t(2 * t) | (hm[0] << 16) | (uint32_t(ex[0]) << 24);
-            if (fl[1])
-                ulist[pos + (fl[0] ? 1 : 0)] =
-                    uint32_t(2 * t + 1) | (hm[1] << 16) | (uint32_t(ex[1]) << 24);
-        }
-        const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-
+        const int total = compact_list(
+            fl[0], fl[1], uint32_t(2 * t) | (hm[0] << 16) | (uint32_t(ex[0]) << 24),
+            uint32_t(2 * t + 1) | (hm[1] << 16) | (uint32_t(ex[1]) << 24), ulist, wsum, t);
         if (a.debug) {
             if (a.counts) {
 #pragma unroll
@@ -628,42 +324,15 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
                         for (int g = 0; g < G; ++g)
                             a.counts[int64_t(bhq0 + g) * n + key0 + e] = uint8_t(cnt[e][g]);
             }
-            // Per-head sampled lists of this chunk (ascending), for the S view.
-            for (int g = 0; g < G; ++g) {
-                const bool s0 = (hm[0] >> g) & 1u, s1 = (hm[1] >> g) & 1u;
-                const unsigned long long b0 = __ballot(s0), b1 = __ballot(s1);
-                const int pre = __popcll(b0 & lt) + __popcll(b1 & lt);
-                __syncthreads();
-                if (lane == 0) wsum[w] = __popcll(b0) + __popcll(b1);
-                __syncthreads();
-                int woff = 0;
-                for (int j = 0; j < w; ++j) woff += wsum[j];
-                int32_t *seg = a.seg_idx + (int64_t(bhq0 + g) * a.n_chunks + chunk) * kChunk;
-                if (s0) seg[woff + pre] = int32_t(key0);
-                if (s1) seg[woff + pre + (s0 ? 1 : 0)] = int32_t(key0 + 1);
-                if (t == 0)
-                    a.seg_cnt[int64_t(bhq0 + g) * a.n_chunks + chunk] =
-                        wsum[0] + wsum[1] + wsum[2] + wsum[3];
-            }
+            write_seg_lists<G>(a, hm[0], hm[1], key0, bhq0, chunk, wsum, t);
         }
         __syncthreads();   // ulist complete
 
-        // Round 0's rows of this chunk, in flight during the next scan.  Every
-        // group loads kRowsPerGroup rows; past the list it re-reads the
-        // chunk's first key, which is never used.
+        // Round 0's rows of this chunk, in flight during the next scan.
         {
-            const int b = bkv / a.H_kv, h = bkv % a.H_kv;
-            const T *kb = static_cast<const T *>(a.k.data) + b * a.k.sb + h * a.k.sh + 8 * li;
-            const T *vb = static_cast<const T *>(a.v.data) + b * a.v.sb + h * a.v.sh + 8 * li;
-            const int ne = min(kRound, total);
-#pragma unroll
-            for (int r = 0; r < kRowsPerGroup; ++r) {
-                const int e = gi + 16 * r;
-                const int64_t i =
-                    int64_t(chunk) * kChunk + (e < ne ? (ulist[e] & 0xFFFFu) : 0u);
-                kraw[r] = Row8<T>::load_raw(kb + i * a.k.sn);
-                vraw[r] = Row8<T>::load_raw(vb + i * a.v.sn);
-            }
+            const T *kb, *vb;
+            row_bases<T>(a, bkv, li, kb, vb);
+            load_rows<T>(a, kb, vb, ulist, 0, min(kRound, total), chunk, gi, kraw, vraw);
         }
         pend = true;
         p_bkv = bkv;
@@ -785,23 +454,46 @@ hipError_t launch_scan_gather_t(const DecodeArgs &a, hipStream_t s)
 template <int G>
 hipError_t launch_scan_gather(const DecodeArgs &a, hipStream_t s)
 {
-    hipError_t e = a.dtype == MP_BF16 ? launch_scan_gather_t<G, uint16_t>(a, s)
-                                      : launch_scan_gather_t<G, float>(a, s);
-    if (e != hipSuccess) return e;
-    merge_kernel<G><<<dim3(a.B * a.H_kv * G, kD / 32), 1024, 0, s>>>(a.part, a.n_chunks, a.H_kv,
-                                                                   a.H_q, a.out);
-    return hipGetLastError();
+    return a.dtype == MP_BF16 ? launch_scan_gather_t<G, uint16_t>(a, s)
+                              : launch_scan_gather_t<G, float>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
+// ---- launches shared with the bucketed-table path (tables.hip) ----
+hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s)
 {
     const int BHq = a.B * a.H_q;
     const int TB = a.K > 0 ? 64 / a.K : 64;
     encode_query_kernel<<<dim3(ceil_div(a.L, TB), ceil_div(BHq, 4)), 256, 0, s>>>(
         a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const DecodeArgs &a, hipStream_t s)
+{
+    const dim3 grid(a.B * a.H_kv * a.G, kD / 32);
+    switch (a.G) {
+    case 1: merge_kernel<1><<<grid, 1024, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
+    case 2: merge_kernel<2><<<grid, 1024, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
+    case 4: merge_kernel<4><<<grid, 1024, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
+    case 8: merge_kernel<8><<<grid, 1024, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_compact(const DecodeArgs &a, hipStream_t s)
+{
+    if (!a.debug || (!a.s_idx && !a.s_len)) return hipSuccess;
+    seg_compact_kernel<<<dim3(a.B * a.H_q), 256, 0, s>>>(a.seg_idx, a.seg_cnt, a.n_chunks, a.n,
+                                                         a.s_idx, a.s_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
+{
+    hipError_t e = launch_encode_query(a, s);
     if (e != hipSuccess) return e;
     switch (a.G) {
     case 1: e = launch_scan_gather<1>(a, s); break;
@@ -811,12 +503,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    if (a.debug && (a.s_idx || a.s_len)) {
-        seg_compact_kernel<<<dim3(BHq), 256, 0, s>>>(a.seg_idx, a.seg_cnt, a.n_chunks, a.n,
-                                                     a.s_idx, a.s_len);
-        e = hipGetLastError();
-    }
-    return e;
+    if ((e = launch_merge(a, s)) != hipSuccess) return e;
+    return launch_seg_compact(a, s);
 }
 
 }  // namespace mp

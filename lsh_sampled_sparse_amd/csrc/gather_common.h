@@ -1,0 +1,416 @@
+// gather_common.h -- device code shared by the two decode paths of
+// decode.hip (code scan) and tables.hip (bucketed tables): row loads, the
+// estimator's log u, cross-lane reductions, the ascending compaction of a
+// chunk's sampled and exact keys, and the gather-SNIS rounds that turn a
+// chunk's list into its partial softmax (page "MagicPIG: LSH Sampling for
+// Efficient LLM Generation", algorithm steps: inner products, collision and
+// sampling probabilities, softmax over [w_S, w_T]/sqrt(d) - log[u, 1]).
+#pragma once
+
+#include "mp_internal.h"
+
+namespace mp {
+namespace {
+
+constexpr int kPart = kD + 2;     // partial softmax: m, l, acc[128]
+#ifndef MP_ROWS_PER_GROUP
+#define MP_ROWS_PER_GROUP 4
+#endif
+constexpr int kRowsPerGroup = MP_ROWS_PER_GROUP;  // listed rows a 16-lane group holds per round
+constexpr int kRound = 16 * kRowsPerGroup;
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive elements of a K or V row: raw 16-byte words, then fp32.
+template <typename T> struct Row8;
+template <> struct Row8<float> {
+    static constexpr int kLoads = 2;
+    struct raw { u32x4 w[2]; };
+    static __device__ __forceinline__ raw load_raw(const float *p)
+    {
+        return raw{{*reinterpret_cast<const u32x4 *>(p), *reinterpret_cast<const u32x4 *>(p + 4)}};
+    }
+    static __device__ __forceinline__ void convert(const raw &r, float (&o)[8])
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            o[j] = __uint_as_float(r.w[0][j]);
+            o[4 + j] = __uint_as_float(r.w[1][j]);
+        }
+    }
+    static __device__ __forceinline__ void store_raw(float *p, const raw &r)
+    {
+        reinterpret_cast<u32x4 *>(p)[0] = r.w[0];
+        reinterpret_cast<u32x4 *>(p)[1] = r.w[1];
+    }
+    static __device__ __forceinline__ void load_pair(const float *p, float &v0, float &v1)
+    {
+        const float2 v = *reinterpret_cast<const float2 *>(p);
+        v0 = v.x;
+        v1 = v.y;
+    }
+};
+template <> struct Row8<uint16_t> {
+    static constexpr int kLoads = 1;
+    struct raw { u32x4 w[1]; };
+    static __device__ __forceinline__ raw load_raw(const uint16_t *p)
+    {
+        return raw{{*reinterpret_cast<const u32x4 *>(p)}};
+    }
+    static __device__ __forceinline__ void convert(const raw &r, float (&o)[8])
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            o[2 * j] = bf16_to_f32(r.w[0][j] & 0xFFFFu);
+            o[2 * j + 1] = bf16_to_f32(r.w[0][j] >> 16);
+        }
+    }
+    static __device__ __forceinline__ void store_raw(uint16_t *p, const raw &r)
+    {
+        *reinterpret_cast<u32x4 *>(p) = r.w[0];
+    }
+    static __device__ __forceinline__ void load_pair(const uint16_t *p, float &v0, float &v1)
+    {
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+        v0 = bf16_to_f32(v & 0xFFFFu);
+        v1 = bf16_to_f32(v >> 16);
+    }
+};
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// log u for u = P[at least 2 of L tables collide], P = p^K (fp32).
+// Closed form 1 - (1-P)^L - L P (1-P)^(L-1) where L*P > 0.05; below that the
+// two subtractions cancel, so u is the binomial tail
+//   C(L,2) P^2 (1-P)^(L-2) * (1 + sum_{j>=3} prod_{i=2}^{j-1} (L-i)/(i+1) P/(1-P))
+// taken in logs.  p is floored at 1e-30: p = 0 only for an exactly
+// anti-parallel centered key, which cannot collide in exact arithmetic.
+__device__ __forceinline__ float log_u_f32(float p, int K, int L)
+{
+    if (K == 0) return 0.0f;
+    p = fminf(fmaxf(p, 1e-30f), 1.0f);
+    const float logP = float(K) * logf(p);
+    const float P = expf(logP);
+    if (P >= 1.0f) return 0.0f;
+    const float a = log1pf(-P);
+    const float LP = float(L) * P;
+    if (LP > 0.05f) {
+        const float u = -expm1f(float(L) * a) - LP * expf(float(L - 1) * a);
+        return logf(u);
+    }
+    const float r = P / (1.0f - P);
+    float term = 1.0f, rest = 0.0f;
+    for (int j = 2; j < L; ++j) {
+        term *= float(L - j) / float(j + 1) * r;
+        rest += term;
+        if (term < 1e-9f * (1.0f + rest)) break;
+    }
+    return logf(0.5f * float(L) * float(L - 1)) + 2.0f * logP + float(L - 2) * a + log1pf(rest);
+}
+
+// Full-rate cross-lane move inside a DPP row of 16 lanes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 16 lanes; every lane of the group gets it.
+// Butterfly over lane ^ 1, lane ^ 2 (quad permutes), then the half-row and
+// row mirrors, which pair the two quads of each half and the two halves.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_mov<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v += dpp_mov<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v += dpp_mov<0x141>(v);   // row_half_mirror
+    v += dpp_mov<0x140>(v);   // row_mirror
+    return v;
+}
+
+// Max / sum over the wave (64 lanes), the same value in every lane: DPP
+// inside each row of 16 lanes, then the four row results in lane order.
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    const int b = __float_as_int(v);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)),
+                       __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)),
+                       __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = row16_sum(v);
+    const int b = __float_as_int(v);
+    return ((__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
+             __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+            __int_as_float(__builtin_amdgcn_readlane(b, 32))) +
+           __int_as_float(__builtin_amdgcn_readlane(b, 48));
+}
+
+
+// LDS of one gather round: per listed row the three reduced products, per
+// (row, head) z and the weight exp(z - running max), and the row's V.
+template <int G, typename T> struct GatherLds {
+    float srow[kRound][2 * G + 1];   // q.k per head, q.(k-mu) per head, |k-mu|^2
+    float sz[kRound][G];             // z, or -inf where the row is not in the head's set
+    float sw[kRound][G];             // exp(z - running max), or 0
+    __align__(16) T sv[kRound][kD];  // the round's V rows
+};
+
+// Thread = (head, pair of dims) slots of one workgroup of 256: its
+// accumulator pair and the head's running max and sum (the same in every
+// lane of a wave, since a wave owns whole heads).
+template <int G> struct GatherAcc {
+    static constexpr int kPairs = (G * (kD / 2) + 255) / 256;
+    float acc0[kPairs], acc1[kPairs], m[kPairs], l[kPairs];
+    __device__ __forceinline__ void reset()
+    {
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p) {
+            acc0[p] = acc1[p] = 0.0f;
+            m[p] = -INFINITY;
+            l[p] = 0.0f;
+        }
+    }
+};
+
+// K/V row pointers of unit bkv at this lane's 8 dims.
+template <typename T>
+__device__ __forceinline__ void row_bases(const DecodeArgs &a, int bkv, int li, const T *&kb,
+                                          const T *&vb)
+{
+    const int b = bkv / a.H_kv, h = bkv % a.H_kv;
+    kb = static_cast<const T *>(a.k.data) + b * a.k.sb + h * a.k.sh + 8 * li;
+    vb = static_cast<const T *>(a.v.data) + b * a.v.sb + h * a.v.sh + 8 * li;
+}
+
+// The K/V words of list entries base + gi + 16 r (r < kRowsPerGroup) of a
+// chunk.  Past the list every group re-reads the chunk's first key, which is
+// never used: the loads stay unconditional.
+template <typename T>
+__device__ __forceinline__ void load_rows(const DecodeArgs &a, const T *kb, const T *vb,
+                                          const uint32_t *ulist, int base, int ne, int chunk,
+                                          int gi, typename Row8<T>::raw (&kr)[kRowsPerGroup],
+                                          typename Row8<T>::raw (&vr)[kRowsPerGroup])
+{
+#pragma unroll
+    for (int r = 0; r < kRowsPerGroup; ++r) {
+        const int e = gi + 16 * r;
+        const int64_t i = int64_t(chunk) * kChunk + (e < ne ? (ulist[base + e] & 0xFFFFu) : 0u);
+        kr[r] = Row8<T>::load_raw(kb + i * a.k.sn);
+        vr[r] = Row8<T>::load_raw(vb + i * a.v.sn);
+    }
+}
+
+// One round over list entries [base, base + ne), ne <= kRound, whose K/V
+// words are kr / vr:
+//   c1: 16 groups of 16 lanes, lane = 8 dims; group gi takes rows gi, gi+16,
+//       ... of the round, stages its V rows in LDS and reduces q_g.k,
+//       q_g.(k - mu) and |k - mu|^2 over its lanes; the group's lanes then
+//       share out its (row, head) pairs and evaluate z for each: on T,
+//       z = q.k*scale; on S, z = q.k*scale - log u with
+//       p = 1 - acos(cos(q, k - mu))/pi;
+//   c2: wave w owns heads w, w+4, ...: it forms the round's max, the weights
+//       exp(z - max) and their sum, and each thread = (head, pair of dims)
+//       rescales its accumulator and adds the weighted V rows.
+template <int G, typename T>
+__device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T> &s,
+                                             const uint32_t *ulist, int base, int ne,
+                                             const float (*sq)[kD], const float *sqn,
+                                             const float *smu,
+                                             const typename Row8<T>::raw (&kr_)[kRowsPerGroup],
+                                             const typename Row8<T>::raw (&vr_)[kRowsPerGroup],
+                                             GatherAcc<G> &acc, int t, int gi, int li)
+{
+    constexpr int kZ = kRowsPerGroup * G;   // (row, head)s per group
+    const int lane = t & 63;
+    const float inv_pi = 0.31830988618379067f;
+    const float4 m0 = reinterpret_cast<const float4 *>(smu)[2 * li];
+    const float4 m1 = reinterpret_cast<const float4 *>(smu)[2 * li + 1];
+    const float mu8[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+    for (int r = 0; r < kRowsPerGroup; ++r) {
+        const int e = gi + 16 * r;
+        if (e >= ne) continue;            // uniform over the 16-lane group
+        Row8<T>::store_raw(&s.sv[e][8 * li], vr_[r]);
+        float kr[8], x[8];
+        Row8<T>::convert(kr_[r], kr);
+        float xx = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            x[j] = kr[j] - mu8[j];
+            xx = fmaf(x[j], x[j], xx);
+        }
+        float sd[G], td[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float4 q0 = *reinterpret_cast<const float4 *>(&sq[g][8 * li]);
+            const float4 q1 = *reinterpret_cast<const float4 *>(&sq[g][8 * li + 4]);
+            const float qg[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+            float s0 = 0.0f, t0 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                s0 = fmaf(qg[j], kr[j], s0);
+                t0 = fmaf(qg[j], x[j], t0);
+            }
+            sd[g] = row16_sum(s0);
+            td[g] = row16_sum(t0);
+        }
+        xx = row16_sum(xx);
+        if (li == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                s.srow[e][g] = sd[g];
+                s.srow[e][G + g] = td[g];
+            }
+            s.srow[e][2 * G] = xx;
+        }
+    }
+    // z of the group's (row, head) pairs, one per lane (srow was written by
+    // this wave: LDS keeps a wave's accesses in order)
+#pragma unroll
+    for (int k = 0; k < (kZ + 15) / 16; ++k) {
+        const int zp = li + 16 * k;
+        const int r = zp / G, g = zp % G;
+        const int e = gi + 16 * r;
+        if (zp < kZ && e < ne) {
+            const uint32_t ent = ulist[base + e];
+            const bool exact = (ent >> 24) & 1u;
+            float z = -INFINITY;
+            if (exact || ((ent >> (16 + g)) & 1u)) {
+                z = s.srow[e][g] * a.scale;
+                if (!exact) {
+                    const float den = sqn[g] * sqrtf(s.srow[e][2 * G]);
+                    float cs = den > 0.0f ? s.srow[e][G + g] / den : 0.0f;
+                    cs = fminf(fmaxf(cs, -1.0f), 1.0f);
+                    const float pc = 1.0f - acosf(cs) * inv_pi;
+                    z -= log_u_f32(pc, a.K, a.L);
+                }
+            }
+            s.sz[e][g] = z;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < GatherAcc<G>::kPairs; ++p) {
+        const int g = uniform((t + 256 * p) / (kD / 2)), dp = lane;
+        if (g < G) {
+            const float z = lane < ne ? s.sz[lane][g] : -INFINITY;
+            const float m_new = fmaxf(acc.m[p], wave_max(z));
+            const float wgt = z == -INFINITY ? 0.0f : __expf(z - m_new);
+            if (lane < ne) s.sw[lane][g] = wgt;
+            const float sc = m_new == -INFINITY ? 1.0f : __expf(acc.m[p] - m_new);
+            acc.l[p] = fmaf(acc.l[p], sc, wave_sum(wgt));
+            acc.m[p] = m_new;
+            // the weights were written by this wave: in order in LDS
+            float x0 = acc.acc0[p] * sc, x1 = acc.acc1[p] * sc;
+            for (int e = 0; e < ne; ++e) {
+                const float wg = s.sw[e][g];
+                float v0, v1;
+                Row8<T>::load_pair(&s.sv[e][2 * dp], v0, v1);
+                x0 = fmaf(wg, v0, x0);
+                x1 = fmaf(wg, v1, x1);
+            }
+            acc.acc0[p] = x0;
+            acc.acc1[p] = x1;
+        }
+    }
+    __syncthreads();   // srow, sz, sw, sv are rewritten by the next round
+}
+
+// The whole list of one chunk: round 0 from rows already loaded (kr0 / vr0),
+// later rounds load theirs; then the chunk's partial softmax (max, sum,
+// unnormalised accumulator) per head goes to `part`.
+template <int G, typename T>
+__device__ __forceinline__ void gather_chunk(const DecodeArgs &a, GatherLds<G, T> &s,
+                                             const uint32_t *ulist, int total, int chunk,
+                                             int bkv, const float (*sq)[kD], const float *sqn,
+                                             const float *smu,
+                                             const typename Row8<T>::raw (&kr0)[kRowsPerGroup],
+                                             const typename Row8<T>::raw (&vr0)[kRowsPerGroup],
+                                             int t, int gi, int li)
+{
+    GatherAcc<G> acc;
+    acc.reset();
+    if (total > 0) gather_round<G, T>(a, s, ulist, 0, min(kRound, total), sq, sqn, smu, kr0, vr0,
+                                      acc, t, gi, li);
+    if (total > kRound) {
+        const T *kb, *vb;
+        row_bases<T>(a, bkv, li, kb, vb);
+        for (int base = kRound; base < total; base += kRound) {
+            const int ne = min(kRound, total - base);
+            typename Row8<T>::raw kr[kRowsPerGroup], vr[kRowsPerGroup];
+            load_rows<T>(a, kb, vb, ulist, base, ne, chunk, gi, kr, vr);
+            gather_round<G, T>(a, s, ulist, base, ne, sq, sqn, smu, kr, vr, acc, t, gi, li);
+        }
+    }
+    const int lane = t & 63;
+    float *part0 = a.part + (int64_t(bkv) * a.n_chunks + chunk) * (G * kPart);
+#pragma unroll
+    for (int p = 0; p < GatherAcc<G>::kPairs; ++p) {
+        const int g = uniform((t + 256 * p) / (kD / 2)), dp = lane;
+        if (g < G) {
+            part0[g * kPart + 2 + 2 * dp] = acc.acc0[p];
+            part0[g * kPart + 3 + 2 * dp] = acc.acc1[p];
+            if (dp == 0) {
+                part0[g * kPart] = acc.m[p];
+                part0[g * kPart + 1] = acc.l[p];
+            }
+        }
+    }
+}
+
+// Ascending compaction of a chunk's flagged keys: thread t owns keys 2t and
+// 2t+1 and hands in their flags and list entries (key | headmask << 16 |
+// exact << 24).  Writes ulist and returns the list length (every thread).
+__device__ __forceinline__ int compact_list(bool fl0, bool fl1, uint32_t ent0, uint32_t ent1,
+                                            uint32_t *ulist, int *wsum, int t)
+{
+    const int lane = t & 63, w = t >> 6;
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const unsigned long long b0 = __ballot(fl0), b1 = __ballot(fl1);
+    const int pre = __popcll(b0 & lt) + __popcll(b1 & lt);
+    if (lane == 0) wsum[w] = __popcll(b0) + __popcll(b1);
+    __syncthreads();
+    int woff = 0;
+    for (int j = 0; j < w; ++j) woff += wsum[j];
+    const int pos = woff + pre;
+    if (fl0) ulist[pos] = ent0;
+    if (fl1) ulist[pos + (fl0 ? 1 : 0)] = ent1;
+    return wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+// Debug view: per-head sampled keys of a chunk (ascending) into seg_idx /
+// seg_cnt; hm0 / hm1 are the head masks of keys key0, key0 + 1.
+template <int G>
+__device__ __forceinline__ void write_seg_lists(const DecodeArgs &a, uint32_t hm0, uint32_t hm1,
+                                                int64_t key0, int bhq0, int chunk, int *wsum,
+                                                int t)
+{
+    const int lane = t & 63, w = t >> 6;
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int g = 0; g < G; ++g) {
+        const bool s0 = (hm0 >> g) & 1u, s1 = (hm1 >> g) & 1u;
+        const unsigned long long b0 = __ballot(s0), b1 = __ballot(s1);
+        const int pre = __popcll(b0 & lt) + __popcll(b1 & lt);
+        __syncthreads();
+        if (lane == 0) wsum[w] = __popcll(b0) + __popcll(b1);
+        __syncthreads();
+        int woff = 0;
+        for (int j = 0; j < w; ++j) woff += wsum[j];
+        int32_t *seg = a.seg_idx + (int64_t(bhq0 + g) * a.n_chunks + chunk) * kChunk;
+        if (s0) seg[woff + pre] = int32_t(key0);
+        if (s1) seg[woff + pre + (s0 ? 1 : 0)] = int32_t(key0 + 1);
+        if (t == 0)
+            a.seg_cnt[int64_t(bhq0 + g) * a.n_chunks + chunk] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    }
+}
+
+}  // namespace
+}  // namespace mp

@@ -34,14 +34,26 @@ struct mp_index_impl {
     float *mu;       // [B*H_kv][128]
     double *mu_part; // [B*H_kv][n_mean_blocks][128]
     uint16_t *codes; // [B*H_kv][n_chunks][L][kChunk]
+    // bucketed tables, once built (NULL until then)
+    uint32_t *tab_off; // [B*H_kv][L][2^K + 1] bucket starts
+    uint32_t *tab_ent; // [B*H_kv][L][n] keys, grouped by bucket
 };
+
+// Workspace layout of the bucketed tables of an index.
+constexpr int kMaxTableK = 12;   // 2^K bucket counters live in LDS while a table is built
+struct TablesLayout {
+    int32_t nbins;
+    int64_t off_offsets, off_entries, total;
+};
+TablesLayout tables_layout(const IndexLayout &lay);
 
 // Decode scratch layout.
 struct DecodeLayout {
     int32_t BHq, n_chunks;
-    int64_t off_qcodes, off_qq, off_qnorm, off_part, off_seg_idx, off_seg_cnt, total;
+    int64_t off_qcodes, off_qq, off_qnorm, off_part, off_seg_idx, off_seg_cnt, off_bits, total;
 };
-DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q);
+// `tables`: also the per-head collision bitmaps of the bucketed-table path.
+DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables = false);
 
 // Row addressing of a [B][H][n][128] view.
 struct KVRows {
@@ -67,6 +79,9 @@ struct DecodeArgs {
     const float *W;          // [R][128]
     const float *mu;         // [B*H_kv][128]
     const uint16_t *codes;   // index codes
+    const uint32_t *tab_off; // bucketed tables (table path only)
+    const uint32_t *tab_ent;
+    uint32_t *bits;          // scratch [BHq][n_pad/16]: 2 bits per key (table path only)
     KVRows k, v;
     int32_t dtype;
     uint16_t *qcodes;        // scratch [BHq][L]
@@ -76,12 +91,17 @@ struct DecodeArgs {
     int32_t *seg_idx;        // scratch [BHq][n_chunks * kChunk] (debug only)
     int32_t *seg_cnt;        // scratch [BHq][n_chunks] (debug only)
     float *out;              // [BHq][128]
-    uint8_t *counts;         // optional [BHq][n]
+    uint8_t *counts;         // optional [BHq][n] (table path: min(count, 2))
     int32_t *s_idx;          // optional [BHq][n]
     int32_t *s_len;          // optional [BHq]
     bool debug;
     hipEvent_t ev_begin, ev_end;   // optional, recorded around scan_gather
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_merge(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_seg_compact(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_build_tables(const mp_index_impl &idx, hipStream_t s);
+hipError_t launch_decode_tables(const DecodeArgs &a, hipStream_t s);
 
 }  // namespace mp

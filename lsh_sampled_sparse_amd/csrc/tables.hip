@@ -1,0 +1,304 @@
+// tables.hip -- MagicPIG decode through bucketed hash tables on gfx950.
+//
+// Page "MagicPIG: LSH Sampling for Efficient LLM Generation", Algorithm 1:
+// the query's code selects one bucket in each of the L tables, and the keys
+// found in at least two of them are the sampled set S; page "MagicPIG: don't
+// pick the tallest", section 6 ("The bill"): a table stores a 32-bit token
+// index per key, and a query reads about L n / 2^K of them.  The set is the
+// one the code scan of decode.hip finds; only the way to it differs.
+//
+//   build_tables   per (sequence, KV head) unit and table: a counting sort of
+//                  the keys by their code (bucket starts + keys grouped by
+//                  bucket).  Keys within a bucket come in no fixed order;
+//                  nothing downstream depends on it.
+//   collide        per query head: its L buckets, each key marked in an LDS
+//                  bitmap of 2 bits (seen once, seen twice), written out.
+//   table_gather   per 512-key chunk: the G heads' bits of its keys give the
+//                  sampled / exact list; gather-SNIS as in the code scan
+//                  (gather_common.h) writes the chunk's partial softmax, which
+//                  the merge of decode.hip combines.
+#include <hip/hip_ext.h>
+
+#include "gather_common.h"
+
+namespace mp {
+
+TablesLayout tables_layout(const IndexLayout &lay)
+{
+    TablesLayout y{};
+    y.nbins = 1 << lay.K;
+    const int64_t BH = int64_t(lay.B) * lay.H_kv;
+    int64_t off = 0;
+    y.off_offsets = off; off = align256(off + BH * lay.L * int64_t(y.nbins + 1) * 4);
+    y.off_entries = off; off = align256(off + BH * lay.L * int64_t(lay.n) * 4);
+    y.total = off;
+    return y;
+}
+
+namespace {
+
+constexpr int kBuildThreads = 1024;
+
+// Exclusive prefix sum of one value per thread over a workgroup of
+// kBuildThreads (16 waves); every thread gets its own prefix and the total.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wtot, uint32_t &total)
+{
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wtot[w] = x;
+    __syncthreads();
+    uint32_t base = 0, all = 0;
+    for (int j = 0; j < kBuildThreads / 64; ++j) {
+        if (j < w) base += wtot[j];
+        all += wtot[j];
+    }
+    total = all;
+    __syncthreads();
+    return base + x - v;
+}
+
+// Block = one (unit, table).  Codes of key i of table l: chunk i/512, row l,
+// position i%512.  hist: nbins counters, then cursors.
+__global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
+    const uint16_t *__restrict__ codes, int32_t n, int32_t n_chunks, int32_t L, int32_t nbins,
+    uint32_t *__restrict__ off, uint32_t *__restrict__ ent)
+{
+    extern __shared__ uint32_t hist[];
+    __shared__ uint32_t wtot[kBuildThreads / 64];
+    const int u = blockIdx.x / L, l = blockIdx.x % L;
+    const int t = threadIdx.x;
+    const uint16_t *cb = codes + (int64_t(u) * n_chunks * L + l) * kChunk;
+    for (int b = t; b < nbins; b += kBuildThreads) hist[b] = 0u;
+    __syncthreads();
+    for (int i = t; i < n; i += kBuildThreads)
+        atomicAdd(&hist[cb[int64_t(i / kChunk) * L * kChunk + i % kChunk]], 1u);
+    __syncthreads();
+    // thread t owns bins [t per, (t+1) per)
+    const int per = (nbins + kBuildThreads - 1) / kBuildThreads;   // <= 4 for K <= 12
+    uint32_t loc[4], sum = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int b = t * per + k;
+        loc[k] = (k < per && b < nbins) ? hist[b] : 0u;
+        sum += loc[k];
+    }
+    uint32_t all;
+    uint32_t start = block_exclusive_scan(sum, wtot, all);
+    uint32_t *o = off + (int64_t(u) * L + l) * (nbins + 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int b = t * per + k;
+        if (k < per && b < nbins) {
+            o[b] = start;
+            hist[b] = start;
+            start += loc[k];
+        }
+    }
+    if (t == 0) o[nbins] = uint32_t(n);
+    __syncthreads();
+    uint32_t *e = ent + (int64_t(u) * L + l) * n;
+    for (int i = t; i < n; i += kBuildThreads) {
+        const uint32_t c = cb[int64_t(i / kChunk) * L * kChunk + i % kChunk];
+        e[atomicAdd(&hist[c], 1u)] = uint32_t(i);
+    }
+}
+
+// Block = one query head.  LDS: the head's bitmap (2 bits per key: bit 0 =
+// seen in a bucket, bit 1 = seen in two), then per table the bucket start and
+// the prefix of bucket sizes.  The entries of all L buckets are walked as one
+// flat range, four per thread at a time so their loads overlap.
+__global__ __launch_bounds__(kBuildThreads) void collide_kernel(
+    const uint16_t *__restrict__ qcodes, const uint32_t *__restrict__ off,
+    const uint32_t *__restrict__ ent, int32_t H_q, int32_t H_kv, int32_t n, int32_t nwords,
+    int32_t L, int32_t nbins, uint32_t *__restrict__ bits)
+{
+    extern __shared__ uint32_t sm[];
+    __shared__ uint32_t wtot[kBuildThreads / 64];
+    uint32_t *bm = sm;
+    uint32_t *bstart = sm + nwords;
+    uint32_t *bpre = bstart + L;   // L + 1 entries
+    const int bhq = blockIdx.x;
+    const int b = bhq / H_q, hq = bhq % H_q, G = H_q / H_kv;
+    const int u = b * H_kv + hq / G;
+    const int t = threadIdx.x;
+    for (int i = t; i < nwords; i += kBuildThreads) bm[i] = 0u;
+    uint32_t size = 0u;
+    if (t < L) {
+        const uint32_t code = qcodes[int64_t(bhq) * L + t];
+        const uint32_t *o = off + (int64_t(u) * L + t) * (nbins + 1);
+        const uint32_t s0 = o[code];
+        bstart[t] = s0;
+        size = o[code + 1] - s0;
+    }
+    uint32_t total;
+    const uint32_t pre = block_exclusive_scan(size, wtot, total);
+    if (t < L) bpre[t] = pre;
+    if (t == 0) bpre[L] = total;
+    __syncthreads();
+    const uint32_t *eu = ent + int64_t(u) * L * n;
+    for (uint32_t base = t; base < total; base += 4 * kBuildThreads) {
+        uint32_t key[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t idx = base + k * kBuildThreads;
+            key[k] = 0xFFFFFFFFu;
+            if (idx < total) {
+                int lo = 0, hi = L - 1;   // last table whose prefix is <= idx
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (bpre[mid] <= idx) lo = mid;
+                    else hi = mid - 1;
+                }
+                key[k] = eu[int64_t(lo) * n + bstart[lo] + (idx - bpre[lo])];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (key[k] == 0xFFFFFFFFu) continue;
+            const uint32_t w = key[k] >> 4, one = 1u << (2 * (key[k] & 15u));
+            if (atomicOr(&bm[w], one) & one) atomicOr(&bm[w], one << 1);
+        }
+    }
+    __syncthreads();
+    for (int i = t; i < nwords; i += kBuildThreads) bits[int64_t(bhq) * nwords + i] = bm[i];
+}
+
+// Block = one 512-key chunk of one unit and its G query heads.
+template <int G, typename T>
+__global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int32_t nwords)
+{
+    __shared__ uint32_t ulist[kChunk];
+    __shared__ int wsum[4];
+    __shared__ __align__(16) float sq[G][kD];
+    __shared__ float sqn[G];
+    __shared__ __align__(16) float smu[kD];
+    __shared__ GatherLds<G, T> gl;
+    const int gc = blockIdx.x;
+    const int bkv = gc / a.n_chunks, chunk = gc - bkv * a.n_chunks;
+    const int bhq0 = (bkv / a.H_kv) * a.H_q + (bkv % a.H_kv) * G;
+    const int t = threadIdx.x, gi = t >> 4, li = t & 15;
+    for (int i = t; i < G * kD; i += 256) sq[i / kD][i % kD] = a.q[int64_t(bhq0) * kD + i];
+    if (t < G) sqn[t] = a.qnorm[bhq0 + t];
+    if (t < kD) smu[t] = a.mu[int64_t(bkv) * kD + t];
+
+    // Thread t owns keys 2t and 2t+1: one 4-bit field of a bitmap word.
+    const int n = a.n;
+    const int64_t key0 = int64_t(chunk) * kChunk + 2 * t;
+    const int word = int(key0 >> 4), sh = 2 * int(key0 & 15);
+    uint32_t hm[2] = {0u, 0u}, c2[2][G];
+    bool ex[2], fl[2];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const uint32_t f = a.bits[int64_t(bhq0 + g) * nwords + word] >> sh;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const uint32_t v = (f >> (2 * e)) & 3u;
+            c2[e][g] = (v & 2u) ? 2u : (v & 1u);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int64_t i = key0 + e;
+        const bool valid = i < n;
+        ex[e] = valid && (i < a.n_sink || i >= int64_t(n) - a.n_local);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            if (valid && !ex[e] && c2[e][g] == 2u) hm[e] |= 1u << g;
+        fl[e] = ex[e] || hm[e] != 0u;
+    }
+    const int total = compact_list(
+        fl[0], fl[1], uint32_t(2 * t) | (hm[0] << 16) | (uint32_t(ex[0]) << 24),
+        uint32_t(2 * t + 1) | (hm[1] << 16) | (uint32_t(ex[1]) << 24), ulist, wsum, t);
+    if (a.debug) {
+        if (a.counts) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                if (key0 + e < n)
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+                        a.counts[int64_t(bhq0 + g) * n + key0 + e] = uint8_t(c2[e][g]);
+        }
+        write_seg_lists<G>(a, hm[0], hm[1], key0, bhq0, chunk, wsum, t);
+    }
+    __syncthreads();   // ulist and the staged queries complete
+
+    typename Row8<T>::raw kr[kRowsPerGroup], vr[kRowsPerGroup];
+    const T *kb, *vb;
+    row_bases<T>(a, bkv, li, kb, vb);
+    load_rows<T>(a, kb, vb, ulist, 0, min(kRound, total), chunk, gi, kr, vr);
+    gather_chunk<G, T>(a, gl, ulist, total, chunk, bkv, sq, sqn, smu, kr, vr, t, gi, li);
+}
+
+template <int G, typename T>
+hipError_t launch_table_gather_t(const DecodeArgs &a, int32_t nwords, hipStream_t s)
+{
+    const dim3 grid(a.B * a.H_kv * a.n_chunks);
+    if (a.ev_begin || a.ev_end) {
+        hipExtLaunchKernelGGL(table_gather_kernel<G, T>, grid, dim3(256), 0, s,
+                              static_cast<hipEvent_t>(a.ev_begin),
+                              static_cast<hipEvent_t>(a.ev_end), 0, a, nwords);
+    } else {
+        table_gather_kernel<G, T><<<grid, 256, 0, s>>>(a, nwords);
+    }
+    return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_table_gather(const DecodeArgs &a, int32_t nwords, hipStream_t s)
+{
+    return a.dtype == MP_BF16 ? launch_table_gather_t<G, uint16_t>(a, nwords, s)
+                              : launch_table_gather_t<G, float>(a, nwords, s);
+}
+
+}  // namespace
+
+// LDS bytes of collide_kernel for an index (the API checks it against the
+// workgroup limit before any launch).
+size_t collide_lds_bytes(const IndexLayout &lay)
+{
+    return size_t(lay.n_pad / 16) * 4 + size_t(2 * lay.L + 1) * 4;
+}
+
+hipError_t launch_build_tables(const mp_index_impl &idx, hipStream_t s)
+{
+    const IndexLayout &lay = idx.lay;
+    const int nbins = 1 << lay.K;
+    const size_t lds = size_t(nbins) * 4;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(build_tables_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    build_tables_kernel<<<dim3(lay.B * lay.H_kv * lay.L), kBuildThreads, lds, s>>>(
+        idx.codes, lay.n, lay.n_chunks, lay.L, nbins, idx.tab_off, idx.tab_ent);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_tables(const DecodeArgs &a, hipStream_t s)
+{
+    hipError_t e = launch_encode_query(a, s);
+    if (e != hipSuccess) return e;
+    const int32_t n_pad = a.n_chunks * kChunk, nwords = n_pad / 16;
+    const size_t lds = size_t(nwords) * 4 + size_t(2 * a.L + 1) * 4;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(collide_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    collide_kernel<<<dim3(a.B * a.H_q), kBuildThreads, lds, s>>>(
+        a.qcodes, a.tab_off, a.tab_ent, a.H_q, a.H_kv, a.n, nwords, a.L, 1 << a.K, a.bits);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    switch (a.G) {
+    case 1: e = launch_table_gather<1>(a, nwords, s); break;
+    case 2: e = launch_table_gather<2>(a, nwords, s); break;
+    case 4: e = launch_table_gather<4>(a, nwords, s); break;
+    case 8: e = launch_table_gather<8>(a, nwords, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    if ((e = launch_merge(a, s)) != hipSuccess) return e;
+    return launch_seg_compact(a, s);
+}
+
+}  // namespace mp

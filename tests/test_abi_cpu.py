@@ -111,3 +111,13 @@ def test_python_layer_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(capi, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         capi.lib()
+
+
+def test_tables_calls_reject_a_dead_handle():
+    """The bucketed-table calls check the index handle on the host."""
+    assert capi.mp_tables_workspace_bytes(None) == 0
+    assert capi.mp_decode_tables_scratch_bytes(None, 32) == 0
+    with pytest.raises(capi.MPError, match="MP_E_HANDLE"):
+        capi.mp_build_tables(None, None, 0, None)
+    with pytest.raises(capi.MPError, match="MP_E_HANDLE"):
+        capi.mp_tables_views(None)
