@@ -49,6 +49,9 @@ IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t 
     return y;
 }
 
+size_t collide_lds_bytes(const IndexLayout &lay);   // tables.hip
+int collide_slices();                               // tables.hip
+
 DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables)
 {
     DecodeLayout y{};
@@ -63,12 +66,11 @@ DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables)
     y.off_seg_idx = off; off = align256(off + BHq * lay.n_chunks * int64_t(kChunk) * 4);
     y.off_seg_cnt = off; off = align256(off + BHq * lay.n_chunks * 4);
     y.off_bits = off;
-    if (tables) off = align256(off + BHq * (lay.n_pad / 16) * 4);
+    if (tables) off = align256(off + BHq * collide_slices() * (lay.n_pad / 16) * 4);
     y.total = off;
     return y;
 }
 
-size_t collide_lds_bytes(const IndexLayout &lay);   // tables.hip
 constexpr size_t kLdsLimit = 160 * 1024 - 1024;     // per workgroup, less the static part
 
 // Why the bucketed tables of an index cannot be used, or NULL.

@@ -81,7 +81,7 @@ struct DecodeArgs {
     const uint16_t *codes;   // index codes
     const uint32_t *tab_off; // bucketed tables (table path only)
     const uint32_t *tab_ent;
-    uint32_t *bits;          // scratch [BHq][n_pad/16]: 2 bits per key (table path only)
+    uint32_t *bits;          // scratch [BHq][slices][n_pad/16]: 2 bits per key (table path only)
     KVRows k, v;
     int32_t dtype;
     uint16_t *qcodes;        // scratch [BHq][L]

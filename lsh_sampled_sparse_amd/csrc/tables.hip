@@ -11,9 +11,11 @@
 //                  the keys by their code (bucket starts + keys grouped by
 //                  bucket).  Keys within a bucket come in no fixed order;
 //                  nothing downstream depends on it.
-//   collide        per query head: its L buckets, each key marked in an LDS
-//                  bitmap of 2 bits (seen once, seen twice), written out.
-//   table_gather   per 512-key chunk: the G heads' bits of its keys give the
+//   collide        per query head and slice of its L tables: the slice's
+//                  buckets, each key marked in an LDS bitmap of 2 bits (seen
+//                  once, seen twice), written out per slice.
+//   table_gather   per 512-key chunk: the G heads' slice bits of its keys
+//                  (seen twice = in one slice, or once in two) give the
 //                  sampled / exact list; gather-SNIS as in the code scan
 //                  (gather_common.h) writes the chunk's partial softmax, which
 //                  the merge of decode.hip combines.
@@ -38,6 +40,7 @@ TablesLayout tables_layout(const IndexLayout &lay)
 namespace {
 
 constexpr int kBuildThreads = 1024;
+constexpr int kSlices = 4;   // collide workgroups per query head, each over L / kSlices tables
 
 // Exclusive prefix sum of one value per thread over a workgroup of
 // kBuildThreads (16 waves); every thread gets its own prefix and the total.
@@ -108,10 +111,12 @@ __global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
     }
 }
 
-// Block = one query head.  LDS: the head's bitmap (2 bits per key: bit 0 =
-// seen in a bucket, bit 1 = seen in two), then per table the bucket start and
-// the prefix of bucket sizes.  The entries of all L buckets are walked as one
-// flat range, four per thread at a time so their loads overlap.
+// Block = one slice of the L tables of one query head (kSlices slices).
+// LDS: the slice's bitmap (2 bits per key: bit 0 = seen in a bucket, bit 1 =
+// seen in two), then per table of the slice the bucket start and the prefix
+// of bucket sizes.  The entries of the slice's buckets are walked as one flat
+// range, four per thread at a time so their loads overlap.  Slice bitmaps go
+// out side by side; the gather combines them.
 __global__ __launch_bounds__(kBuildThreads) void collide_kernel(
     const uint16_t *__restrict__ qcodes, const uint32_t *__restrict__ off,
     const uint32_t *__restrict__ ent, int32_t H_q, int32_t H_kv, int32_t n, int32_t nwords,
@@ -119,28 +124,29 @@ __global__ __launch_bounds__(kBuildThreads) void collide_kernel(
 {
     extern __shared__ uint32_t sm[];
     __shared__ uint32_t wtot[kBuildThreads / 64];
+    const int bhq = blockIdx.x / kSlices, sl = blockIdx.x % kSlices;
+    const int l0 = (sl * L) / kSlices, nl = ((sl + 1) * L) / kSlices - l0;
     uint32_t *bm = sm;
     uint32_t *bstart = sm + nwords;
-    uint32_t *bpre = bstart + L;   // L + 1 entries
-    const int bhq = blockIdx.x;
+    uint32_t *bpre = bstart + nl;   // nl + 1 entries
     const int b = bhq / H_q, hq = bhq % H_q, G = H_q / H_kv;
     const int u = b * H_kv + hq / G;
     const int t = threadIdx.x;
     for (int i = t; i < nwords; i += kBuildThreads) bm[i] = 0u;
     uint32_t size = 0u;
-    if (t < L) {
-        const uint32_t code = qcodes[int64_t(bhq) * L + t];
-        const uint32_t *o = off + (int64_t(u) * L + t) * (nbins + 1);
+    if (t < nl) {
+        const uint32_t code = qcodes[int64_t(bhq) * L + l0 + t];
+        const uint32_t *o = off + (int64_t(u) * L + l0 + t) * (nbins + 1);
         const uint32_t s0 = o[code];
         bstart[t] = s0;
         size = o[code + 1] - s0;
     }
     uint32_t total;
     const uint32_t pre = block_exclusive_scan(size, wtot, total);
-    if (t < L) bpre[t] = pre;
-    if (t == 0) bpre[L] = total;
+    if (t < nl) bpre[t] = pre;
+    if (t == 0) bpre[nl] = total;
     __syncthreads();
-    const uint32_t *eu = ent + int64_t(u) * L * n;
+    const uint32_t *eu = ent + (int64_t(u) * L + l0) * n;
     for (uint32_t base = t; base < total; base += 4 * kBuildThreads) {
         uint32_t key[4];
 #pragma unroll
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(kBuildThreads) void collide_kernel(
             const uint32_t idx = base + k * kBuildThreads;
             key[k] = 0xFFFFFFFFu;
             if (idx < total) {
-                int lo = 0, hi = L - 1;   // last table whose prefix is <= idx
+                int lo = 0, hi = nl - 1;   // last table whose prefix is <= idx
                 while (lo < hi) {
                     const int mid = (lo + hi + 1) >> 1;
                     if (bpre[mid] <= idx) lo = mid;
@@ -165,7 +171,8 @@ __global__ __launch_bounds__(kBuildThreads) void collide_kernel(
         }
     }
     __syncthreads();
-    for (int i = t; i < nwords; i += kBuildThreads) bits[int64_t(bhq) * nwords + i] = bm[i];
+    uint32_t *ob = bits + int64_t(bhq) * kSlices * nwords + sl * nwords;
+    for (int i = t; i < nwords; i += kBuildThreads) ob[i] = bm[i];
 }
 
 // Block = one 512-key chunk of one unit and its G query heads.
@@ -192,14 +199,20 @@ __global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int3
     const int word = int(key0 >> 4), sh = 2 * int(key0 & 15);
     uint32_t hm[2] = {0u, 0u}, c2[2][G];
     bool ex[2], fl[2];
+    uint32_t once[G], twice[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const uint32_t f = a.bits[int64_t(bhq0 + g) * nwords + word] >> sh;
+        // seen twice: in one slice, or once in each of two slices
+        uint32_t o = 0u, w2 = 0u;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const uint32_t v = (f >> (2 * e)) & 3u;
-            c2[e][g] = (v & 2u) ? 2u : (v & 1u);
+        for (int sl = 0; sl < kSlices; ++sl) {
+            const uint32_t f = a.bits[(int64_t(bhq0 + g) * kSlices + sl) * nwords + word] >> sh;
+            const uint32_t f1 = f & 0x5u, f2 = (f >> 1) & 0x5u;   // 2 keys x 2 bits
+            w2 |= f2 | (o & f1);
+            o |= f1;
         }
+        once[g] = o;
+        twice[g] = w2;
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -207,8 +220,10 @@ __global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int3
         const bool valid = i < n;
         ex[e] = valid && (i < a.n_sink || i >= int64_t(n) - a.n_local);
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g) {
+            c2[e][g] = ((twice[g] >> (2 * e)) & 1u) ? 2u : ((once[g] >> (2 * e)) & 1u);
             if (valid && !ex[e] && c2[e][g] == 2u) hm[e] |= 1u << g;
+        }
         fl[e] = ex[e] || hm[e] != 0u;
     }
     const int total = compact_list(
@@ -258,7 +273,8 @@ hipError_t launch_table_gather(const DecodeArgs &a, int32_t nwords, hipStream_t 
 }  // namespace
 
 // LDS bytes of collide_kernel for an index (the API checks it against the
-// workgroup limit before any launch).
+// workgroup limit before any launch); also the number of slice bitmaps.
+int collide_slices() { return kSlices; }
 size_t collide_lds_bytes(const IndexLayout &lay)
 {
     return size_t(lay.n_pad / 16) * 4 + size_t(2 * lay.L + 1) * 4;
@@ -282,11 +298,11 @@ hipError_t launch_decode_tables(const DecodeArgs &a, hipStream_t s)
     hipError_t e = launch_encode_query(a, s);
     if (e != hipSuccess) return e;
     const int32_t n_pad = a.n_chunks * kChunk, nwords = n_pad / 16;
-    const size_t lds = size_t(nwords) * 4 + size_t(2 * a.L + 1) * 4;
+    const size_t lds = size_t(nwords) * 4 + size_t(2 * a.L + 1) * 4;   // bounds any slice
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(collide_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
-    collide_kernel<<<dim3(a.B * a.H_q), kBuildThreads, lds, s>>>(
+    collide_kernel<<<dim3(a.B * a.H_q * kSlices), kBuildThreads, lds, s>>>(
         a.qcodes, a.tab_off, a.tab_ent, a.H_q, a.H_kv, a.n, nwords, a.L, 1 << a.K, a.bits);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     switch (a.G) {
