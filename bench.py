@@ -9,6 +9,11 @@ seed, index and KV cache, ~20 GB in total) are cycled so that every step reads
 its codes and rows from HBM rather than the 256 MB last-level cache.  The
 index build (centering + key encode) is timed separately.
 
+A second leg times the same steps through the bucketed hash tables
+(mp_build_tables once per layer, then mp_decode_attn_tables): query encode,
+bucket walk, per-chunk gather-SNIS, merge.  It is reported under "tables";
+the headline value stays the code-scan path.
+
 Prints one JSON line (see the keys below).
 """
 
@@ -28,20 +33,44 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, published
 METRIC = "decode attn steps/s + achieved HBM GB/s (% peak), 1 layer, 96K ctx, K=10 L=150"
-DECODE_SRC = os.path.join(ROOT, "lsh_sampled_sparse_amd", "csrc", "decode.hip")
-
-# HBM bytes per scan_gather launch read from hardware counters with rocprofv3
-# (FETCH_SIZE and WRITE_SIZE in two separate --pmc runs of this script with
-# --calib-copy), each counter scaled by the factor that makes it read the
-# known bytes of the 256 MiB fp32 negation that --calib-copy runs in the same
-# process.  Valid only for the kernel source they were taken on: reported as
-# null once decode.hip no longer hashes to decode_hip_sha256.
-MEASURED_TRAFFIC = {
-    "decode_hip_sha256": "0f4d00e1e7bbad82cb7fdd518e29ab8039bd5dc11bc8308c1db5352f674464cb",
-    "fetch_kib": 127093.1, "fetch_scale": 1.9999,
-    "write_kib": 3336.9, "write_scale": 1.0000,
-    "bytes_per_launch": 263689754,
+CSRC = os.path.join(ROOT, "lsh_sampled_sparse_amd", "csrc")
+KERNEL_SOURCES = {   # the files whose text fixes each timed kernel's code
+    "scan_gather": ("decode.hip", "gather_common.h", "mp_internal.h"),
+    "table_gather": ("tables.hip", "gather_common.h", "mp_internal.h"),
 }
+
+# HBM bytes per launch read from hardware counters with rocprofv3 (FETCH_SIZE
+# and WRITE_SIZE in two separate --pmc runs of this script with --calib-copy),
+# each counter scaled by the factor that makes it read the known bytes of the
+# 256 MiB fp32 negation that --calib-copy runs in the same process.  Valid only
+# for the kernel source they were taken on: reported as null once the sources
+# no longer hash to sources_sha256.
+MEASURED_TRAFFIC = {
+    "scan_gather": {
+        "sources_sha256": "61697d75b287ab103d0f0e90c29377d446e006eb2de7e28e07ad558975ceba5b",
+        "fetch_kib": 127091.7, "fetch_scale": 1.9999, "write_kib": 3336.2, "write_scale": 1.0,
+        "bytes_per_launch": 263686170},
+    "table_gather": {
+        "sources_sha256": "2cbb78dc03886e4c9a130020816f86fb3ecdcdfc65f739e01de752e28e92f06a",
+        "fetch_kib": 13299.4, "fetch_scale": 1.9999, "write_kib": 3316.5, "write_scale": 1.0,
+        "bytes_per_launch": 30631813},
+}
+
+
+def sources_sha256(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    m = MEASURED_TRAFFIC.get(kernel)
+    if m is None or sources_sha256(kernel) != m["sources_sha256"]:
+        return None
+    return m["bytes_per_launch"]
 
 
 def scan_bytes_per_launch(cfg, union_rows: int) -> int:
@@ -60,6 +89,29 @@ def decode_bytes_per_step(cfg, union_rows: int) -> int:
     """Whole decode step: the scan launch plus W (query encode) and the output."""
     return (scan_bytes_per_launch(cfg, union_rows) + cfg.K * cfg.L * cfg.d * 4
             + cfg.B * cfg.H_q * cfg.d * 4)
+
+
+def table_gather_bytes_per_launch(cfg, union_rows: int) -> int:
+    """Algorithmic bytes of one table-gather launch: the K and V rows of the
+    union over the G query heads of sampled and exact keys (2 * d * elt B
+    each) and the fp32 queries.  The per-head collision bitmaps it also reads
+    belong to this design, not to the method, and are left out."""
+    elt = 2 if str(cfg.dtype).endswith("bfloat16") else 4
+    return union_rows * 2 * cfg.d * elt + cfg.B * cfg.H_q * cfg.d * 4
+
+
+def bucket_entries_of(cfg, idx, qcodes) -> int:
+    """Table entries the bucket walk reads: the size of the query's bucket,
+    summed over query heads and tables (4 B each, plus two 4-byte bucket
+    starts per head and table)."""
+    import torch
+    offs, _ = idx.table_views()                    # [B][H_kv][L][2^K + 1] int32
+    G = cfg.H_q // cfg.H_kv
+    qc = qcodes.long().view(cfg.B, cfg.H_kv, G, cfg.L)
+    o = offs.long().unsqueeze(2).expand(cfg.B, cfg.H_kv, G, cfg.L, offs.shape[-1])
+    lo = torch.gather(o, 4, qc.unsqueeze(-1)).squeeze(-1)
+    hi = torch.gather(o, 4, (qc + 1).unsqueeze(-1)).squeeze(-1)
+    return int((hi - lo).sum())
 
 
 def union_rows_of(cfg, res, device):
@@ -120,6 +172,93 @@ def cpu_baseline(cfg, k, v, q, seed, threads):
                        "and is excluded, as on the GPU")}
 
 
+def time_steps(step, warmup, steps):
+    """Warm up, then time `steps` calls of step(i) with events around the
+    whole region (all kernels of a step) and, in a second pass over the same
+    steps, with per-step events stamped by the step's dominant kernel launch
+    (step(i, ev_begin, ev_end)).  Returns (total ms, wall s, [kernel ms])."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        step(warmup + i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for e in ev_b + ev_e:
+        e.record()                      # creates the underlying hipEvent_t
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(warmup + i, ev_b[i].cuda_event, ev_e[i].cuda_event)
+    torch.cuda.synchronize()
+    return total_ms, wall, [ev_b[i].elapsed_time(ev_e[i]) for i in range(steps)]
+
+
+def tables_leg(args, cfg, state, layers, sh):
+    """The bucketed-table path over the same layers and steps."""
+    import torch
+    import lsh_sampled_sparse_amd as mp
+    from lsh_sampled_sparse_amd import capi
+    build_ms, entries, tscr = [], [], []
+    for l in range(layers):
+        k, v, q, idx = state[l][:4]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mp.build_tables(idx)
+        e1.record()
+        torch.cuda.synchronize()
+        build_ms.append(e0.elapsed_time(e1))
+        scr = torch.empty(idx.scratch_bytes(cfg.H_q, tables=True), dtype=torch.uint8,
+                          device=q.device)
+        res = mp.decode_tables_debug(q, idx, k, v, cfg.n_sink, cfg.n_local, scratch=scr)
+        entries.append(bucket_entries_of(cfg, idx, res["qcodes"]))
+        del res
+        tscr.append(scr)
+
+    def step(i, eb=None, ee=None):
+        _, _, q, idx, _, out, kv_k, kv_v, _ = state[i % layers]
+        scr = tscr[i % layers]
+        if eb is None:
+            capi.mp_decode_attn_tables(q.data_ptr(), cfg.H_q, idx.handle, kv_k, kv_v,
+                                       cfg.n_sink, cfg.n_local, 0.0, out.data_ptr(),
+                                       scr.data_ptr(), scr.numel(), sh)
+        else:
+            capi.mp_decode_attn_tables_timed(q.data_ptr(), cfg.H_q, idx.handle, kv_k, kv_v,
+                                             cfg.n_sink, cfg.n_local, 0.0, out.data_ptr(),
+                                             scr.data_ptr(), scr.numel(), sh, eb, ee)
+
+    total_ms, wall, g_ms = time_steps(step, args.warmup, args.steps)
+    lay = [(args.warmup + i) % layers for i in range(args.steps)]
+    g_bytes = sum(table_gather_bytes_per_launch(cfg, state[l][8]) for l in lay)
+    g_gbs = g_bytes / (sum(g_ms) / 1e3) / 1e9
+    value = args.steps / (total_ms / 1e3)
+    build_avg = (sum(build_ms[1:]) / (len(build_ms) - 1)) if len(build_ms) > 1 else build_ms[0]
+    n_units = cfg.B * cfg.H_kv * cfg.L
+    return {
+        "value": round(value, 2), "unit": "decode layer-steps/s",
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "vs_code_scan": None,
+        "mean_bucket_entries_per_head_table": round(
+            sum(entries) / len(entries) / (cfg.B * cfg.H_q * cfg.L), 1),
+        "roofline": {"kernel": "table_gather", "bound": "hbm", "achieved": round(g_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("table_gather"),
+                     "avg_launch_us": round(sum(g_ms) / len(g_ms) * 1e3, 3),
+                     "algorithmic_bytes_per_launch": round(g_bytes / args.steps)},
+        "table_build": {"ms_per_layer": round(build_avg, 3),
+                        "entries_per_layer": n_units * cfg.n,
+                        "workspace_bytes_per_layer": int(state[0][3].tables.numel())},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,11 +267,18 @@ def main():
     ap.add_argument("--config", default="llama8b_96k")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tables", action="store_true",
+                    help="skip the bucketed-table leg")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--source-hashes", action="store_true",
+                    help="print the source hash of each timed kernel and exit")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a device copy of 256 MiB (read + write), the known-size "
                          "reference for hardware byte counters")
     args = ap.parse_args()
+    if args.source_hashes:
+        print(json.dumps({k: sources_sha256(k) for k in KERNEL_SOURCES}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the per-(sequence, KV head) units would shard across GPUs with no exchange; "
@@ -171,12 +317,12 @@ def main():
         del res
         union_rows.append(u)
         mean_S.append(s)
-        state.append((k, v, q, idx, scratch, out, mp.kv_view(k), mp.kv_view(v)))
+        state.append((k, v, q, idx, scratch, out, mp.kv_view(k), mp.kv_view(v), u))
         print(f"layer {l}: build {build_ms[-1]:.2f} ms, mean |S| {s:.0f}, union rows {u}",
               file=sys.stderr, flush=True)
 
     def step(i, eb=None, ee=None):
-        k, v, q, idx, scratch, out, kv_k, kv_v = state[i % layers]
+        k, v, q, idx, scratch, out, kv_k, kv_v, _ = state[i % layers]
         if eb is None:
             capi.mp_decode_attn(q.data_ptr(), cfg.H_q, idx.handle, kv_k, kv_v, cfg.n_sink,
                                 cfg.n_local, 0.0, out.data_ptr(), scratch.data_ptr(),
@@ -197,30 +343,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # Timed region: the production call, K steps cycling the layers.
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    # Same steps again through the timed entry point: HIP events on the launch
-    # stream right around the scan + gather kernel give its own duration.
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for e in ev_b + ev_e:
-        e.record()                      # creates the underlying hipEvent_t
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(args.warmup + i, ev_b[i].cuda_event, ev_e[i].cuda_event)
-    torch.cuda.synchronize()
-    scan_ms = [ev_b[i].elapsed_time(ev_e[i]) for i in range(args.steps)]
+    # Timed region: the production call, K steps cycling the layers; then the
+    # same steps through the timed entry point, whose HIP events on the launch
+    # stream sit right around the scan + gather kernel.
+    total_ms, wall, scan_ms = time_steps(step, args.warmup, args.steps)
+
     lay = [(args.warmup + i) % layers for i in range(args.steps)]
     scan_bytes = sum(scan_bytes_per_launch(cfg, union_rows[l]) for l in lay)
     dec_bytes = sum(decode_bytes_per_step(cfg, union_rows[l]) for l in lay)
@@ -232,12 +359,10 @@ def main():
     flops_build = 2.0 * cfg.B * cfg.H_kv * cfg.n * cfg.d * cfg.K * cfg.L
     build_avg = sum(build_ms[1:]) / max(1, len(build_ms) - 1) if len(build_ms) > 1 else build_ms[0]
 
-    traffic = None
-    if MEASURED_TRAFFIC is not None:
-        import hashlib
-        with open(DECODE_SRC, "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() == MEASURED_TRAFFIC["decode_hip_sha256"]:
-                traffic = MEASURED_TRAFFIC["bytes_per_launch"]
+    tables = None
+    if not args.no_tables:
+        tables = tables_leg(args, cfg, state, layers, sh)
+        tables["vs_code_scan"] = round(tables["value"] / value, 3)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -270,13 +395,15 @@ def main():
         "mean_union_rows_per_layer": round(sum(union_rows) / len(union_rows), 1),
         "roofline": {"kernel": "scan_gather", "bound": "hbm", "achieved": round(scan_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("scan_gather"),
                      "avg_launch_us": round(scan_avg_ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": round(scan_bytes / args.steps)},
         "index_build": {"ms_per_layer": round(build_avg, 3),
                         "tflops_fp32_mfma": round(flops_build / (build_avg / 1e3) / 1e12, 2),
                         "frac_fp32_mfma_peak": round(flops_build / (build_avg / 1e3) / 1e12
                                                      / FP32_MFMA_PEAK_TFLOPS, 4)},
+        "tables": tables,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
