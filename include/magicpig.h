@@ -90,7 +90,8 @@ size_t mp_index_workspace_bytes(int32_t B, int32_t H_kv, int32_t n, int32_t d,
                                 int32_t K, int32_t L);
 
 /* Build the index of `keys` ([B][H_kv][n][128], fp32 or bf16): hyperplanes W
- * from `seed`, per-(sequence, KV head) mean mu, and the codes of every key.
+ * from `seed`, per-(sequence, KV head) mean mu, and the codes of every key
+ * (K bits per key and table, stored as bit planes: see mp_index_views).
  * The index holds W, mu and the codes only; keys and values are not copied,
  * and decode reads them again through its own views.  The workspace
  * (>= mp_index_workspace_bytes, 256-byte aligned) must stay alive and
@@ -200,14 +201,17 @@ mp_status mp_decode_tables_debug(const float *q, int32_t H_q, const mp_index *id
 mp_status mp_tables_views(const mp_index *idx, const uint32_t **offsets, const uint32_t **entries);
 
 /* Device pointers into the index workspace (valid while the workspace is):
- *   W     [R][128] fp32, R = K*L
- *   mu    [B][H_kv][128] fp32
- *   codes [B][H_kv][n_pad/MP_CHUNK][L][MP_CHUNK] uint16: the code of table l
- *         for key i = c*MP_CHUNK + j is at ((bh*nc + c)*L + l)*MP_CHUNK + j;
- *         keys i >= n are padding and never sampled.
+ *   W      [R][128] fp32, R = K*L
+ *   mu     [B][H_kv][128] fp32
+ *   planes the key codes as bit planes, [B][H_kv][n_pad/MP_CHUNK][L*Kr][MP_CHUNK/32]
+ *          uint32 with Kr = max(K, 1): bit j of word w of row l*Kr + b of
+ *          chunk c is bit b of the table-l code of key c*MP_CHUNK + 32*w + j
+ *          (K bits per key and table, the code's own width).  With K = 0
+ *          every code is 0 and the one row per table is zero.  Keys i >= n
+ *          are padding and never sampled.
  * Any output pointer may be NULL. */
 mp_status mp_index_views(const mp_index *idx, const float **W, const float **mu,
-                         const uint16_t **codes, int32_t *n_pad);
+                         const uint32_t **planes, int32_t *n_pad);
 
 /* Free the host handle (not the workspace).  NULL is ignored. */
 void mp_index_destroy(mp_index *idx);

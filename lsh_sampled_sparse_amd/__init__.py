@@ -45,7 +45,7 @@ def kv_view(t: torch.Tensor) -> capi.mp_kv_view:
 
 class MagicPIGIndex:
     """A built index: the host handle plus the device workspace that holds
-    W, mu and the key codes."""
+    W, mu and the key codes (as bit planes)."""
 
     def __init__(self, handle: int, workspace: torch.Tensor, keys_shape, K: int, L: int,
                  seed: int, dtype):
@@ -72,14 +72,18 @@ class MagicPIGIndex:
 
     def views(self):
         """Device tensors aliasing the workspace: W [R][128] fp32, mu [B][H_kv][128]
-        fp32 and codes [B][H_kv][n_pad/512][L][512] uint16 (as int16 storage)."""
-        W, mu, codes, n_pad = capi.mp_index_views(self.handle)
+        fp32 and the key codes as bit planes [B][H_kv][n_pad/512][L*Kr][16]
+        uint32 (as int32 storage), Kr = max(K, 1): bit j of word w of row
+        l*Kr + b of chunk c is bit b of the table-l code of key 512c + 32w + j."""
+        W, mu, planes, n_pad = capi.mp_index_views(self.handle)
         R = self.K * self.L
         Wt = self._slice(W, R * 128, torch.float32).view(R, 128)
         mut = self._slice(mu, self.B * self.H_kv * 128, torch.float32).view(self.B, self.H_kv, 128)
         nc = n_pad // MP_CHUNK
-        ct = self._slice(codes, self.B * self.H_kv * nc * self.L * MP_CHUNK, torch.int16)
-        return Wt, mut, ct.view(self.B, self.H_kv, nc, self.L, MP_CHUNK)
+        rows = self.L * max(self.K, 1)
+        words = MP_CHUNK // 32
+        pt = self._slice(planes, self.B * self.H_kv * nc * rows * words, torch.int32)
+        return Wt, mut, pt.view(self.B, self.H_kv, nc, rows, words)
 
     def scratch_bytes(self, H_q: int, tables: bool = False) -> int:
         if tables:

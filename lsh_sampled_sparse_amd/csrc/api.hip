@@ -38,13 +38,14 @@ IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t 
     y.L = L;
     y.R = K * L;
     y.R_pad = y.R > 0 ? ceil_div(y.R, 16) * 16 : 16;
+    y.Kr = K > 0 ? K : 1;
     const int64_t BH = int64_t(B) * H_kv;
     int64_t off = 0;
     y.off_W = off;       off = align256(off + int64_t(y.R_pad) * kD * 4);
     y.off_Wp = off;      off = align256(off + int64_t(y.R_pad) * kD * 4);
     y.off_mu = off;      off = align256(off + BH * kD * 4);
     y.off_mu_part = off; off = align256(off + BH * y.n_mean_blocks * kD * 8);
-    y.off_codes = off;   off = align256(off + BH * y.n_chunks * int64_t(L) * kChunk * 2);
+    y.off_planes = off;  off = align256(off + BH * y.n_chunks * int64_t(L) * y.Kr * kWords * 4);
     y.total = off;
     return y;
 }
@@ -174,7 +175,8 @@ static mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx,
     a.scale = scale > 0.0f ? scale : 1.0f / sqrtf(float(kD));
     a.W = idx->W;
     a.mu = idx->mu;
-    a.codes = idx->codes;
+    a.planes = idx->planes;
+    a.Kr = lay.Kr;
     a.k = KVRows{k->data, k->stride_b, k->stride_h, k->stride_n, k->H};
     a.v = KVRows{v->data, v->stride_b, v->stride_h, v->stride_n, v->H};
     a.dtype = k->dtype;
@@ -250,7 +252,7 @@ mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t 
     idx->Wp = reinterpret_cast<float *>(wp + lay.off_Wp);
     idx->mu = reinterpret_cast<float *>(wp + lay.off_mu);
     idx->mu_part = reinterpret_cast<double *>(wp + lay.off_mu_part);
-    idx->codes = reinterpret_cast<uint16_t *>(wp + lay.off_codes);
+    idx->planes = reinterpret_cast<uint32_t *>(wp + lay.off_planes);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const KVRows rows{keys->data, keys->stride_b, keys->stride_h, keys->stride_n, keys->H};
@@ -259,12 +261,12 @@ mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t 
         e = launch_mean(rows, keys->dtype, lay.B, lay.H_kv, lay.n, lay.n_mean_blocks, idx->mu_part,
                         idx->mu, s);
     if (e == hipSuccess) {
-        const int64_t ncodes = int64_t(lay.B) * lay.H_kv * lay.n_chunks * int64_t(L) * kChunk;
+        const int64_t nwords = int64_t(lay.B) * lay.H_kv * lay.n_chunks * int64_t(L) * lay.Kr * kWords;
         if (K == 0)
-            e = launch_fill_u16(idx->codes, ncodes, s);
+            e = launch_fill_u32(idx->planes, nwords, s);   // every code is 0: one zero row per table
         else
             e = launch_encode_keys(rows, keys->dtype, lay.B, lay.H_kv, lay.n, lay.n_chunks, idx->mu,
-                                   idx->Wp, K, L, lay.R_pad, idx->codes, s);
+                                   idx->Wp, K, L, lay.R_pad, idx->planes, s);
     }
     if (e != hipSuccess) {
         idx->magic = 0;
@@ -389,13 +391,13 @@ mp_status mp_tables_views(const mp_index *idx, const uint32_t **offsets, const u
 }
 
 mp_status mp_index_views(const mp_index *idx, const float **W, const float **mu,
-                         const uint16_t **codes, int32_t *n_pad)
+                         const uint32_t **planes, int32_t *n_pad)
 {
     g_err[0] = 0;
     if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
     if (W) *W = idx->W;
     if (mu) *mu = idx->mu;
-    if (codes) *codes = idx->codes;
+    if (planes) *planes = idx->planes;
     if (n_pad) *n_pad = idx->lay.n_pad;
     return MP_OK;
 }

@@ -6,9 +6,11 @@
 //   scan_gather    a workgroup takes a run of 512-key chunks (each of one KV
 //                  head and its G query heads), as many workgroups as are
 //                  resident at once; per chunk:
-//                  (a) stream the chunk's codes (16-byte lane loads) and count,
-//                      per key and query head, the tables where the key shares
-//                      the query's bucket;
+//                  (a) stream the chunk's code planes and mark, per key and
+//                      query head, whether the key shares the query's bucket
+//                      in at least one and in at least two tables (32 keys per
+//                      32-bit word: a key matches a table iff each of its K
+//                      plane bits equals the query's bit);
 //                  (b) a key is sampled for a head iff that count is >= 2 and
 //                      the key is not in the exact set T (method details and
 //                      page "MagicPIG: don't pick the tallest", section 5);
@@ -24,6 +26,8 @@
 //                  The code stream runs two batches ahead across chunks, and
 //                  (c) runs one chunk late, so a chunk's rows arrive while the
 //                  next chunk is scanned.
+//   counts         (debug only) the exact collision count of every key and
+//                  query head, from the planes.
 //   merge          log-sum-exp merge of the chunk partials of every query head
 //                  (system co-design: partial attention outputs are merged
 //                  recursively).  A kernel of its own: its launch boundary is
@@ -38,18 +42,14 @@
 namespace mp {
 namespace {
 
-#ifndef MP_SCAN_BATCH
-#define MP_SCAN_BATCH 4
-#endif
-constexpr int kScanBatch = MP_SCAN_BATCH;   // tables per code batch in the scan
+// Table slots of a workgroup: thread t scans word t % kWords of the chunk in
+// tables t / kWords, + kSlots, ...
+constexpr int kSlots = 256 / kWords;
 
-// Per 16-bit half: min(a, b).  Written out because the compiler turns the
-// vector-extension form into compares and selects.
-__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b)
+// Bit b of x, replicated over 32 bits (0 or ~0).
+__device__ __forceinline__ uint32_t bit_mask(uint32_t x, int b)
 {
-    uint32_t d;
-    asm("v_pk_min_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
-    return d;
+    return uint32_t(__builtin_amdgcn_sbfe(int32_t(x), uint32_t(b), 1u));
 }
 
 // ---------------------------------------------------------------- query codes
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restri
 
 // ---------------------------------------------------------------- scan + gather
 // Waves per SIMD the register budget is cut for: 3 up to G = 4 with bf16 rows
-// (the next chunk's first code batches stay in registers through a gather),
+// (the next chunk's first plane batches stay in registers through a gather),
 // 2 otherwise.
 #ifndef MP_SCAN_OCC
 #define MP_SCAN_OCC 3
@@ -124,27 +124,39 @@ __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restri
 template <int G, typename T>
 constexpr int scan_occupancy() { return G <= 2 || (G == 4 && sizeof(T) == 2) ? MP_SCAN_OCC : 2; }
 
+// Plane rows loaded per table: Kr rounded up to one of a few compiled widths
+// (rows past Kr re-read row Kr - 1, which changes nothing).
+inline int plane_rows_class(int Kr)
+{
+    return Kr <= 4 ? 4 : Kr <= 8 ? 8 : Kr <= 10 ? 10 : Kr <= 12 ? 12 : 16;
+}
+
 // One workgroup takes a run of `cpb` consecutive 512-key chunks (numbered
 // over (sequence, KV head) units, then chunks); runs are as equal as the
 // chunk count allows and the grid is no larger than what is resident at
 // once.  Per chunk:
-//   (a) scan: wave w counts the chunk's tables [w L/4, (w+1) L/4);
+//   (a) scan: thread t takes the 32-key word t % 16 of the chunk in tables
+//       t / 16, t / 16 + 16, ...  For each table and query head, the key
+//       matches iff its K plane bits equal the query's code bits: an AND of
+//       K XNORs per 32 keys.  Per head the thread keeps two masks, "matched
+//       at least once" and "at least twice"; the 16 threads of a word merge
+//       theirs through LDS atomics;
 //   (b) the union of sampled and exact keys is compacted into an ascending
 //       LDS list, and the K/V rows of its first kRound entries are loaded;
 //   (c) gather-SNIS over the list, run one chunk late: after the next
 //       chunk's scan, when the rows have long arrived.  The chunk's partial
 //       softmax goes to `part`.
-// Each wave reads its tables of all chunks of the run as one stream of
-// kScanBatch-table batches in two alternating register buffers, issued two
-// batches ahead across chunk boundaries.  Every load on the main path is
-// unconditional (padding batches and rows re-read an address already read
-// and count nothing), so the compiler can wait on each buffer alone rather
-// than on every load in flight.
-template <int G, typename T>
+// Each thread reads its tables of all chunks of the run as one stream, one
+// table (KP plane words) per batch, in two alternating register buffers
+// issued two batches ahead across chunk boundaries.  Every load on the main
+// path is unconditional (padding batches and rows re-read an address already
+// read and count nothing), so the compiler can wait on each buffer alone
+// rather than on every load in flight.
+template <int G, typename T, int KP>
 __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_kernel(DecodeArgs a,
                                                                                     int32_t cpb)
 {
-    __shared__ uint32_t red[G][256];         // packed mismatch counts, word = 2 keys
+    __shared__ uint32_t seen[2][G][kWords];  // per head and word: matched once / twice
     __shared__ __align__(16) uint32_t sqq[256][G];   // query codes, code | code << 16
     __shared__ uint32_t ulist[kChunk];       // key | headmask << 16 | exact << 24
     __shared__ int wsum[4];
@@ -153,30 +165,25 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     __shared__ __align__(16) float smu[2][kD];   // mean of the unit's keys
     __shared__ GatherLds<G, T> gl;           // one gather round
 
-    const int w = uniform(threadIdx.x >> 6);
-    const int L = a.L;
+    const int L = a.L, Kr = a.Kr;
     const int gc_begin = blockIdx.x * cpb;
     const int nrun = min(cpb, a.B * a.H_kv * a.n_chunks - gc_begin);
-    const int lb = uniform((w * L) / 4), le = uniform(((w + 1) * L) / 4);
-    const int lmax = max(le - 1, 0);
-    // batches per chunk for this wave: even, and at least 2 (a wave without
-    // tables still streams, and counts nothing)
-    const int nb = uniform(max(2, ((le - lb + kScanBatch - 1) / kScanBatch + 1) & ~1));
-    const uint32_t one2 = 0x00010001u;
+    // batches (tables) per chunk for every thread: even, and at least 2
+    const int nb = uniform(max(2, ((L + kSlots - 1) / kSlots + 1) & ~1));
+    const int64_t rows_per_chunk = int64_t(L) * Kr * kWords;
 
-    // ---- the code stream: next batch to load is batch ls of chunk lc of the run ----
-    u32x4 bufA[kScanBatch], bufB[kScanBatch];
-    const int slane = threadIdx.x & 63;
+    // ---- the plane stream: next batch to load is batch ls of chunk lc of the run ----
+    uint32_t bufA[KP], bufB[KP];
+    const int sslot = threadIdx.x / kWords, sword = threadIdx.x % kWords;
     int lc = 0, ls = 0;
-    auto load_next = [&](u32x4(&buf)[kScanBatch]) {
+    auto load_next = [&](uint32_t(&buf)[KP]) {
         const bool past = lc >= nrun;                     // beyond the run: re-read the last batch
         const int c = past ? nrun - 1 : lc, sb = past ? nb - 1 : ls;
-        const u32x4 *cp = reinterpret_cast<const u32x4 *>(
-                               a.codes + int64_t(gc_begin + c) * L * kChunk) + slane;
-        const int l0 = lb + sb * kScanBatch;
+        const int l = min(sslot + sb * kSlots, L - 1);
+        const uint32_t *p = a.planes + int64_t(gc_begin + c) * rows_per_chunk +
+                            int64_t(l) * Kr * kWords + sword;
 #pragma unroll
-        for (int u = 0; u < kScanBatch; ++u)
-            buf[u] = cp[int64_t(min(l0 + u, lmax)) * (kChunk / 8)];
+        for (int r = 0; r < KP; ++r) buf[r] = p[min(r, Kr - 1) * kWords];
         if (++ls == nb) {
             ls = 0;
             ++lc;
@@ -187,8 +194,8 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     // Wait for both here (nothing else is in flight yet), so that at the top
     // of the chunk loop only the steady-state order of loads is possible:
     // bufA, bufB, then the previous chunk's rows.
-    asm volatile("" ::"v"(bufA[0]), "v"(bufA[1]), "v"(bufA[2]), "v"(bufA[3]), "v"(bufB[0]),
-                 "v"(bufB[1]), "v"(bufB[2]), "v"(bufB[3]));
+#pragma unroll
+    for (int r = 0; r < KP; ++r) asm volatile("" ::"v"(bufA[r]), "v"(bufB[r]));
 
     // the chunk whose gather is pending, and its rows
     bool pend = false;
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         // registers through it.
         int t = threadIdx.x;
         asm volatile("" : "+v"(t));
-        const int lane = t & 63, gi = t >> 4, li = t & 15;
+        const int gi = t >> 4, li = t & 15;
         const bool scan = it < nrun;
         const int gc = gc_begin + it;
         const int bkv = scan ? gc / a.n_chunks : 0;
@@ -212,9 +219,9 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         if (scan) {
             if (bkv != cur_unit) {
                 // A new (sequence, KV head) unit: its query codes for the scan
-                // ([table][head], one broadcast per table) and, in the other
-                // slot, the queries, norms and mean for its gathers (the
-                // pending chunk still reads the current slot).
+                // ([table][head]) and, in the other slot, the queries, norms
+                // and mean for its gathers (the pending chunk still reads the
+                // current slot).
                 slot ^= 1;
                 for (int i = t; i < G * L; i += 256) sqq[i % L][i / L] = a.qq[int64_t(bhq0) * L + i];
                 for (int i = t; i < G * kD; i += 256)
@@ -223,51 +230,49 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
                 if (t < kD) smu[slot][t] = a.mu[int64_t(bkv) * kD + t];
                 cur_unit = bkv;
             }
-            for (int i = t; i < G * 256; i += 256) (&red[0][0])[i] = 0u;
+            if (t < 2 * G * kWords) (&seen[0][0][0])[t] = 0u;
             __syncthreads();
 
-            // ---- (a) collision counts ----
-            uint32_t mism[4][G];
+            // ---- (a) collision masks ----
+            const int tslot = t / kWords, tword = t % kWords;
+            uint32_t once[G], twice[G];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+            for (int g = 0; g < G; ++g) once[g] = twice[g] = 0u;
+            auto count_batch = [&](const uint32_t(&buf)[KP], int sb) {
+                const int l = tslot + sb * kSlots;
+                const uint32_t live = l < L ? ~0u : 0u;   // padding batches match nothing
+                const int lu = min(l, L - 1);
 #pragma unroll
-                for (int g = 0; g < G; ++g) mism[k][g] = 0u;
-            auto count_batch = [&](const u32x4(&buf)[kScanBatch], int l0) {
-                const int nv = min(kScanBatch, le - l0);
+                for (int g = 0; g < G; ++g) {
+                    const uint32_t qv = sqq[lu][g];
+                    uint32_t eq = live;
 #pragma unroll
-                for (int u = 0; u < kScanBatch; ++u) {
-                    // padding (u >= nv) adds min(x, 0) = 0 mismatches
-                    const uint32_t lim = u < nv ? one2 : 0u;
-                    const int lu = min(l0 + u, lmax);
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const uint32_t qv = sqq[lu][g];
-                        mism[0][g] += pk_min_u16(buf[u].x ^ qv, lim);
-                        mism[1][g] += pk_min_u16(buf[u].y ^ qv, lim);
-                        mism[2][g] += pk_min_u16(buf[u].z ^ qv, lim);
-                        mism[3][g] += pk_min_u16(buf[u].w ^ qv, lim);
-                    }
+                    for (int r = 0; r < KP; ++r)
+                        eq &= ~(buf[r] ^ bit_mask(qv, min(r, Kr - 1)));
+                    twice[g] |= once[g] & eq;
+                    once[g] |= eq;
                 }
             };
             // The first pair is peeled: entering it, the previous chunk's
             // round-0 rows are younger than bufA and bufB and need not be
             // waited for; inside the loop only the other buffer is younger.
-            count_batch(bufA, lb);
+            count_batch(bufA, 0);
             load_next(bufA);
-            count_batch(bufB, lb + kScanBatch);
+            count_batch(bufB, 1);
             load_next(bufB);
             for (int sb = 2; sb < nb; sb += 2) {
-                count_batch(bufA, lb + sb * kScanBatch);
+                count_batch(bufA, sb);
                 load_next(bufA);
-                count_batch(bufB, lb + (sb + 1) * kScanBatch);
+                count_batch(bufB, sb + 1);
                 load_next(bufB);
             }
-            // Each half counts at most 255 tables, so a 32-bit add of the
-            // packed pair never carries between keys.
+            // Merge the 16 slots of each word: a key is seen twice if some
+            // slot saw it twice or two slots saw it once.
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int g = 0; g < G; ++g) atomicAdd(&red[g][lane * 4 + k], mism[k][g]);
+            for (int g = 0; g < G; ++g) {
+                const uint32_t before = atomicOr(&seen[0][g][tword], once[g]);
+                atomicOr(&seen[1][g][tword], twice[g] | (once[g] & before));
+            }
         }
 
         if (!scan && pend) {
@@ -286,46 +291,38 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
             gather_chunk<G, T>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot], sqn[p_slot],
                                smu[p_slot], kraw, vraw, t, gi, li);
         }
-        // counts in red are complete; the pending chunk's list is no longer
-        // read
+        // the masks in seen are complete; the pending chunk's list is no
+        // longer read
         __syncthreads();
         pend = false;
         if (!scan) break;
 
         // ---- (b) sampled / exact sets and ascending compaction ----
-        // Thread t owns keys 2t and 2t+1 of the chunk.
+        // Thread t owns keys 2t and 2t+1 of the chunk: bits 2(t%16), +1 of
+        // word t/16.
         const int n = a.n;
         const int64_t key0 = int64_t(chunk) * kChunk + 2 * t;
+        const int kw = t >> 4, ksh = 2 * (t & 15);
         uint32_t hm[2] = {0u, 0u};
         bool ex[2], fl[2];
-        uint32_t cnt[2][G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const uint32_t f = seen[1][g][kw] >> ksh;
+            hm[0] |= (f & 1u) << g;
+            hm[1] |= ((f >> 1) & 1u) << g;
+        }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int64_t i = key0 + e;
             const bool valid = i < n;
             ex[e] = valid && (i < a.n_sink || i >= int64_t(n) - a.n_local);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const uint32_t mm = (red[g][t] >> (16 * e)) & 0xFFFFu;
-                cnt[e][g] = uint32_t(L) - mm;
-                if (valid && !ex[e] && cnt[e][g] >= 2u) hm[e] |= 1u << g;
-            }
+            if (!valid || ex[e]) hm[e] = 0u;
             fl[e] = ex[e] || hm[e] != 0u;
         }
         const int total = compact_list(
             fl[0], fl[1], uint32_t(2 * t) | (hm[0] << 16) | (uint32_t(ex[0]) << 24),
             uint32_t(2 * t + 1) | (hm[1] << 16) | (uint32_t(ex[1]) << 24), ulist, wsum, t);
-        if (a.debug) {
-            if (a.counts) {
-#pragma unroll
-                for (int e = 0; e < 2; ++e)
-                    if (key0 + e < n)
-#pragma unroll
-                        for (int g = 0; g < G; ++g)
-                            a.counts[int64_t(bhq0 + g) * n + key0 + e] = uint8_t(cnt[e][g]);
-            }
-            write_seg_lists<G>(a, hm[0], hm[1], key0, bhq0, chunk, wsum, t);
-        }
+        if (a.debug) write_seg_lists<G>(a, hm[0], hm[1], key0, bhq0, chunk, wsum, t);
         __syncthreads();   // ulist complete
 
         // Round 0's rows of this chunk, in flight during the next scan.
@@ -340,6 +337,40 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         p_total = total;
         p_slot = slot;
     }
+}
+
+// ---------------------------------------------------------------- debug counts
+// Block = one 512-key chunk of one unit; thread t = keys 2t, 2t+1.  For each
+// table the two codes are read back from the planes and compared with the
+// codes of the G query heads (the exact count, which the scan never forms).
+template <int G>
+__global__ __launch_bounds__(256) void counts_kernel(DecodeArgs a)
+{
+    const int gc = blockIdx.x;
+    const int bkv = gc / a.n_chunks, chunk = gc - bkv * a.n_chunks;
+    const int bhq0 = (bkv / a.H_kv) * a.H_q + (bkv % a.H_kv) * G;
+    const int t = threadIdx.x, kw = t >> 4, ksh = 2 * (t & 15);
+    const int n = a.n, K = a.K, Kr = a.Kr;
+    const uint32_t *pc = a.planes + int64_t(gc) * a.L * Kr * kWords + kw;
+    uint32_t cnt[2][G] = {};
+    for (int l = 0; l < a.L; ++l) {
+        uint32_t code0 = 0u, code1 = 0u;
+        for (int b = 0; b < K; ++b) {
+            const uint32_t wv = pc[(int64_t(l) * Kr + b) * kWords] >> ksh;
+            code0 |= (wv & 1u) << b;
+            code1 |= ((wv >> 1) & 1u) << b;
+        }
+        for (int g = 0; g < G; ++g) {
+            const uint32_t qc = a.qcodes[int64_t(bhq0 + g) * a.L + l];
+            cnt[0][g] += code0 == qc;
+            cnt[1][g] += code1 == qc;
+        }
+    }
+    const int64_t key0 = int64_t(chunk) * kChunk + 2 * t;
+    for (int e = 0; e < 2; ++e)
+        if (key0 + e < n)
+            for (int g = 0; g < G; ++g)
+                a.counts[int64_t(bhq0 + g) * n + key0 + e] = uint8_t(cnt[e][g]);
 }
 
 // ---------------------------------------------------------------- merge
@@ -412,9 +443,9 @@ __global__ __launch_bounds__(256) void seg_compact_kernel(const int32_t *__restr
     if (t == 0 && s_len) s_len[bhq] = int32_t(off);
 }
 
-// Workgroups of scan_gather_kernel<G, T> resident at once on the current
+// Workgroups of scan_gather_kernel<G, T, KP> resident at once on the current
 // device (compute units x workgroups per unit), cached per device.
-template <int G, typename T>
+template <int G, typename T, int KP>
 int resident_workgroups()
 {
     static int cached[64] = {};
@@ -423,39 +454,51 @@ int resident_workgroups()
     if (cached[dev] == 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan_gather_kernel<G, T>, 256, 0) !=
-                hipSuccess)
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan_gather_kernel<G, T, KP>, 256,
+                                                         0) != hipSuccess)
             return 0;
         cached[dev] = cus * (per_cu > 0 ? per_cu : 1);
     }
     return cached[dev];
 }
 
-template <int G, typename T>
+template <int G, typename T, int KP>
 hipError_t launch_scan_gather_t(const DecodeArgs &a, hipStream_t s)
 {
     const int64_t chunks = int64_t(a.B) * a.H_kv * a.n_chunks;
-    const int slots = resident_workgroups<G, T>();
+    const int slots = resident_workgroups<G, T, KP>();
     if (slots <= 0) return hipErrorInvalidDevice;
     const int32_t cpb = ceil_div(chunks, slots);
     const dim3 grid(ceil_div(chunks, cpb));
     if (a.ev_begin || a.ev_end) {
         // timed entry point: the runtime stamps the events at this kernel's
         // own start and end
-        hipExtLaunchKernelGGL(scan_gather_kernel<G, T>, grid, dim3(256), 0, s,
+        hipExtLaunchKernelGGL(scan_gather_kernel<G, T, KP>, grid, dim3(256), 0, s,
                               static_cast<hipEvent_t>(a.ev_begin),
                               static_cast<hipEvent_t>(a.ev_end), 0, a, cpb);
     } else {
-        scan_gather_kernel<G, T><<<grid, 256, 0, s>>>(a, cpb);
+        scan_gather_kernel<G, T, KP><<<grid, 256, 0, s>>>(a, cpb);
     }
     return hipGetLastError();
+}
+
+template <int G, typename T>
+hipError_t launch_scan_gather_kp(const DecodeArgs &a, hipStream_t s)
+{
+    switch (plane_rows_class(a.Kr)) {
+    case 4: return launch_scan_gather_t<G, T, 4>(a, s);
+    case 8: return launch_scan_gather_t<G, T, 8>(a, s);
+    case 10: return launch_scan_gather_t<G, T, 10>(a, s);
+    case 12: return launch_scan_gather_t<G, T, 12>(a, s);
+    default: return launch_scan_gather_t<G, T, 16>(a, s);
+    }
 }
 
 template <int G>
 hipError_t launch_scan_gather(const DecodeArgs &a, hipStream_t s)
 {
-    return a.dtype == MP_BF16 ? launch_scan_gather_t<G, uint16_t>(a, s)
-                              : launch_scan_gather_t<G, float>(a, s);
+    return a.dtype == MP_BF16 ? launch_scan_gather_kp<G, uint16_t>(a, s)
+                              : launch_scan_gather_kp<G, float>(a, s);
 }
 
 }  // namespace
@@ -483,6 +526,20 @@ hipError_t launch_merge(const DecodeArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+hipError_t launch_counts(const DecodeArgs &a, hipStream_t s)
+{
+    if (!a.debug || !a.counts) return hipSuccess;
+    const dim3 grid(a.B * a.H_kv * a.n_chunks);
+    switch (a.G) {
+    case 1: counts_kernel<1><<<grid, 256, 0, s>>>(a); break;
+    case 2: counts_kernel<2><<<grid, 256, 0, s>>>(a); break;
+    case 4: counts_kernel<4><<<grid, 256, 0, s>>>(a); break;
+    case 8: counts_kernel<8><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_seg_compact(const DecodeArgs &a, hipStream_t s)
 {
     if (!a.debug || (!a.s_idx && !a.s_len)) return hipSuccess;
@@ -504,6 +561,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
     }
     if (e != hipSuccess) return e;
     if ((e = launch_merge(a, s)) != hipSuccess) return e;
+    if ((e = launch_counts(a, s)) != hipSuccess) return e;
     return launch_seg_compact(a, s);
 }
 

@@ -5,9 +5,11 @@
 //                 system co-design item 2: one random projector serves every head)
 //   mean          mu = mean of all n keys of each (sequence, KV head), fp64 sums
 //                 (same page, method details: centering before hashing)
-//   encode_keys   SimHash codes of x_i = k_i - mu on fp32 MFMA: bit j = [W_j.x_i > 0],
-//                 K bits per table packed LSB-first into uint16 (same page,
-//                 background: SimHash sign(w^T x); method details: K x L vectors)
+//   encode_keys   SimHash codes of x_i = k_i - mu on fp32 MFMA: bit j = [W_j.x_i > 0]
+//                 (same page, background: SimHash sign(w^T x); method details:
+//                 K x L vectors), stored as bit planes: per 512-key chunk and
+//                 hyperplane j = l*K + b, 16 words whose bit i is bit b of the
+//                 table-l code of key 32w + i.  A code costs its K bits.
 #include "mp_internal.h"
 
 namespace mp {
@@ -120,16 +122,17 @@ __global__ __launch_bounds__(kD) void mean_final_kernel(const double *__restrict
 
 // ---------------------------------------------------------------- encode
 // One block = 4 waves = 256 consecutive keys of one head; wave w owns keys
-// k0 = 256*blockIdx.x + 64*w .. +63 as 4 row tiles of 16.
+// k0 = 256*blockIdx.x + 64*w .. +63 as 4 tiles of 16.
 //
-// Contraction P[i][j] = sum_c x_i[c] W_j[c] on v_mfma_f32_16x16x4_f32
-// (A 16x4, B 4x16, 16x16 fp32 accumulate).  The 128-long contraction is split
-// in 32 k-steps; in k-step s, lane l feeds dim c = 32*(l/16) + s of row l%16
-// (A = keys) and of column l%16 (B = hyperplanes), so a lane reads 32
-// contiguous dims of one key row.  The result lane l holds rows
-// 4*(l/16) + r, column l%16 of the tile, so a ballot of register r gives
-// 16 sign bits of each of 4 rows: they go to LDS as 16-bit pieces and the
-// codes are cut out of the bit rows once every column tile is done.
+// Contraction P[j][i] = sum_c W_j[c] x_i[c] on v_mfma_f32_16x16x4_f32
+// (A 16x4, B 4x16, 16x16 fp32 accumulate), A = hyperplanes, B = keys.  The
+// 128-long contraction is split in 32 k-steps; in k-step s, lane l feeds dim
+// c = 32*(l/16) + s of hyperplane l%16 (A) and of key l%16 (B), so a lane
+// reads 32 contiguous dims of one key row.  The result lane l holds
+// hyperplanes 4*(l/16) + r of the tile, key l%16, so a ballot of register r
+// gives the sign bits of 16 keys for each of 4 hyperplanes: a 16-bit piece of
+// a plane word.  Pieces go to LDS ([hyperplane][key tile]) and leave as
+// 32-key words once every hyperplane tile is done.
 //
 // W tiles (8 KB each, fragment order) are staged through a double-buffered LDS
 // slot shared by the 4 waves.
@@ -137,18 +140,18 @@ template <typename T>
 __global__ __launch_bounds__(256) void encode_keys_kernel(
     const T *__restrict__ keys, int64_t sb, int64_t sh, int64_t sn, int32_t H, int32_t n,
     int32_t n_chunks, const float *__restrict__ mu, const float *__restrict__ Wp, int32_t K,
-    int32_t L, int32_t NT, int32_t pstride, uint16_t *__restrict__ codes)
+    int32_t L, int32_t NT, uint32_t *__restrict__ planes)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     float4 *wbuf = reinterpret_cast<float4 *>(smem);                       // [2][512] float4
-    uint16_t *bits = reinterpret_cast<uint16_t *>(smem + 2 * 512 * 16);    // [4][64][pstride]
+    uint16_t *pieces = reinterpret_cast<uint16_t *>(smem + 2 * 512 * 16);  // [4][16 NT][4]
 
     const int bh = blockIdx.y, b = bh / H, h = bh % H;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int il = lane & 15, g = lane >> 4;
     const int64_t k0 = int64_t(blockIdx.x) * 256 + 64 * w;
 
-    // A fragments: x = k - mu for 4 row tiles, dims 32g .. 32g+31.
+    // B fragments: x = k - mu for 4 key tiles, dims 32g .. 32g+31.
     float a[4][32];
     {
         float m[32];
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(256) void encode_keys_kernel(
     wbuf[256 + t] = pre1;
     __syncthreads();
 
-    uint16_t *mybits = bits + int64_t(w) * 64 * pstride;
+    uint16_t *mine = pieces + int64_t(w) * (16 * NT) * 4;
     for (int ct = 0; ct < NT; ++ct) {
         if (ct + 1 < NT) {
             pre0 = wp4[int64_t(ct + 1) * 512 + t];
@@ -201,13 +204,12 @@ __global__ __launch_bounds__(256) void encode_keys_kernel(
             floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 32; ++s)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt][s], bf[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[s], a[rt][s], acc, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const unsigned long long m = __ballot(acc[r] > 0.0f);
-                if (lane < 4)
-                    mybits[(16 * rt + 4 * lane + r) * pstride + ct] =
-                        uint16_t((m >> (16 * lane)) & 0xFFFFu);
+                if (lane < 4)   // lane q: hyperplane 16 ct + 4 q + r, keys 16 rt .. +15
+                    mine[(16 * ct + 4 * lane + r) * 4 + rt] = uint16_t((m >> (16 * lane)) & 0xFFFFu);
             }
         }
         if (ct + 1 < NT) {
@@ -217,21 +219,18 @@ __global__ __launch_bounds__(256) void encode_keys_kernel(
         __syncthreads();
     }
 
-    // Cut table codes out of the bit rows: lane = key.
-    const int64_t key = k0 + lane;
-    const int chunk = int(key / kChunk), within = int(key % kChunk);
-    uint16_t *cout = codes + (int64_t(bh) * n_chunks + chunk) * int64_t(L) * kChunk + within;
-    const uint16_t *row = mybits + lane * pstride;
-    const uint32_t kmask = (1u << K) - 1u;
-    for (int l = 0; l < L; ++l) {
-        const int pos = l * K, t0 = pos >> 4, o = pos & 15;
-        const uint32_t lo = row[t0];
-        const uint32_t hi = (t0 + 1 < NT) ? uint32_t(row[t0 + 1]) : 0u;
-        cout[int64_t(l) * kChunk] = uint16_t(((lo | (hi << 16)) >> o) & kmask);
+    // Plane words: item = (hyperplane j, half hf of the wave's 64 keys); the
+    // two 16-bit pieces of a half are one 32-bit LDS word.
+    const int chunk = int(k0 / kChunk), word0 = int(k0 % kChunk) / 32;
+    uint32_t *pout = planes + (int64_t(bh) * n_chunks + chunk) * int64_t(K) * L * kWords + word0;
+    const uint32_t *mine32 = reinterpret_cast<const uint32_t *>(mine);
+    for (int it = lane; it < 2 * K * L; it += 64) {
+        const int j = it >> 1, hf = it & 1;
+        pout[int64_t(j) * kWords + hf] = mine32[2 * j + hf];
     }
 }
 
-__global__ __launch_bounds__(256) void fill_u16_kernel(uint16_t *p, int64_t count)
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, int64_t count)
 {
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
          i += int64_t(gridDim.x) * blockDim.x)
@@ -267,11 +266,10 @@ hipError_t launch_mean(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, 
 
 hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
                               int32_t n_chunks, const float *mu, const float *Wp, int32_t K,
-                              int32_t L, int32_t R_pad, uint16_t *codes, hipStream_t s)
+                              int32_t L, int32_t R_pad, uint32_t *planes, hipStream_t s)
 {
     const int32_t NT = R_pad / 16;
-    const int32_t pstride = NT + ((6 - NT % 4) % 4);   // pstride % 4 == 2: odd dword stride
-    const size_t shmem = size_t(2) * 512 * 16 + size_t(4) * 64 * pstride * 2;
+    const size_t shmem = size_t(2) * 512 * 16 + size_t(4) * (16 * NT) * 4 * 2;
     const dim3 grid(n_chunks * (kChunk / 256), B * H);
     hipError_t e;
     if (dtype == MP_BF16) {
@@ -280,24 +278,24 @@ hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int3
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
         if (e != hipSuccess) return e;
         fn<<<grid, 256, shmem, s>>>(static_cast<const uint16_t *>(keys.data), keys.sb, keys.sh,
-                                    keys.sn, H, n, n_chunks, mu, Wp, K, L, NT, pstride, codes);
+                                    keys.sn, H, n, n_chunks, mu, Wp, K, L, NT, planes);
     } else {
         auto fn = encode_keys_kernel<float>;
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
         if (e != hipSuccess) return e;
         fn<<<grid, 256, shmem, s>>>(static_cast<const float *>(keys.data), keys.sb, keys.sh,
-                                    keys.sn, H, n, n_chunks, mu, Wp, K, L, NT, pstride, codes);
+                                    keys.sn, H, n, n_chunks, mu, Wp, K, L, NT, planes);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_fill_u16(uint16_t *p, int64_t count, hipStream_t s)
+hipError_t launch_fill_u32(uint32_t *p, int64_t count, hipStream_t s)
 {
     int64_t blocks = (count + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
-    fill_u16_kernel<<<dim3(uint32_t(blocks)), 256, 0, s>>>(p, count);
+    fill_u32_kernel<<<dim3(uint32_t(blocks)), 256, 0, s>>>(p, count);
     return hipGetLastError();
 }
 

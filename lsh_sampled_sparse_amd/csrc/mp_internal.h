@@ -10,6 +10,7 @@ namespace mp {
 
 constexpr int kD = 128;            // head dimension
 constexpr int kChunk = MP_CHUNK;   // keys per scan chunk: 64 lanes x 8 keys
+constexpr int kWords = kChunk / 32;   // 32-key words per chunk and plane row
 constexpr int kMeanRows = 1024;    // keys per partial-sum block of the mean pass
 constexpr uint64_t kMagic = 0x4D50494458303031ULL;  // "MPIDX001"
 
@@ -19,7 +20,8 @@ inline int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b);
 // Workspace layout of an index (all offsets 256-byte aligned).
 struct IndexLayout {
     int32_t B, H_kv, n, n_pad, n_chunks, n_mean_blocks, K, L, R, R_pad;
-    int64_t off_W, off_Wp, off_mu, off_mu_part, off_codes, total;
+    int32_t Kr;        // plane rows per table: K, or 1 (all zero) when K = 0
+    int64_t off_W, off_Wp, off_mu, off_mu_part, off_planes, total;
 };
 IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t L);
 
@@ -33,7 +35,8 @@ struct mp_index_impl {
     float *Wp;       // [R_pad/16][8][64][4] MFMA B-fragment order
     float *mu;       // [B*H_kv][128]
     double *mu_part; // [B*H_kv][n_mean_blocks][128]
-    uint16_t *codes; // [B*H_kv][n_chunks][L][kChunk]
+    uint32_t *planes; // [B*H_kv][n_chunks][L*Kr][kWords]: bit j of word w of row
+                      // l*Kr + b is bit b of the code of key 32w + j in table l
     // bucketed tables, once built (NULL until then)
     uint32_t *tab_off; // [B*H_kv][L][2^K + 1] bucket starts
     uint32_t *tab_ent; // [B*H_kv][L][n] keys, grouped by bucket
@@ -68,17 +71,17 @@ hipError_t launch_mean(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, 
                        int32_t n_mean_blocks, double *mu_part, float *mu, hipStream_t s);
 hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
                               int32_t n_chunks, const float *mu, const float *Wp, int32_t K,
-                              int32_t L, int32_t R_pad, uint16_t *codes, hipStream_t s);
-hipError_t launch_fill_u16(uint16_t *p, int64_t count, hipStream_t s);
+                              int32_t L, int32_t R_pad, uint32_t *planes, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t *p, int64_t count, hipStream_t s);
 
 struct DecodeArgs {
     const float *q;          // [BHq][128]
-    int32_t B, H_q, H_kv, G, n, n_chunks, K, L;
+    int32_t B, H_q, H_kv, G, n, n_chunks, K, L, Kr;
     int32_t n_sink, n_local;
     float scale;
     const float *W;          // [R][128]
     const float *mu;         // [B*H_kv][128]
-    const uint16_t *codes;   // index codes
+    const uint32_t *planes;  // index code planes
     const uint32_t *tab_off; // bucketed tables (table path only)
     const uint32_t *tab_ent;
     uint32_t *bits;          // scratch [BHq][slices][n_pad/16]: 2 bits per key (table path only)
@@ -91,7 +94,7 @@ struct DecodeArgs {
     int32_t *seg_idx;        // scratch [BHq][n_chunks * kChunk] (debug only)
     int32_t *seg_cnt;        // scratch [BHq][n_chunks] (debug only)
     float *out;              // [BHq][128]
-    uint8_t *counts;         // optional [BHq][n] (table path: min(count, 2))
+    uint8_t *counts;         // optional [BHq][n] (debug; table path: min(count, 2))
     int32_t *s_idx;          // optional [BHq][n]
     int32_t *s_len;          // optional [BHq]
     bool debug;
@@ -100,6 +103,7 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_counts(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_seg_compact(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_build_tables(const mp_index_impl &idx, hipStream_t s);
 hipError_t launch_decode_tables(const DecodeArgs &a, hipStream_t s);

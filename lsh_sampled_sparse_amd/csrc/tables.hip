@@ -65,21 +65,32 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *w
     return base + x - v;
 }
 
-// Block = one (unit, table).  Codes of key i of table l: chunk i/512, row l,
-// position i%512.  hist: nbins counters, then cursors.
+// Code of key i in the table whose plane rows start at `pl` (rows of one
+// chunk are L*Kr apart in whole chunks): its K bits, one per row.
+__device__ __forceinline__ uint32_t key_code(const uint32_t *pl, int64_t chunk_stride, int K,
+                                             int i)
+{
+    const uint32_t *w = pl + int64_t(i / kChunk) * chunk_stride + (i % kChunk) / 32;
+    const int bit = i % 32;
+    uint32_t c = 0u;
+    for (int b = 0; b < K; ++b) c |= ((w[b * kWords] >> bit) & 1u) << b;
+    return c;
+}
+
+// Block = one (unit, table).  hist: nbins counters, then cursors.
 __global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
-    const uint16_t *__restrict__ codes, int32_t n, int32_t n_chunks, int32_t L, int32_t nbins,
-    uint32_t *__restrict__ off, uint32_t *__restrict__ ent)
+    const uint32_t *__restrict__ planes, int32_t n, int32_t n_chunks, int32_t L, int32_t K,
+    int32_t Kr, int32_t nbins, uint32_t *__restrict__ off, uint32_t *__restrict__ ent)
 {
     extern __shared__ uint32_t hist[];
     __shared__ uint32_t wtot[kBuildThreads / 64];
     const int u = blockIdx.x / L, l = blockIdx.x % L;
     const int t = threadIdx.x;
-    const uint16_t *cb = codes + (int64_t(u) * n_chunks * L + l) * kChunk;
+    const int64_t cstride = int64_t(L) * Kr * kWords;
+    const uint32_t *pl = planes + int64_t(u) * n_chunks * cstride + int64_t(l) * Kr * kWords;
     for (int b = t; b < nbins; b += kBuildThreads) hist[b] = 0u;
     __syncthreads();
-    for (int i = t; i < n; i += kBuildThreads)
-        atomicAdd(&hist[cb[int64_t(i / kChunk) * L * kChunk + i % kChunk]], 1u);
+    for (int i = t; i < n; i += kBuildThreads) atomicAdd(&hist[key_code(pl, cstride, K, i)], 1u);
     __syncthreads();
     // thread t owns bins [t per, (t+1) per)
     const int per = (nbins + kBuildThreads - 1) / kBuildThreads;   // <= 4 for K <= 12
@@ -106,7 +117,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
     __syncthreads();
     uint32_t *e = ent + (int64_t(u) * L + l) * n;
     for (int i = t; i < n; i += kBuildThreads) {
-        const uint32_t c = cb[int64_t(i / kChunk) * L * kChunk + i % kChunk];
+        const uint32_t c = key_code(pl, cstride, K, i);
         e[atomicAdd(&hist[c], 1u)] = uint32_t(i);
     }
 }
@@ -289,7 +300,7 @@ hipError_t launch_build_tables(const mp_index_impl &idx, hipStream_t s)
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
     build_tables_kernel<<<dim3(lay.B * lay.H_kv * lay.L), kBuildThreads, lds, s>>>(
-        idx.codes, lay.n, lay.n_chunks, lay.L, nbins, idx.tab_off, idx.tab_ent);
+        idx.planes, lay.n, lay.n_chunks, lay.L, lay.K, lay.Kr, nbins, idx.tab_off, idx.tab_ent);
     return hipGetLastError();
 }
 

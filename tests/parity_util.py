@@ -32,12 +32,31 @@ def ulp_distance_f32(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(ai - bi)
 
 
+def unpack_planes(planes: np.ndarray, K: int, L: int, n: int) -> np.ndarray:
+    """Codes [L][n] uint16 of one (sequence, KV head) from its bit planes
+    [nc][L*max(K,1)][16] uint32: bit j of word w of row l*K + b is bit b of
+    the table-l code of key 32w + j of the chunk."""
+    nc, rows, words = planes.shape
+    Kr = max(K, 1)
+    assert rows == L * Kr and words * 32 == mp.MP_CHUNK
+    by = np.ascontiguousarray(planes.astype("<u4")).view(np.uint8).reshape(nc, L, Kr, words * 4)
+    bits = np.unpackbits(by, axis=-1, bitorder="little")          # [nc][L][Kr][512]
+    codes = np.zeros((nc, L, mp.MP_CHUNK), dtype=np.uint16)
+    for b in range(K):
+        codes |= bits[:, :, b, :].astype(np.uint16) << b
+    return codes.transpose(1, 0, 2).reshape(L, nc * mp.MP_CHUNK)[:, :n]
+
+
 def gpu_codes_table_major(idx: mp.MagicPIGIndex) -> np.ndarray:
-    """[B][H_kv][L][n] uint16 from the chunked device layout."""
-    _, _, codes = idx.views()
-    c = codes.cpu().numpy().view(np.uint16)            # [B][H][nc][L][512]
-    B, H, nc, L, ch = c.shape
-    return c.transpose(0, 1, 3, 2, 4).reshape(B, H, L, nc * ch)[..., :idx.n]
+    """[B][H_kv][L][n] uint16 from the device's bit planes."""
+    _, _, planes = idx.views()
+    p = planes.cpu().numpy().view(np.uint32)            # [B][H][nc][L*Kr][16]
+    B, H = p.shape[:2]
+    out = np.empty((B, H, idx.L, idx.n), dtype=np.uint16)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = unpack_planes(p[b, h], idx.K, idx.L, idx.n)
+    return out
 
 
 def check_codes(ref_vecs: np.ndarray, W: np.ndarray, K: int, L: int, got: np.ndarray, what: str):

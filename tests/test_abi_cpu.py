@@ -44,7 +44,8 @@ def test_workspace_bytes_rejects_bad_sizes_and_covers_codes():
     assert f(0, 8, 98304, 128, 10, 150) == 0
     assert f(1, 8, 0, 128, 10, 150) == 0
     a = f(1, 8, 98304, 128, 10, 150)
-    assert a >= 8 * 98304 * 150 * 2 and a % 256 == 0
+    codes = 8 * 98304 * 150 * 10 // 8            # K = 10 bits per key and table
+    assert codes <= a < codes + (8 << 20) and a % 256 == 0
     assert f(1, 8, 98305, 128, 10, 150) > a                 # ragged tail pads a chunk
     assert f(1, 8, 1, 128, 0, 2) > 0                         # K = 0 is allowed
 

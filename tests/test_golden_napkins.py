@@ -4,8 +4,8 @@ section 6 "The bill": table entries per token and per query at K=10, L=150),
 stored in tests/golden/page_napkins.json, against:
   * their own arithmetic (the stored numbers follow from the model shape);
   * the 96K workload the benchmark times (same model shape and (K, L));
-  * the index size the library reports (uint16 codes, one per table, instead
-    of the page's 32-bit token index per table entry);
+  * the index size the library reports (K-bit codes per table, the page's
+    packed hash bits, instead of its 32-bit token index per table entry);
   * the oracle's encoder and collision counts: a query's bucket in one table
     holds sum_i p_i^K keys in expectation over the hyperplanes, with
     p_i = 1 - theta_i/pi (page "MagicPIG: LSH Sampling for Efficient LLM
@@ -63,8 +63,9 @@ def test_index_bytes_against_the_pages_tables():
     m = GOLD["llama31_8b"]
     n, H, K, L = m["context"], m["kv_heads"], GOLD["K"], GOLD["L"]
     total = capi.mp_index_workspace_bytes(1, H, n, 128, K, L)
-    codes = H * n * L * 2                       # one uint16 per table, key and KV head
-    assert codes * 2 == H * n * GOLD["table_bytes_per_token_per_head_layer"]
+    codes = H * n * L * K // 8                  # K bits per table, key and KV head
+    # a 32-bit table entry per table and token is 32/K times the packed code
+    assert codes * 32 == H * n * GOLD["table_bytes_per_token_per_head_layer"] * K
     # the rest is W (two copies, fp32), mu and the fp64 partial sums of the mean
     assert 0 <= total - codes < 4 << 20
 
