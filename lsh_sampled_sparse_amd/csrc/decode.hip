@@ -45,11 +45,28 @@ namespace {
 // Table slots of a workgroup: thread t scans word t % kWords of the chunk in
 // tables t / kWords, + kSlots, ...
 constexpr int kSlots = 256 / kWords;
+#ifndef MP_SCAN_TB
+#define MP_SCAN_TB 1
+#endif
+constexpr int kTB = MP_SCAN_TB;   // tables per plane batch of a thread
 
 // Bit b of x, replicated over 32 bits (0 or ~0).
 __device__ __forceinline__ uint32_t bit_mask(uint32_t x, int b)
 {
     return uint32_t(__builtin_amdgcn_sbfe(int32_t(x), uint32_t(b), 1u));
+}
+
+// Fourth word of a raw buffer resource on gfx9-family parts: 32-bit data
+// format, no swizzle, no index stride.
+constexpr int kBufferWord3 = 0x00020000;
+
+// acc & ~(p ^ m) in one v_bitop3_b32 (truth table over (p, acc, m): set where
+// acc = 1 and p = m).  The compiler splits this form into XOR and OR3.
+__device__ __forceinline__ uint32_t and_xnor(uint32_t acc, uint32_t p, uint32_t m)
+{
+    uint32_t d;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x84" : "=v"(d) : "v"(p), "v"(acc), "v"(m));
+    return d;
 }
 
 // ---------------------------------------------------------------- query codes
@@ -168,22 +185,31 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     const int L = a.L, Kr = a.Kr;
     const int gc_begin = blockIdx.x * cpb;
     const int nrun = min(cpb, a.B * a.H_kv * a.n_chunks - gc_begin);
-    // batches (tables) per chunk for every thread: even, and at least 2
-    const int nb = uniform(max(2, ((L + kSlots - 1) / kSlots + 1) & ~1));
+    // batches per chunk for every thread: even, and at least 2
+    const int nt = (L + kSlots - 1) / kSlots;
+    const int nb = uniform(max(2, ((nt + kTB - 1) / kTB + 1) & ~1));
     const int64_t rows_per_chunk = int64_t(L) * Kr * kWords;
 
     // ---- the plane stream: next batch to load is batch ls of chunk lc of the run ----
-    uint32_t bufA[KP], bufB[KP];
+    uint32_t bufA[kTB][KP], bufB[kTB][KP];
     const int sslot = threadIdx.x / kWords, sword = threadIdx.x % kWords;
     int lc = 0, ls = 0;
-    auto load_next = [&](uint32_t(&buf)[KP]) {
+    auto load_next = [&](uint32_t(&buf)[kTB][KP]) {
         const bool past = lc >= nrun;                     // beyond the run: re-read the last batch
         const int c = past ? nrun - 1 : lc, sb = past ? nb - 1 : ls;
-        const int l = min(sslot + sb * kSlots, L - 1);
-        const uint32_t *p = a.planes + int64_t(gc_begin + c) * rows_per_chunk +
-                            int64_t(l) * Kr * kWords + sword;
+        // Raw buffer loads over the chunk's planes: the row offset is an
+        // SGPR and the lane's offset one VGPR, so a load costs no VALU.
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t *>(a.planes + int64_t(gc_begin + c) * rows_per_chunk), 0,
+            0x7FFFFFFF, kBufferWord3);
 #pragma unroll
-        for (int r = 0; r < KP; ++r) buf[r] = p[min(r, Kr - 1) * kWords];
+        for (int u = 0; u < kTB; ++u) {
+            const int l = min(sslot + (sb * kTB + u) * kSlots, L - 1);
+            const uint32_t off = uint32_t(l * Kr * kWords + sword) * 4u;
+#pragma unroll
+            for (int r = 0; r < KP; ++r)
+                buf[u][r] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, min(r, Kr - 1) * (kWords * 4), 0);
+        }
         if (++ls == nb) {
             ls = 0;
             ++lc;
@@ -195,7 +221,9 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     // of the chunk loop only the steady-state order of loads is possible:
     // bufA, bufB, then the previous chunk's rows.
 #pragma unroll
-    for (int r = 0; r < KP; ++r) asm volatile("" ::"v"(bufA[r]), "v"(bufB[r]));
+    for (int u = 0; u < kTB; ++u)
+#pragma unroll
+        for (int r = 0; r < KP; ++r) asm volatile("" ::"v"(bufA[u][r]), "v"(bufB[u][r]));
 
     // the chunk whose gather is pending, and its rows
     bool pend = false;
@@ -238,19 +266,22 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
             uint32_t once[G], twice[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) once[g] = twice[g] = 0u;
-            auto count_batch = [&](const uint32_t(&buf)[KP], int sb) {
-                const int l = tslot + sb * kSlots;
-                const uint32_t live = l < L ? ~0u : 0u;   // padding batches match nothing
-                const int lu = min(l, L - 1);
+            auto count_batch = [&](const uint32_t(&buf)[kTB][KP], int sb) {
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const uint32_t qv = sqq[lu][g];
-                    uint32_t eq = live;
+                for (int u = 0; u < kTB; ++u) {
+                    const int l = tslot + (sb * kTB + u) * kSlots;
+                    const uint32_t live = l < L ? ~0u : 0u;   // padding tables match nothing
+                    const int lu = min(l, L - 1);
 #pragma unroll
-                    for (int r = 0; r < KP; ++r)
-                        eq &= ~(buf[r] ^ bit_mask(qv, min(r, Kr - 1)));
-                    twice[g] |= once[g] & eq;
-                    once[g] |= eq;
+                    for (int g = 0; g < G; ++g) {
+                        const uint32_t qv = sqq[lu][g];
+                        uint32_t eq = live;
+#pragma unroll
+                        for (int r = 0; r < KP; ++r)
+                            eq = and_xnor(eq, buf[u][r], bit_mask(qv, min(r, Kr - 1)));
+                        twice[g] |= once[g] & eq;
+                        once[g] |= eq;
+                    }
                 }
             };
             // The first pair is peeled: entering it, the previous chunk's
