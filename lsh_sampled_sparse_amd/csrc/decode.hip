@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     __shared__ uint32_t ulist[kChunk];       // key | headmask << 16 | exact << 24
     __shared__ int wsum[4];
     __shared__ __align__(16) float sq[2][G][kD];   // per staged unit: the group's queries
-    __shared__ float sqn[2][G];              // their norms
+    __shared__ float sqn[2][2 * G];          // their norms, then q_g.mu
     __shared__ __align__(16) float smu[2][kD];   // mean of the unit's keys
     __shared__ GatherLds<G, T> gl;           // one gather round
 
@@ -245,7 +245,8 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         const int chunk = scan ? gc - bkv * a.n_chunks : 0;
         const int bhq0 = (bkv / a.H_kv) * a.H_q + (bkv % a.H_kv) * G;
         if (scan) {
-            if (bkv != cur_unit) {
+            const bool staged = bkv != cur_unit;
+            if (staged) {
                 // A new (sequence, KV head) unit: its query codes for the scan
                 // ([table][head]) and, in the other slot, the queries, norms
                 // and mean for its gathers (the pending chunk still reads the
@@ -260,6 +261,11 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
             }
             if (t < 2 * G * kWords) (&seen[0][0][0])[t] = 0u;
             __syncthreads();
+            if (staged && t < G) {   // q_g.mu of the new unit, read by its gathers
+                float qm = 0.0f;
+                for (int c = 0; c < kD; ++c) qm = fmaf(sq[slot][t][c], smu[slot][c], qm);
+                sqn[slot][G + t] = qm;
+            }
 
             // ---- (a) collision masks ----
             const int tslot = t / kWords, tword = t % kWords;

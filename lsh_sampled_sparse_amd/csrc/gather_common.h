@@ -157,7 +157,7 @@ __device__ __forceinline__ float wave_sum(float v)
 // LDS of one gather round: per listed row the three reduced products, per
 // (row, head) z and the weight exp(z - running max), and the row's V.
 template <int G, typename T> struct GatherLds {
-    float srow[kRound][2 * G + 1];   // q.k per head, q.(k-mu) per head, |k-mu|^2
+    float srow[kRound][G + 1];       // q.k per head, |k-mu|^2
     float sz[kRound][G];             // z, or -inf where the row is not in the head's set
     float sw[kRound][G];             // exp(z - running max), or 0
     __align__(16) T sv[kRound][kD];  // the round's V rows
@@ -209,10 +209,11 @@ __device__ __forceinline__ void load_rows(const DecodeArgs &a, const T *kb, cons
 }
 
 // One round over list entries [base, base + ne), ne <= kRound, whose K/V
-// words are kr / vr:
+// words are kr / vr.  sq: the G queries; sqn: their norms |q_g|, then q_g.mu;
+// smu: mu.
 //   c1: 16 groups of 16 lanes, lane = 8 dims; group gi takes rows gi, gi+16,
-//       ... of the round, stages its V rows in LDS and reduces q_g.k,
-//       q_g.(k - mu) and |k - mu|^2 over its lanes; the group's lanes then
+//       ... of the round, stages its V rows in LDS and reduces q_g.k and
+//       |k - mu|^2 over its lanes (q_g.(k - mu) is q_g.k - q_g.mu); the group's lanes then
 //       share out its (row, head) pairs and evaluate z for each: on T,
 //       z = q.k*scale; on S, z = q.k*scale - log u with
 //       p = 1 - acos(cos(q, k - mu))/pi;
@@ -247,29 +248,22 @@ __device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T
             x[j] = kr[j] - mu8[j];
             xx = fmaf(x[j], x[j], xx);
         }
-        float sd[G], td[G];
+        float sd[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const float4 q0 = *reinterpret_cast<const float4 *>(&sq[g][8 * li]);
             const float4 q1 = *reinterpret_cast<const float4 *>(&sq[g][8 * li + 4]);
             const float qg[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-            float s0 = 0.0f, t0 = 0.0f;
+            float s0 = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                s0 = fmaf(qg[j], kr[j], s0);
-                t0 = fmaf(qg[j], x[j], t0);
-            }
+            for (int j = 0; j < 8; ++j) s0 = fmaf(qg[j], kr[j], s0);
             sd[g] = row16_sum(s0);
-            td[g] = row16_sum(t0);
         }
         xx = row16_sum(xx);
         if (li == 0) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                s.srow[e][g] = sd[g];
-                s.srow[e][G + g] = td[g];
-            }
-            s.srow[e][2 * G] = xx;
+            for (int g = 0; g < G; ++g) s.srow[e][g] = sd[g];
+            s.srow[e][G] = xx;
         }
     }
     // z of the group's (row, head) pairs, one per lane (srow was written by
@@ -286,8 +280,9 @@ __device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T
             if (exact || ((ent >> (16 + g)) & 1u)) {
                 z = s.srow[e][g] * a.scale;
                 if (!exact) {
-                    const float den = sqn[g] * sqrtf(s.srow[e][2 * G]);
-                    float cs = den > 0.0f ? s.srow[e][G + g] / den : 0.0f;
+                    // q.(k - mu) = q.k - q.mu
+                    const float den = sqn[g] * sqrtf(s.srow[e][G]);
+                    float cs = den > 0.0f ? (s.srow[e][g] - sqn[G + g]) / den : 0.0f;
                     cs = fminf(fmaxf(cs, -1.0f), 1.0f);
                     const float pc = 1.0f - acosf(cs) * inv_pi;
                     z -= log_u_f32(pc, a.K, a.L);

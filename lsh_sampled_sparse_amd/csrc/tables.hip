@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int3
     __shared__ uint32_t ulist[kChunk];
     __shared__ int wsum[4];
     __shared__ __align__(16) float sq[G][kD];
-    __shared__ float sqn[G];
+    __shared__ float sqn[2 * G];   // |q_g|, then q_g.mu
     __shared__ __align__(16) float smu[kD];
     __shared__ GatherLds<G, T> gl;
     const int gc = blockIdx.x;
@@ -251,7 +251,12 @@ __global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int3
         }
         write_seg_lists<G>(a, hm[0], hm[1], key0, bhq0, chunk, wsum, t);
     }
-    __syncthreads();   // ulist and the staged queries complete
+    if (t < G) {   // q_g.mu (the staged queries are visible past the compaction's barriers)
+        float qm = 0.0f;
+        for (int c = 0; c < kD; ++c) qm = fmaf(sq[t][c], smu[c], qm);
+        sqn[G + t] = qm;
+    }
+    __syncthreads();   // ulist, the staged queries and q.mu complete
 
     typename Row8<T>::raw kr[kRowsPerGroup], vr[kRowsPerGroup];
     const T *kb, *vb;
