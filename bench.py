@@ -75,11 +75,11 @@ def measured_traffic(kernel: str):
 
 def scan_bytes_per_launch(cfg, union_rows: int) -> int:
     """Algorithmic bytes of one collision-scan + gather launch: every key code
-    of every (sequence, KV head) unit (L * n * 2 B), the K and V rows of the
-    union over the G query heads of sampled and exact keys (2 * d * elt B
-    each), and the fp32 queries."""
+    of every (sequence, KV head) unit (K bits per key and table: L * n * K / 8
+    B), the K and V rows of the union over the G query heads of sampled and
+    exact keys (2 * d * elt B each), and the fp32 queries."""
     elt = 2 if str(cfg.dtype).endswith("bfloat16") else 4
-    codes = cfg.B * cfg.H_kv * cfg.L * cfg.n * 2
+    codes = cfg.B * cfg.H_kv * cfg.L * cfg.n * cfg.K // 8
     rows = union_rows * 2 * cfg.d * elt
     q = cfg.B * cfg.H_q * cfg.d * 4
     return codes + rows + q
@@ -380,7 +380,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u16+f32",
+        "dtype": "u32+f32",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} "
                                f"n={cfg.n} d={cfg.d} K={cfg.K} L={cfg.L} T={cfg.n_sink}+"

@@ -87,18 +87,21 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 //   C(L,2) P^2 (1-P)^(L-2) * (1 + sum_{j>=3} prod_{i=2}^{j-1} (L-i)/(i+1) P/(1-P))
 // taken in logs.  p is floored at 1e-30: p = 0 only for an exactly
 // anti-parallel centered key, which cannot collide in exact arithmetic.
+// Plain logs and exponentials use the hardware log2/exp2 (about 1 ulp);
+// log1p(-P) and the expm1 of the closed form, which carry the cancellation,
+// use the full-precision routines.
 __device__ __forceinline__ float log_u_f32(float p, int K, int L)
 {
     if (K == 0) return 0.0f;
     p = fminf(fmaxf(p, 1e-30f), 1.0f);
-    const float logP = float(K) * logf(p);
-    const float P = expf(logP);
+    const float logP = float(K) * __logf(p);
+    const float P = __expf(logP);
     if (P >= 1.0f) return 0.0f;
     const float a = log1pf(-P);
     const float LP = float(L) * P;
     if (LP > 0.05f) {
-        const float u = -expm1f(float(L) * a) - LP * expf(float(L - 1) * a);
-        return logf(u);
+        const float u = -expm1f(float(L) * a) - LP * __expf(float(L - 1) * a);
+        return __logf(u);
     }
     const float r = P / (1.0f - P);
     float term = 1.0f, rest = 0.0f;
@@ -107,7 +110,26 @@ __device__ __forceinline__ float log_u_f32(float p, int K, int L)
         rest += term;
         if (term < 1e-9f * (1.0f + rest)) break;
     }
-    return logf(0.5f * float(L) * float(L - 1)) + 2.0f * logP + float(L - 2) * a + log1pf(rest);
+    return __logf(0.5f * float(L) * float(L - 1)) + 2.0f * logP + float(L - 2) * a + log1pf(rest);
+}
+
+// arccos(x) / pi for x in [-1, 1], from the minimax form of Abramowitz and
+// Stegun 4.4.46: on [0, 1], arccos(x) = sqrt(1 - x) (a0 + a1 x + ... + a7 x^7)
+// with absolute error at most 2e-8; arccos(-x) = pi - arccos(x).
+__device__ __forceinline__ float acos_over_pi(float x)
+{
+    const float ax = fabsf(x);
+    float r = -0.0012624911f;
+    r = fmaf(r, ax, 0.0066700901f);
+    r = fmaf(r, ax, -0.0170881256f);
+    r = fmaf(r, ax, 0.0308918810f);
+    r = fmaf(r, ax, -0.0501743046f);
+    r = fmaf(r, ax, 0.0889789874f);
+    r = fmaf(r, ax, -0.2145988016f);
+    r = fmaf(r, ax, 1.5707963050f);
+    r *= sqrtf(1.0f - ax);
+    const float inv_pi = 0.31830988618379067f;
+    return x >= 0.0f ? r * inv_pi : 1.0f - r * inv_pi;
 }
 
 // Full-rate cross-lane move inside a DPP row of 16 lanes.
@@ -210,43 +232,44 @@ __device__ __forceinline__ void load_rows(const DecodeArgs &a, const T *kb, cons
 
 // One round over list entries [base, base + ne), ne <= kRound, whose K/V
 // words are kr / vr.  sq: the G queries; sqn: their norms |q_g|, then q_g.mu;
-// smu: mu.
+// smu: mu.  Three steps:
 //   c1: 16 groups of 16 lanes, lane = 8 dims; group gi takes rows gi, gi+16,
 //       ... of the round, stages its V rows in LDS and reduces q_g.k and
-//       |k - mu|^2 over its lanes (q_g.(k - mu) is q_g.k - q_g.mu); the group's lanes then
-//       share out its (row, head) pairs and evaluate z for each: on T,
-//       z = q.k*scale; on S, z = q.k*scale - log u with
+//       |k - mu|^2 over its lanes (q_g.(k - mu) is q_g.k - q_g.mu);
+//   z:  the group's lanes share out its (row, head) pairs and evaluate z for
+//       each: on T, z = q.k*scale; on S, z = q.k*scale - log u with
 //       p = 1 - acos(cos(q, k - mu))/pi;
+//   (barrier)
 //   c2: wave w owns heads w, w+4, ...: it forms the round's max, the weights
 //       exp(z - max) and their sum, and each thread = (head, pair of dims)
-//       rescales its accumulator and adds the weighted V rows.
+//       rescales its accumulator and adds the weighted V rows;
+//   (barrier: the round's LDS may then be rewritten).
+// c1 and z of a group touch only LDS that the group's own wave writes, so
+// they need no barrier between them.
+
+// c1 for the group's rows gi + 16 r, r in [r0, r1).
 template <int G, typename T>
-__device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T> &s,
-                                             const uint32_t *ulist, int base, int ne,
-                                             const float (*sq)[kD], const float *sqn,
-                                             const float *smu,
-                                             const typename Row8<T>::raw (&kr_)[kRowsPerGroup],
-                                             const typename Row8<T>::raw (&vr_)[kRowsPerGroup],
-                                             GatherAcc<G> &acc, int t, int gi, int li)
+__device__ __forceinline__ void gather_c1(GatherLds<G, T> &s, int ne, const float (*sq)[kD],
+                                          const float *smu,
+                                          const typename Row8<T>::raw (&kr_)[kRowsPerGroup],
+                                          const typename Row8<T>::raw (&vr_)[kRowsPerGroup],
+                                          int gi, int li, int r0, int r1)
 {
-    constexpr int kZ = kRowsPerGroup * G;   // (row, head)s per group
-    const int lane = t & 63;
-    const float inv_pi = 0.31830988618379067f;
     const float4 m0 = reinterpret_cast<const float4 *>(smu)[2 * li];
     const float4 m1 = reinterpret_cast<const float4 *>(smu)[2 * li + 1];
     const float mu8[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
     for (int r = 0; r < kRowsPerGroup; ++r) {
         const int e = gi + 16 * r;
-        if (e >= ne) continue;            // uniform over the 16-lane group
+        if (r < r0 || r >= r1 || e >= ne) continue;   // uniform over the 16-lane group
         Row8<T>::store_raw(&s.sv[e][8 * li], vr_[r]);
-        float kr[8], x[8];
+        float kr[8];
         Row8<T>::convert(kr_[r], kr);
         float xx = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            x[j] = kr[j] - mu8[j];
-            xx = fmaf(x[j], x[j], xx);
+            const float x = kr[j] - mu8[j];
+            xx = fmaf(x, x, xx);
         }
         float sd[G];
 #pragma unroll
@@ -266,8 +289,16 @@ __device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T
             s.srow[e][G] = xx;
         }
     }
-    // z of the group's (row, head) pairs, one per lane (srow was written by
-    // this wave: LDS keeps a wave's accesses in order)
+}
+
+// z of the group's (row, head) pairs, one per lane (srow was written by this
+// wave: LDS keeps a wave's accesses in order).
+template <int G, typename T>
+__device__ __forceinline__ void gather_z(const DecodeArgs &a, GatherLds<G, T> &s,
+                                         const uint32_t *ulist, int base, int ne,
+                                         const float *sqn, int gi, int li)
+{
+    constexpr int kZ = kRowsPerGroup * G;   // (row, head)s per group
 #pragma unroll
     for (int k = 0; k < (kZ + 15) / 16; ++k) {
         const int zp = li + 16 * k;
@@ -284,14 +315,20 @@ __device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T
                     const float den = sqn[g] * sqrtf(s.srow[e][G]);
                     float cs = den > 0.0f ? (s.srow[e][g] - sqn[G + g]) / den : 0.0f;
                     cs = fminf(fmaxf(cs, -1.0f), 1.0f);
-                    const float pc = 1.0f - acosf(cs) * inv_pi;
+                    const float pc = 1.0f - acos_over_pi(cs);
                     z -= log_u_f32(pc, a.K, a.L);
                 }
             }
             s.sz[e][g] = z;
         }
     }
-    __syncthreads();
+}
+
+// c2 (after a barrier that makes every group's z visible).
+template <int G, typename T>
+__device__ __forceinline__ void gather_c2(GatherLds<G, T> &s, int ne, GatherAcc<G> &acc, int t)
+{
+    const int lane = t & 63;
 #pragma unroll
     for (int p = 0; p < GatherAcc<G>::kPairs; ++p) {
         const int g = uniform((t + 256 * p) / (kD / 2)), dp = lane;
@@ -316,7 +353,64 @@ __device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T
             acc.acc1[p] = x1;
         }
     }
+}
+
+template <int G, typename T>
+__device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T> &s,
+                                             const uint32_t *ulist, int base, int ne,
+                                             const float (*sq)[kD], const float *sqn,
+                                             const float *smu,
+                                             const typename Row8<T>::raw (&kr_)[kRowsPerGroup],
+                                             const typename Row8<T>::raw (&vr_)[kRowsPerGroup],
+                                             GatherAcc<G> &acc, int t, int gi, int li)
+{
+    gather_c1<G, T>(s, ne, sq, smu, kr_, vr_, gi, li, 0, kRowsPerGroup);
+    gather_z<G, T>(a, s, ulist, base, ne, sqn, gi, li);
+    __syncthreads();
+    gather_c2<G, T>(s, ne, acc, t);
     __syncthreads();   // srow, sz, sw, sv are rewritten by the next round
+}
+
+// Rounds after the first of a chunk's list (each loads its own rows); the
+// first round may have ended without its trailing barrier.
+template <int G, typename T>
+__device__ __forceinline__ void gather_rest(const DecodeArgs &a, GatherLds<G, T> &s,
+                                            const uint32_t *ulist, int total, int chunk, int bkv,
+                                            const float (*sq)[kD], const float *sqn,
+                                            const float *smu, GatherAcc<G> &acc, int t, int gi,
+                                            int li)
+{
+    if (total <= kRound) return;
+    __syncthreads();   // the first round's c2 may still read its LDS
+    const T *kb, *vb;
+    row_bases<T>(a, bkv, li, kb, vb);
+    for (int base = kRound; base < total; base += kRound) {
+        const int ne = min(kRound, total - base);
+        typename Row8<T>::raw kr[kRowsPerGroup], vr[kRowsPerGroup];
+        load_rows<T>(a, kb, vb, ulist, base, ne, chunk, gi, kr, vr);
+        gather_round<G, T>(a, s, ulist, base, ne, sq, sqn, smu, kr, vr, acc, t, gi, li);
+    }
+}
+
+// The chunk's partial softmax (max, sum, unnormalised accumulator) per head.
+template <int G>
+__device__ __forceinline__ void gather_store(const DecodeArgs &a, const GatherAcc<G> &acc,
+                                             int chunk, int bkv, int t)
+{
+    const int lane = t & 63;
+    float *part0 = a.part + (int64_t(bkv) * a.n_chunks + chunk) * (G * kPart);
+#pragma unroll
+    for (int p = 0; p < GatherAcc<G>::kPairs; ++p) {
+        const int g = uniform((t + 256 * p) / (kD / 2)), dp = lane;
+        if (g < G) {
+            part0[g * kPart + 2 + 2 * dp] = acc.acc0[p];
+            part0[g * kPart + 3 + 2 * dp] = acc.acc1[p];
+            if (dp == 0) {
+                part0[g * kPart] = acc.m[p];
+                part0[g * kPart + 1] = acc.l[p];
+            }
+        }
+    }
 }
 
 // The whole list of one chunk: round 0 from rows already loaded (kr0 / vr0),
@@ -335,30 +429,8 @@ __device__ __forceinline__ void gather_chunk(const DecodeArgs &a, GatherLds<G, T
     acc.reset();
     if (total > 0) gather_round<G, T>(a, s, ulist, 0, min(kRound, total), sq, sqn, smu, kr0, vr0,
                                       acc, t, gi, li);
-    if (total > kRound) {
-        const T *kb, *vb;
-        row_bases<T>(a, bkv, li, kb, vb);
-        for (int base = kRound; base < total; base += kRound) {
-            const int ne = min(kRound, total - base);
-            typename Row8<T>::raw kr[kRowsPerGroup], vr[kRowsPerGroup];
-            load_rows<T>(a, kb, vb, ulist, base, ne, chunk, gi, kr, vr);
-            gather_round<G, T>(a, s, ulist, base, ne, sq, sqn, smu, kr, vr, acc, t, gi, li);
-        }
-    }
-    const int lane = t & 63;
-    float *part0 = a.part + (int64_t(bkv) * a.n_chunks + chunk) * (G * kPart);
-#pragma unroll
-    for (int p = 0; p < GatherAcc<G>::kPairs; ++p) {
-        const int g = uniform((t + 256 * p) / (kD / 2)), dp = lane;
-        if (g < G) {
-            part0[g * kPart + 2 + 2 * dp] = acc.acc0[p];
-            part0[g * kPart + 3 + 2 * dp] = acc.acc1[p];
-            if (dp == 0) {
-                part0[g * kPart] = acc.m[p];
-                part0[g * kPart + 1] = acc.l[p];
-            }
-        }
-    }
+    gather_rest<G, T>(a, s, ulist, total, chunk, bkv, sq, sqn, smu, acc, t, gi, li);
+    gather_store<G>(a, acc, chunk, bkv, t);
 }
 
 // Ascending compaction of a chunk's flagged keys: thread t owns keys 2t and
