@@ -102,6 +102,34 @@ mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t 
                          void *workspace, size_t workspace_bytes, void *stream,
                          mp_index **out);
 
+/* mp_build_index over the n keys of `keys` into an index that
+ * mp_index_append can later grow to n_cap keys (n <= n_cap): the workspace
+ * must hold mp_index_workspace_bytes(B, H_kv, n_cap, 128, K, L) bytes.
+ * MP_E_ARG if n_cap < n or n_cap is not a valid key count. */
+mp_status mp_build_index_cap(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t seed,
+                             int32_t n_cap, void *workspace, size_t workspace_bytes,
+                             void *stream, mp_index **out);
+
+/* Grow an index to the first keys->n keys of its key cache: the keys past the
+ * index's n are centered by the mean mu fixed at build time and encoded with
+ * the index's hyperplanes, so a token that leaves the exact local window can
+ * join the sampled keys without a rebuild (page "MagicPIG: LSH Sampling for
+ * Efficient LLM Generation", system co-design: the sink and local tokens sit
+ * in a static cache beside the hashed keys; the pages do not say how mu
+ * moves as keys arrive: here it stays as built).
+ *   keys   the index's key cache viewed with its new length: [B][H_kv][n_new][128],
+ *          same B, H_kv and dtype, index's n <= n_new <= n_cap; its first n
+ *          keys must be the ones indexed.
+ * The enqueued encode also rewrites the plane words of the last 256 keys
+ * already indexed, with the same bits; decodes that read the index on other
+ * streams must be ordered with it.  The index then covers n_new keys: decode
+ * calls must pass K/V views of that length.  Bucketed tables built before are
+ * detached (the table calls then return MP_E_ARG until mp_build_tables runs
+ * again with a workspace for the new n).
+ * MP_E_HANDLE for a dead handle, MP_E_DTYPE / MP_E_SHAPE for keys that do not
+ * fit, MP_E_ARG when called on another device than the index's. */
+mp_status mp_index_append(mp_index *idx, const mp_kv_view *keys, void *stream);
+
 /* Bytes of device scratch one mp_decode_attn / mp_decode_debug call needs
  * for H_q query heads per sequence; 0 if invalid. */
 size_t mp_decode_scratch_bytes(const mp_index *idx, int32_t H_q);
@@ -203,12 +231,14 @@ mp_status mp_tables_views(const mp_index *idx, const uint32_t **offsets, const u
 /* Device pointers into the index workspace (valid while the workspace is):
  *   W      [R][128] fp32, R = K*L
  *   mu     [B][H_kv][128] fp32
- *   planes the key codes as bit planes, [B][H_kv][n_pad/MP_CHUNK][L*Kr][MP_CHUNK/32]
- *          uint32 with Kr = max(K, 1): bit j of word w of row l*Kr + b of
- *          chunk c is bit b of the table-l code of key c*MP_CHUNK + 32*w + j
- *          (K bits per key and table, the code's own width).  With K = 0
- *          every code is 0 and the one row per table is zero.  Keys i >= n
- *          are padding and never sampled.
+ *   planes the key codes as bit planes, [B][H_kv][nc][L*Kr][MP_CHUNK/32]
+ *          uint32 with Kr = max(K, 1) and nc = ceil(n_cap / MP_CHUNK) chunks
+ *          per (sequence, KV head) (n_cap = n unless built by
+ *          mp_build_index_cap); *n_pad/MP_CHUNK of them hold keys: bit j of
+ *          word w of row l*Kr + b of chunk c is bit b of the table-l code of
+ *          key c*MP_CHUNK + 32*w + j (K bits per key and table, the code's
+ *          own width).  With K = 0 every code is 0 and the one row per table
+ *          is zero.  Keys i >= n are padding and never sampled.
  * Any output pointer may be NULL. */
 mp_status mp_index_views(const mp_index *idx, const float **W, const float **mu,
                          const uint32_t **planes, int32_t *n_pad);

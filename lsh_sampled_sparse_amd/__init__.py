@@ -16,7 +16,8 @@ import torch
 from . import capi
 from .capi import MPError, MP_CHUNK
 
-__all__ = ["MagicPIGIndex", "build_index", "build_tables", "decode_attn", "decode_debug",
+__all__ = ["MagicPIGIndex", "build_index", "build_tables", "append_index", "decode_attn",
+           "decode_debug",
            "decode_attn_tables", "decode_tables_debug", "kv_view", "capi", "MPError", "MP_CHUNK"]
 
 _DTYPES = {torch.float32: capi.MP_F32, torch.bfloat16: capi.MP_BF16}
@@ -48,10 +49,11 @@ class MagicPIGIndex:
     W, mu and the key codes (as bit planes)."""
 
     def __init__(self, handle: int, workspace: torch.Tensor, keys_shape, K: int, L: int,
-                 seed: int, dtype):
+                 seed: int, dtype, capacity: int = 0):
         self.handle = handle
         self.workspace = workspace
         self.B, self.H_kv, self.n, self.d = keys_shape
+        self.capacity = max(capacity, self.n)
         self.K, self.L, self.seed, self.dtype = K, L, seed, dtype
         self.tables = None      # table workspace, once build_tables ran
 
@@ -80,10 +82,11 @@ class MagicPIGIndex:
         Wt = self._slice(W, R * 128, torch.float32).view(R, 128)
         mut = self._slice(mu, self.B * self.H_kv * 128, torch.float32).view(self.B, self.H_kv, 128)
         nc = n_pad // MP_CHUNK
+        nc_cap = -(-self.capacity // MP_CHUNK)       # chunks between units
         rows = self.L * max(self.K, 1)
         words = MP_CHUNK // 32
-        pt = self._slice(planes, self.B * self.H_kv * nc * rows * words, torch.int32)
-        return Wt, mut, pt.view(self.B, self.H_kv, nc, rows, words)
+        pt = self._slice(planes, self.B * self.H_kv * nc_cap * rows * words, torch.int32)
+        return Wt, mut, pt.view(self.B, self.H_kv, nc_cap, rows, words)[:, :, :nc]
 
     def scratch_bytes(self, H_q: int, tables: bool = False) -> int:
         if tables:
@@ -106,15 +109,33 @@ class MagicPIGIndex:
         return buf[off:off + numel * esz].view(dtype)
 
 
-def build_index(keys: torch.Tensor, K: int, L: int, seed: int, stream=None) -> MagicPIGIndex:
+def build_index(keys: torch.Tensor, K: int, L: int, seed: int, stream=None,
+                capacity: int | None = None) -> MagicPIGIndex:
+    """Index of `keys` [B][H_kv][n][128]; with `capacity` (>= n) it can later
+    grow to that many keys by append_index (see mp_build_index_cap)."""
     view = kv_view(keys)
-    nbytes = capi.mp_index_workspace_bytes(view.B, view.H, view.n, view.d, K, L)
+    n_cap = view.n if capacity is None else capacity
+    nbytes = capi.mp_index_workspace_bytes(view.B, view.H, n_cap, view.d, K, L)
     if nbytes == 0:
-        raise ValueError(f"invalid index sizes B={view.B} H={view.H} n={view.n} d={view.d} "
+        raise ValueError(f"invalid index sizes B={view.B} H={view.H} n={n_cap} d={view.d} "
                          f"K={K} L={L}")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=keys.device)
-    h = capi.mp_build_index(view, K, L, seed, ws.data_ptr(), nbytes, _stream(stream))
-    return MagicPIGIndex(h, ws, tuple(keys.shape), K, L, seed, keys.dtype)
+    if capacity is None:
+        h = capi.mp_build_index(view, K, L, seed, ws.data_ptr(), nbytes, _stream(stream))
+    else:
+        h = capi.mp_build_index_cap(view, K, L, seed, n_cap, ws.data_ptr(), nbytes,
+                                    _stream(stream))
+    return MagicPIGIndex(h, ws, tuple(keys.shape), K, L, seed, keys.dtype, n_cap)
+
+
+def append_index(index: MagicPIGIndex, keys: torch.Tensor, stream=None) -> MagicPIGIndex:
+    """Grow `index` to the keys of `keys` [B][H_kv][n_new][128], whose first
+    index.n keys are the indexed ones (see mp_index_append).  Detaches any
+    bucketed tables."""
+    capi.mp_index_append(index.handle, kv_view(keys), _stream(stream))
+    index.n = keys.shape[2]
+    index.tables = None
+    return index
 
 
 def build_tables(index: MagicPIGIndex, stream=None) -> MagicPIGIndex:

@@ -22,7 +22,7 @@ EXPORTED = [
     "mp_decode_attn_timed", "mp_decode_debug", "mp_index_views", "mp_index_destroy", "mp_status_str", "mp_last_error",
     "mp_tables_workspace_bytes", "mp_build_tables", "mp_decode_tables_scratch_bytes",
     "mp_decode_attn_tables", "mp_decode_attn_tables_timed", "mp_decode_tables_debug",
-    "mp_tables_views",
+    "mp_tables_views", "mp_build_index_cap", "mp_index_append",
 ]
 
 
@@ -58,6 +58,11 @@ def lib():
         L.mp_build_index.restype = C.c_int
         L.mp_build_index.argtypes = [C.POINTER(mp_kv_view), i32, i32, C.c_uint64, vp, sz, vp,
                                      C.POINTER(vp)]
+        L.mp_build_index_cap.restype = C.c_int
+        L.mp_build_index_cap.argtypes = [C.POINTER(mp_kv_view), i32, i32, C.c_uint64, i32, vp, sz,
+                                         vp, C.POINTER(vp)]
+        L.mp_index_append.restype = C.c_int
+        L.mp_index_append.argtypes = [vp, C.POINTER(mp_kv_view), vp]
         L.mp_decode_scratch_bytes.restype = sz
         L.mp_decode_scratch_bytes.argtypes = [vp, i32]
         dec = [vp, i32, vp, C.POINTER(mp_kv_view), C.POINTER(mp_kv_view), i32, i32, C.c_float,
@@ -120,6 +125,20 @@ def mp_build_index(keys: mp_kv_view, K: int, L: int, seed: int, workspace: int,
                               workspace_bytes, stream, C.byref(out))
     _check(st, "mp_build_index")
     return out.value
+
+
+def mp_build_index_cap(keys: mp_kv_view, K: int, L: int, seed: int, n_cap: int, workspace: int,
+                       workspace_bytes: int, stream: int) -> int:
+    """mp_build_index with room to grow to n_cap keys; returns the handle."""
+    out = C.c_void_p()
+    st = lib().mp_build_index_cap(C.byref(keys), K, L, seed & (2**64 - 1), n_cap, workspace,
+                                  workspace_bytes, stream, C.byref(out))
+    _check(st, "mp_build_index_cap")
+    return out.value
+
+
+def mp_index_append(idx: int, keys: mp_kv_view, stream: int) -> None:
+    _check(lib().mp_index_append(idx, C.byref(keys), stream), "mp_index_append")
 
 
 def mp_decode_scratch_bytes(idx: int, H_q: int) -> int:

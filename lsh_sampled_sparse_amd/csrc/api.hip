@@ -25,15 +25,27 @@ static mp_status fail(mp_status s, const char *fmt, ...)
     return s;
 }
 
-IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t L)
+// The counts that describe the first n keys of an index.
+static void set_index_keys(IndexLayout &y, int32_t n)
 {
-    IndexLayout y{};
-    y.B = B;
-    y.H_kv = H_kv;
     y.n = n;
     y.n_chunks = ceil_div(n, kChunk);
     y.n_pad = y.n_chunks * kChunk;
     y.n_mean_blocks = ceil_div(n, kMeanRows);
+}
+
+IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t L, int32_t n_cap)
+{
+    if (n_cap < n) n_cap = n;
+    IndexLayout y{};
+    y.B = B;
+    y.H_kv = H_kv;
+    y.n = n_cap;             // regions are sized for n_cap; n is set below
+    y.n_chunks = ceil_div(n_cap, kChunk);
+    y.n_pad = y.n_chunks * kChunk;
+    y.n_mean_blocks = ceil_div(n_cap, kMeanRows);
+    y.n_cap = n_cap;
+    y.nc_cap = y.n_chunks;
     y.K = K;
     y.L = L;
     y.R = K * L;
@@ -45,8 +57,9 @@ IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t 
     y.off_Wp = off;      off = align256(off + int64_t(y.R_pad) * kD * 4);
     y.off_mu = off;      off = align256(off + BH * kD * 4);
     y.off_mu_part = off; off = align256(off + BH * y.n_mean_blocks * kD * 8);
-    y.off_planes = off;  off = align256(off + BH * y.n_chunks * int64_t(L) * y.Kr * kWords * 4);
+    y.off_planes = off;  off = align256(off + BH * y.nc_cap * int64_t(L) * y.Kr * kWords * 4);
     y.total = off;
+    set_index_keys(y, n);
     return y;
 }
 
@@ -177,6 +190,7 @@ static mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx,
     a.mu = idx->mu;
     a.planes = idx->planes;
     a.Kr = lay.Kr;
+    a.nc_cap = lay.nc_cap;
     a.k = KVRows{k->data, k->stride_b, k->stride_h, k->stride_n, k->H};
     a.v = KVRows{v->data, v->stride_b, v->stride_h, v->stride_n, v->H};
     a.dtype = k->dtype;
@@ -218,8 +232,9 @@ size_t mp_index_workspace_bytes(int32_t B, int32_t H_kv, int32_t n, int32_t d, i
     return size_t(index_layout(B, H_kv, n, K, L).total);
 }
 
-mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t seed,
-                         void *workspace, size_t workspace_bytes, void *stream, mp_index **out)
+static mp_status build_index_impl(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t seed,
+                                  int32_t n_cap, void *workspace, size_t workspace_bytes,
+                                  void *stream, mp_index **out)
 {
     g_err[0] = 0;
     if (!out) return fail(MP_E_ARG, "out is NULL");
@@ -230,7 +245,10 @@ mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t 
     if (L < 2 || L > 255) return fail(MP_E_ARG, "L = %d outside [2, 255]", L);
     if (int64_t(keys->B) * keys->H > 65535)
         return fail(MP_E_SHAPE, "B*H_kv = %lld is too large", (long long)keys->B * keys->H);
-    const IndexLayout lay = index_layout(keys->B, keys->H, keys->n, K, L);
+    if (n_cap < keys->n) return fail(MP_E_ARG, "capacity %d is below the %d keys", n_cap, keys->n);
+    if (mp_index_workspace_bytes(keys->B, keys->H, n_cap, keys->d, K, L) == 0)
+        return fail(MP_E_ARG, "capacity %d is not a valid key count", n_cap);
+    const IndexLayout lay = index_layout(keys->B, keys->H, keys->n, K, L, n_cap);
     if (!workspace) return fail(MP_E_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) & 255)
         return fail(MP_E_WORKSPACE, "workspace must be 256-byte aligned");
@@ -261,12 +279,12 @@ mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t 
         e = launch_mean(rows, keys->dtype, lay.B, lay.H_kv, lay.n, lay.n_mean_blocks, idx->mu_part,
                         idx->mu, s);
     if (e == hipSuccess) {
-        const int64_t nwords = int64_t(lay.B) * lay.H_kv * lay.n_chunks * int64_t(L) * lay.Kr * kWords;
+        const int64_t nwords = int64_t(lay.B) * lay.H_kv * lay.nc_cap * int64_t(L) * lay.Kr * kWords;
         if (K == 0)
             e = launch_fill_u32(idx->planes, nwords, s);   // every code is 0: one zero row per table
         else
-            e = launch_encode_keys(rows, keys->dtype, lay.B, lay.H_kv, lay.n, lay.n_chunks, idx->mu,
-                                   idx->Wp, K, L, lay.R_pad, idx->planes, s);
+            e = launch_encode_keys(rows, keys->dtype, lay.B, lay.H_kv, lay.n, lay.nc_cap, idx->mu,
+                                   idx->Wp, K, L, lay.R_pad, idx->planes, 0, s);
     }
     if (e != hipSuccess) {
         idx->magic = 0;
@@ -274,6 +292,56 @@ mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t 
         return fail(MP_E_HIP, "index build launch failed: %s", hipGetErrorString(e));
     }
     *out = idx;
+    return MP_OK;
+}
+
+mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t seed,
+                         void *workspace, size_t workspace_bytes, void *stream, mp_index **out)
+{
+    return build_index_impl(keys, K, L, seed, keys ? keys->n : 0, workspace, workspace_bytes,
+                            stream, out);
+}
+
+mp_status mp_build_index_cap(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t seed,
+                             int32_t n_cap, void *workspace, size_t workspace_bytes, void *stream,
+                             mp_index **out)
+{
+    return build_index_impl(keys, K, L, seed, n_cap, workspace, workspace_bytes, stream, out);
+}
+
+mp_status mp_index_append(mp_index *idx, const mp_kv_view *keys, void *stream)
+{
+    g_err[0] = 0;
+    if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
+    mp_status st = check_view(keys, "keys");
+    if (st != MP_OK) return st;
+    IndexLayout &lay = idx->lay;
+    if (keys->dtype != idx->key_dtype) return fail(MP_E_DTYPE, "keys dtype differs from the index's");
+    if (keys->B != lay.B || keys->H != lay.H_kv)
+        return fail(MP_E_SHAPE, "keys are [%d][%d][...], the index covers [%d][%d]", keys->B,
+                    keys->H, lay.B, lay.H_kv);
+    if (keys->n < lay.n)
+        return fail(MP_E_SHAPE, "keys hold %d keys, fewer than the index's %d", keys->n, lay.n);
+    if (keys->n > lay.n_cap)
+        return fail(MP_E_SHAPE, "%d keys exceed the index capacity %d", keys->n, lay.n_cap);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != idx->device)
+        return fail(MP_E_ARG, "the current device is not the index's device");
+    if (keys->n == lay.n) return MP_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (lay.K > 0) {
+        // from the 256-key block holding the first new key: its old keys are
+        // encoded again to the same bits, so every plane word is written whole
+        const KVRows rows{keys->data, keys->stride_b, keys->stride_h, keys->stride_n, keys->H};
+        const hipError_t e =
+            launch_encode_keys(rows, keys->dtype, lay.B, lay.H_kv, keys->n, lay.nc_cap, idx->mu,
+                               idx->Wp, lay.K, lay.L, lay.R_pad, idx->planes, lay.n / 256, s);
+        if (e != hipSuccess)
+            return fail(MP_E_HIP, "append launch failed: %s", hipGetErrorString(e));
+    }
+    set_index_keys(lay, keys->n);
+    idx->tab_off = nullptr;    // tables of the old keys no longer describe the index
+    idx->tab_ent = nullptr;
     return MP_OK;
 }
 

@@ -199,9 +199,10 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         const int c = past ? nrun - 1 : lc, sb = past ? nb - 1 : ls;
         // Raw buffer loads over the chunk's planes: the row offset is an
         // SGPR and the lane's offset one VGPR, so a load costs no VALU.
+        const int gcx = gc_begin + c, ubkv = gcx / a.n_chunks;
+        const int64_t pchunk = int64_t(ubkv) * a.nc_cap + (gcx - ubkv * a.n_chunks);
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint32_t *>(a.planes + int64_t(gc_begin + c) * rows_per_chunk), 0,
-            0x7FFFFFFF, kBufferWord3);
+            const_cast<uint32_t *>(a.planes + pchunk * rows_per_chunk), 0, 0x7FFFFFFF, kBufferWord3);
 #pragma unroll
         for (int u = 0; u < kTB; ++u) {
             const int l = min(sslot + (sb * kTB + u) * kSlots, L - 1);
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(256) void counts_kernel(DecodeArgs a)
     const int bhq0 = (bkv / a.H_kv) * a.H_q + (bkv % a.H_kv) * G;
     const int t = threadIdx.x, kw = t >> 4, ksh = 2 * (t & 15);
     const int n = a.n, K = a.K, Kr = a.Kr;
-    const uint32_t *pc = a.planes + int64_t(gc) * a.L * Kr * kWords + kw;
+    const uint32_t *pc = a.planes + (int64_t(bkv) * a.nc_cap + chunk) * a.L * Kr * kWords + kw;
     uint32_t cnt[2][G] = {};
     for (int l = 0; l < a.L; ++l) {
         uint32_t code0 = 0u, code1 = 0u;

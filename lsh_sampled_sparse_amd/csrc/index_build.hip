@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kD) void mean_final_kernel(const double *__restrict
 
 // ---------------------------------------------------------------- encode
 // One block = 4 waves = 256 consecutive keys of one head; wave w owns keys
-// k0 = 256*blockIdx.x + 64*w .. +63 as 4 tiles of 16.
+// k0 = 256*(kb0 + blockIdx.x) + 64*w .. +63 as 4 tiles of 16.
 //
 // Contraction P[j][i] = sum_c W_j[c] x_i[c] on v_mfma_f32_16x16x4_f32
 // (A 16x4, B 4x16, 16x16 fp32 accumulate), A = hyperplanes, B = keys.  The
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(kD) void mean_final_kernel(const double *__restrict
 template <typename T>
 __global__ __launch_bounds__(256) void encode_keys_kernel(
     const T *__restrict__ keys, int64_t sb, int64_t sh, int64_t sn, int32_t H, int32_t n,
-    int32_t n_chunks, const float *__restrict__ mu, const float *__restrict__ Wp, int32_t K,
-    int32_t L, int32_t NT, uint32_t *__restrict__ planes)
+    int32_t nc_cap, const float *__restrict__ mu, const float *__restrict__ Wp, int32_t K,
+    int32_t L, int32_t NT, uint32_t *__restrict__ planes, int32_t kb0)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     float4 *wbuf = reinterpret_cast<float4 *>(smem);                       // [2][512] float4
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void encode_keys_kernel(
     const int bh = blockIdx.y, b = bh / H, h = bh % H;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int il = lane & 15, g = lane >> 4;
-    const int64_t k0 = int64_t(blockIdx.x) * 256 + 64 * w;
+    const int64_t k0 = int64_t(kb0 + blockIdx.x) * 256 + 64 * w;
 
     // B fragments: x = k - mu for 4 key tiles, dims 32g .. 32g+31.
     float a[4][32];
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256) void encode_keys_kernel(
     // Plane words: item = (hyperplane j, half hf of the wave's 64 keys); the
     // two 16-bit pieces of a half are one 32-bit LDS word.
     const int chunk = int(k0 / kChunk), word0 = int(k0 % kChunk) / 32;
-    uint32_t *pout = planes + (int64_t(bh) * n_chunks + chunk) * int64_t(K) * L * kWords + word0;
+    uint32_t *pout = planes + (int64_t(bh) * nc_cap + chunk) * int64_t(K) * L * kWords + word0;
     const uint32_t *mine32 = reinterpret_cast<const uint32_t *>(mine);
     for (int it = lane; it < 2 * K * L; it += 64) {
         const int j = it >> 1, hf = it & 1;
@@ -265,12 +265,17 @@ hipError_t launch_mean(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, 
 }
 
 hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
-                              int32_t n_chunks, const float *mu, const float *Wp, int32_t K,
-                              int32_t L, int32_t R_pad, uint32_t *planes, hipStream_t s)
+                              int32_t nc_cap, const float *mu, const float *Wp, int32_t K,
+                              int32_t L, int32_t R_pad, uint32_t *planes, int32_t kb0,
+                              hipStream_t s)
 {
     const int32_t NT = R_pad / 16;
     const size_t shmem = size_t(2) * 512 * 16 + size_t(4) * (16 * NT) * 4 * 2;
-    const dim3 grid(n_chunks * (kChunk / 256), B * H);
+    // every 256-key block up to the end of the last chunk, so the padding
+    // keys of the last chunk are written too (as zero rows)
+    const int32_t nblocks = ceil_div(n, kChunk) * (kChunk / 256) - kb0;
+    if (nblocks <= 0) return hipSuccess;
+    const dim3 grid(nblocks, B * H);
     hipError_t e;
     if (dtype == MP_BF16) {
         auto fn = encode_keys_kernel<uint16_t>;
@@ -278,14 +283,14 @@ hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int3
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
         if (e != hipSuccess) return e;
         fn<<<grid, 256, shmem, s>>>(static_cast<const uint16_t *>(keys.data), keys.sb, keys.sh,
-                                    keys.sn, H, n, n_chunks, mu, Wp, K, L, NT, planes);
+                                    keys.sn, H, n, nc_cap, mu, Wp, K, L, NT, planes, kb0);
     } else {
         auto fn = encode_keys_kernel<float>;
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
         if (e != hipSuccess) return e;
         fn<<<grid, 256, shmem, s>>>(static_cast<const float *>(keys.data), keys.sb, keys.sh,
-                                    keys.sn, H, n, n_chunks, mu, Wp, K, L, NT, planes);
+                                    keys.sn, H, n, nc_cap, mu, Wp, K, L, NT, planes, kb0);
     }
     return hipGetLastError();
 }

@@ -21,9 +21,13 @@ inline int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b);
 struct IndexLayout {
     int32_t B, H_kv, n, n_pad, n_chunks, n_mean_blocks, K, L, R, R_pad;
     int32_t Kr;        // plane rows per table: K, or 1 (all zero) when K = 0
+    int32_t n_cap, nc_cap;   // keys the index may grow to; plane chunks per unit
     int64_t off_W, off_Wp, off_mu, off_mu_part, off_planes, total;
 };
-IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t L);
+// Layout of an index over n keys with room for n_cap >= n (regions sized for
+// n_cap; the n-dependent counts describe the n keys).
+IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t L,
+                         int32_t n_cap = 0);
 
 struct mp_index_impl {
     uint64_t magic;
@@ -69,14 +73,18 @@ struct KVRows {
 hipError_t launch_wgen(uint64_t seed, int32_t R, int32_t R_pad, float *W, float *Wp, hipStream_t s);
 hipError_t launch_mean(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
                        int32_t n_mean_blocks, double *mu_part, float *mu, hipStream_t s);
+// Encodes keys [256 kb0, n) (whole 256-key blocks; keys >= n are zero rows)
+// into planes whose units are nc_cap chunks apart.
 hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
-                              int32_t n_chunks, const float *mu, const float *Wp, int32_t K,
-                              int32_t L, int32_t R_pad, uint32_t *planes, hipStream_t s);
+                              int32_t nc_cap, const float *mu, const float *Wp, int32_t K,
+                              int32_t L, int32_t R_pad, uint32_t *planes, int32_t kb0,
+                              hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int64_t count, hipStream_t s);
 
 struct DecodeArgs {
     const float *q;          // [BHq][128]
     int32_t B, H_q, H_kv, G, n, n_chunks, K, L, Kr;
+    int32_t nc_cap;          // plane chunks per unit (units are this far apart)
     int32_t n_sink, n_local;
     float scale;
     const float *W;          // [R][128]

@@ -79,7 +79,7 @@ __device__ __forceinline__ uint32_t key_code(const uint32_t *pl, int64_t chunk_s
 
 // Block = one (unit, table).  hist: nbins counters, then cursors.
 __global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
-    const uint32_t *__restrict__ planes, int32_t n, int32_t n_chunks, int32_t L, int32_t K,
+    const uint32_t *__restrict__ planes, int32_t n, int32_t nc_cap, int32_t L, int32_t K,
     int32_t Kr, int32_t nbins, uint32_t *__restrict__ off, uint32_t *__restrict__ ent)
 {
     extern __shared__ uint32_t hist[];
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
     const int u = blockIdx.x / L, l = blockIdx.x % L;
     const int t = threadIdx.x;
     const int64_t cstride = int64_t(L) * Kr * kWords;
-    const uint32_t *pl = planes + int64_t(u) * n_chunks * cstride + int64_t(l) * Kr * kWords;
+    const uint32_t *pl = planes + int64_t(u) * nc_cap * cstride + int64_t(l) * Kr * kWords;
     for (int b = t; b < nbins; b += kBuildThreads) hist[b] = 0u;
     __syncthreads();
     for (int i = t; i < n; i += kBuildThreads) atomicAdd(&hist[key_code(pl, cstride, K, i)], 1u);
@@ -305,7 +305,7 @@ hipError_t launch_build_tables(const mp_index_impl &idx, hipStream_t s)
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
     build_tables_kernel<<<dim3(lay.B * lay.H_kv * lay.L), kBuildThreads, lds, s>>>(
-        idx.planes, lay.n, lay.n_chunks, lay.L, lay.K, lay.Kr, nbins, idx.tab_off, idx.tab_ent);
+        idx.planes, lay.n, lay.nc_cap, lay.L, lay.K, lay.Kr, nbins, idx.tab_off, idx.tab_ent);
     return hipGetLastError();
 }
 

@@ -122,3 +122,26 @@ def test_tables_calls_reject_a_dead_handle():
         capi.mp_build_tables(None, None, 0, None)
     with pytest.raises(capi.MPError, match="MP_E_HANDLE"):
         capi.mp_tables_views(None)
+
+
+def test_capacity_build_and_append_check_their_arguments_on_the_host():
+    """mp_build_index_cap refuses a capacity below the key count or above the
+    size limits before touching the device; mp_index_append refuses a dead
+    handle."""
+    L = capi.lib()
+    out = C.c_void_p(123)
+    v = _view()                                   # n = 1000 keys
+    need = capi.mp_index_workspace_bytes(1, 2, 4000, 128, 10, 150)
+    assert need > capi.mp_index_workspace_bytes(1, 2, 1000, 128, 10, 150)
+    for cap in (999, 0, -5):
+        st = L.mp_build_index_cap(C.byref(v), 10, 150, 0, cap, 0x100000, need, None, C.byref(out))
+        assert st == capi.MP_E_ARG, capi.mp_last_error()
+        assert out.value is None
+    assert "capacity" in capi.mp_last_error()
+    st = L.mp_build_index_cap(C.byref(v), 10, 150, 0, 4000, 0x100000, need - 1, None, C.byref(out))
+    assert st == capi.MP_E_WORKSPACE
+    fake = (C.c_uint8 * 4096)()
+    for h in (None, C.addressof(fake)):
+        assert L.mp_index_append(h, C.byref(v), None) == capi.MP_E_HANDLE
+    with pytest.raises(capi.MPError, match="MP_E_HANDLE"):
+        capi.mp_index_append(None, v, 0)

@@ -1,0 +1,178 @@
+"""GPU parity of the incremental index (mp_build_index_cap, mp_index_append),
+through the C ABI.
+
+An index is built over the first n0 keys of a key cache with room for more,
+then grown step by step to longer prefixes of the same cache.  The reading
+checked (the pages do not say how the mean moves as keys arrive): appended
+keys are centered by the mean of the n0 keys the index was built on, and
+encoded with the same hyperplanes.  After every append:
+  * mu is bit for bit the one of the build;
+  * every key's codes (old and appended) match the oracle's encoding of
+    k - mu0 outside the 1e-5 band, with mismatches under 0.01% of bits;
+  * counts and sampled sets are exact (the oracle's integer steps on the
+    GPU's codes), with T taken at the new length;
+  * outputs are within 2e-3 per row of the oracle's fp64 estimator with mu0;
+  * mp_decode_attn equals mp_decode_debug bit for bit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import lsh_sampled_sparse_amd as mp
+import oracle
+import synth
+from parity_util import OUT_TOL, check_codes, gpu_codes_table_major, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _cache(B, H_q, H_kv, n, dtype, seed):
+    seeds = [seed + 100 * b for b in range(B)]
+    inp = synth.cone_inputs(B=B, H_q=H_q, H_kv=H_kv, n=n, d=128, dtype=dtype, seeds=seeds,
+                            device=DEV)
+    return inp["k"], inp["v"], inp["q"].contiguous()
+
+
+def check_index(idx, k, v, q, n, n0, K, L, seed, n_sink, n_local, heads=None, key_rows=None):
+    B, H_kv = k.shape[:2]
+    H_q = q.shape[1]
+    G = H_q // H_kv
+    kk, vv = k[:, :, :n], v[:, :, :n]
+    res = mp.decode_debug(q, idx, kk, vv, n_sink, n_local)
+    out2 = mp.decode_attn(q, idx, kk, vv, n_sink, n_local)
+    torch.cuda.synchronize()
+    assert torch.equal(res["out"], out2), "mp_decode_attn and mp_decode_debug differ"
+    W = oracle.hyperplanes(seed, K * L, 128)
+    codes = gpu_codes_table_major(idx)
+    assert codes.shape[-1] == n
+    qcodes = res["qcodes"].cpu().numpy().view(np.uint16)
+    counts = res["counts"].cpu().numpy().astype(np.int32)
+    s_idx = res["s_idx"].cpu().numpy()
+    s_len = res["s_len"].cpu().numpy()
+    out = res["out"].cpu().double().numpy()
+    scl = 1.0 / math.sqrt(128)
+    errs, mism, bits = [], 0, 0
+    for b in range(B):
+        for h in range(H_kv):
+            kh = k[b, h, :n].cpu().double().numpy()
+            vh = v[b, h, :n].cpu().double().numpy()
+            mu0 = oracle.mean(k[b, h, :n0].cpu().double().numpy())     # frozen at build
+            rows = np.arange(n) if key_rows is None else key_rows(n)
+            m_, _, b_ = check_codes(kh[rows] - mu0, W, K, L, codes[b, h][:, rows].T, "key")
+            mism += m_
+            bits += b_
+            for g in range(G):
+                hq = h * G + g
+                if heads is not None and (b, hq) not in heads:
+                    continue
+                qh = q[b, hq].cpu().double().numpy()
+                check_codes(qh[None], W, K, L, qcodes[b, hq][None], "query")
+                cnt = oracle.collision_counts(codes[b, h], qcodes[b, hq])
+                assert np.array_equal(cnt, counts[b, hq]), f"counts differ at ({b},{hq}), n={n}"
+                S = oracle.select(cnt, n_sink, n_local)
+                assert s_len[b, hq] == len(S) and np.array_equal(S, s_idx[b, hq, :len(S)]), \
+                    f"S differs at ({b},{hq}), n={n}"
+                ref = oracle.estimate(qh, kh, vh, mu0, S, K, L, n_sink, n_local, scl)
+                e = row_rel_err(out[b, hq], ref)
+                errs.append(e)
+                assert e <= OUT_TOL, f"output error {e:.3g} at ({b},{hq}), n={n}"
+    return dict(n=n, max_out_err=max(errs) if errs else 0.0, mismatched_bits=mism, bits=bits,
+                mean_S=float(s_len.mean()))
+
+
+def run_growth(B, H_q, H_kv, dtype, K, L, n0, steps, n_sink, n_local, seed, **kw):
+    cap = max(steps + [n0])
+    k, v, q = _cache(B, H_q, H_kv, cap, dtype, seed)
+    idx = mp.build_index(k[:, :, :n0], K, L, seed, capacity=cap)
+    torch.cuda.synchronize()
+    mu_built = idx.views()[1].clone()
+    reps = [check_index(idx, k, v, q, n0, n0, K, L, seed, n_sink, n_local, **kw)]
+    for n in steps:
+        mp.append_index(idx, k[:, :, :n])
+        torch.cuda.synchronize()
+        assert idx.n == n
+        assert torch.equal(idx.views()[1], mu_built), "mu moved on append"
+        reps.append(check_index(idx, k, v, q, n, n0, K, L, seed, n_sink, n_local, **kw))
+    return reps
+
+
+def test_grow_bf16_gqa4_across_words_blocks_and_chunks():
+    # 700 -> 701 (inside a word), 1023, 1024 (block edge), 1500, 2600 (new chunks)
+    for r in run_growth(1, 8, 2, torch.bfloat16, 10, 60, 700, [701, 1023, 1024, 1500, 2600],
+                        4, 32, seed=21):
+        print("bf16 growth", r, flush=True)
+
+
+def test_grow_fp32_batch2_gqa2_with_a_no_op_step():
+    for r in run_growth(2, 4, 2, torch.float32, 8, 40, 300, [300, 513, 1100], 2, 16, seed=22):
+        print("fp32 growth", r, flush=True)
+
+
+def test_grow_from_one_key_gqa8():
+    for r in run_growth(1, 8, 1, torch.bfloat16, 6, 24, 1, [2, 255, 256, 257, 800], 1, 8,
+                        seed=23):
+        print("from one key", r, flush=True)
+
+
+def test_grow_K0_every_key_collides():
+    for r in run_growth(1, 4, 1, torch.bfloat16, 0, 8, 200, [900], 4, 16, seed=24):
+        print("K0 growth", r, flush=True)
+
+
+def test_grow_96k_one_layer_sampled():
+    """The timed workload's shape: built 300 keys short of 96K, grown in two
+    steps; keys sampled for the code check, a few heads for the outputs."""
+    cfg = synth.CONFIGS["llama8b_96k"]
+    n1 = cfg.n
+    heads = [(0, hq) for hq in range(0, cfg.H_q, 9)]
+    rng = np.random.default_rng(5)
+
+    def key_rows(n):
+        return np.unique(np.concatenate([rng.choice(n - 400, 300, replace=False),
+                                         np.arange(n - 400, n)]))
+
+    for r in run_growth(1, cfg.H_q, cfg.H_kv, cfg.dtype, cfg.K, cfg.L, n1 - 300,
+                        [n1 - 211, n1], cfg.n_sink, cfg.n_local, seed=cfg.hyperplane_seed(2),
+                        heads=heads, key_rows=key_rows):
+        print("96k growth", r, flush=True)
+
+
+def test_tables_after_append_are_rebuilt_and_agree():
+    k, v, q = _cache(1, 8, 2, 3000, torch.bfloat16, 25)
+    idx = mp.build_index(k[:, :, :1200], 9, 50, 25, capacity=3000)
+    mp.build_tables(idx)
+    mp.append_index(idx, k[:, :, :3000])
+    assert idx.tables is None
+    with pytest.raises(mp.MPError, match="MP_E_ARG"):
+        mp.decode_attn_tables(q, idx, k, v, 4, 32)
+    mp.build_tables(idx)
+    rt = mp.decode_tables_debug(q, idx, k, v, 4, 32)
+    rs = mp.decode_debug(q, idx, k, v, 4, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(rt["s_len"], rs["s_len"])
+    assert np.array_equal(rt["counts"].cpu().numpy(), np.minimum(rs["counts"].cpu().numpy(), 2))
+    err = max(row_rel_err(a, b) for a, b in zip(rt["out"].cpu().double().numpy().reshape(-1, 128),
+                                                rs["out"].cpu().double().numpy().reshape(-1, 128)))
+    assert err <= 1e-5, err
+
+
+def test_append_rejections():
+    k, v, q = _cache(1, 4, 1, 1000, torch.bfloat16, 26)
+    idx = mp.build_index(k[:, :, :600], 8, 20, 26, capacity=900)
+    with pytest.raises(mp.MPError, match="MP_E_SHAPE"):        # fewer keys than indexed
+        mp.append_index(idx, k[:, :, :599])
+    assert idx.n == 600
+    with pytest.raises(mp.MPError, match="MP_E_SHAPE"):        # beyond the capacity
+        mp.append_index(idx, k[:, :, :901])
+    with pytest.raises(mp.MPError, match="MP_E_DTYPE"):
+        mp.append_index(idx, k[:, :, :700].float())
+    with pytest.raises(mp.MPError, match="MP_E_SHAPE"):        # decode at the old length
+        mp.append_index(idx, k[:, :, :700])
+        mp.decode_attn(q, idx, k[:, :, :600], v[:, :, :600], 4, 16)
+    with pytest.raises(mp.MPError, match="MP_E_ARG"):
+        mp.build_index(k[:, :, :600], 8, 20, 26, capacity=599)

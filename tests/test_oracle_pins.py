@@ -317,6 +317,46 @@ def test_centering_is_score_invariant_and_needed():
     assert np.mean(fr) < 1e-3
 
 
+def test_frozen_mean_append_equals_full_build_when_the_mean_holds():
+    """Reading for a growing index (the pages fix the mean only for a static
+    set of keys): keys that arrive later are centered by the mean of the keys
+    the index was built on.  When the new keys come in pairs mu0 + e, mu0 - e,
+    the mean of all keys is still mu0, so the grown index must be the index a
+    full build over all keys gives: same codes, counts, sets and estimate."""
+    k, v, q = _tiny_inputs(31)
+    K, L = 5, 24
+    W = oracle.hyperplanes(seed=31, R=K * L, d=128)
+    n0 = 600
+    mu0 = oracle.mean(k[:n0])
+    rng = np.random.default_rng(31)
+    e = rng.standard_normal((150, 128)) * 0.3
+    k_new = np.concatenate([mu0 + e, mu0 - e])            # mean exactly mu0 in fp64 sums
+    k_all = np.concatenate([k[:n0], k_new])
+    v_all = np.concatenate([v[:n0], rng.standard_normal((300, 128))])
+    mu_all = oracle.mean(k_all)
+    assert np.max(np.abs(mu_all - mu0)) <= 1e-12
+    grown = np.concatenate([oracle.encode_keys(k[:n0], W, K, L, mu0)[0],
+                            oracle.encode_keys(k_new, W, K, L, mu0)[0]], axis=1)
+    full, _ = oracle.encode_keys(k_all, W, K, L, mu_all)
+    differ = grown != full
+    # codes may differ only where a projection sits in the 1e-5 band
+    for l, i in zip(*np.nonzero(differ)):
+        _, band = oracle.encode(k_all[i] - mu0, W, K, L)
+        assert band[l * K:(l + 1) * K].any()
+    assert differ.sum() <= 1
+    qc, _ = oracle.encode(q, W, K, L)
+    cg, cf = oracle.collision_counts(grown, qc), oracle.collision_counts(full, qc)
+    S = oracle.select(cg, 1, 16)
+    if not differ.any():
+        assert np.array_equal(cg, cf)
+        a = oracle.estimate(q, k_all, v_all, mu0, S, K, L, 1, 16)
+        b = oracle.estimate(q, k_all, v_all, mu_all, oracle.select(cf, 1, 16), K, L, 1, 16)
+        assert np.max(np.abs(a - b)) <= 1e-9 * np.max(np.abs(b))
+    # and a key appended again is coded exactly like its first copy
+    again = oracle.encode_keys(k[:40], W, K, L, mu0)[0]
+    assert np.array_equal(again, grown[:, :40])
+
+
 def test_mean_matches_exact_column_sums():
     rng = np.random.default_rng(2)
     k = rng.standard_normal((3000, 7)) * 5 + 1
