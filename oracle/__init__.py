@@ -28,6 +28,7 @@ _lib = None
 
 SCORE_CENTERED = 1
 CONST_LOG_U = 2
+AUGMENTED = 4
 
 _dp = C.POINTER(C.c_double)
 _fp = C.POINTER(C.c_float)
@@ -72,7 +73,14 @@ def lib():
         L.orc_estimate.restype = C.c_int
         L.orc_estimate.argtypes = [_dp, _dp, _dp, _dp, C.c_int64, C.c_int, C.c_int, C.c_int,
                                    _i32p, C.c_int64, C.c_int64, C.c_int64, C.c_double, C.c_int,
-                                   C.c_double, _dp]
+                                   C.c_double, C.c_double, _dp]
+        L.orc_aug_radius.restype = C.c_double
+        L.orc_aug_radius.argtypes = [_dp, C.c_int64, C.c_int, _dp]
+        L.orc_hyperplane_extra.restype = None
+        L.orc_hyperplane_extra.argtypes = [C.c_uint64, C.c_int64, C.c_int, _fp]
+        L.orc_encode_keys_aug.restype = C.c_int64
+        L.orc_encode_keys_aug.argtypes = [_dp, C.c_int64, C.c_int, _dp, _fp, _fp, C.c_double,
+                                          C.c_int, C.c_int, _u16p]
         _lib = L
     return _lib
 
@@ -204,7 +212,9 @@ def collision_p(a, b) -> float:
 
 # --------------------------------------------------------------- estimator
 def estimate(q, keys, values, mu, S, K, L, n_sink, n_local, scale=None, flags=0,
-             const_log_u=0.0):
+             const_log_u=0.0, aug_r=None):
+    """flags: SCORE_CENTERED, CONST_LOG_U; aug_r (the augmentation radius)
+    switches p_i to the lifted pair, see aug_radius."""
     q = _f64(q)
     k = _f64(keys)
     v = _f64(values)
@@ -219,11 +229,41 @@ def estimate(q, keys, values, mu, S, K, L, n_sink, n_local, scale=None, flags=0,
         mup = _p(mu, _dp)
     Sp = _p(S, _i32p) if S.size else None
     rc = lib().orc_estimate(_p(q, _dp), _p(k, _dp), _p(v, _dp), mup, n, d, K, L, Sp, S.size,
-                            n_sink, n_local, float(scale), flags, float(const_log_u),
-                            _p(out, _dp))
+                            n_sink, n_local, float(scale),
+                            flags | (AUGMENTED if aug_r is not None else 0), float(const_log_u),
+                            float(aug_r or 0.0), _p(out, _dp))
     if rc != 0:
         raise ValueError(f"orc_estimate failed with status {rc}")
     return out
+
+
+# ------------------------------------------------ inner-product-to-cosine augmentation
+def aug_radius(keys, mu=None) -> float:
+    """r = max_i |k_i - mu| (the norm every lifted key gets)."""
+    k = _f64(keys)
+    mup = None if mu is None else _p(_f64(mu), _dp)
+    return float(lib().orc_aug_radius(_p(k, _dp), k.shape[0], k.shape[1], mup))
+
+
+def hyperplane_extra(seed: int, R: int, d: int) -> np.ndarray:
+    """The lifted coordinate w_j of hyperplanes j < R (normal numbers R*d + j)."""
+    w = np.empty(R, dtype=np.float32)
+    lib().orc_hyperplane_extra(seed, R, d, _p(w, _fp))
+    return w
+
+
+def encode_keys_aug(keys, W, w, K, L, mu, r):
+    """Table-major codes [L][n] of the lifted keys [k - mu, sqrt(r^2 - |k - mu|^2)]
+    against the lifted hyperplanes [W_j, w_j]; band count."""
+    k = _f64(keys)
+    n, d = k.shape
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    codes = np.empty((L, n), dtype=np.uint16)
+    mup = None if mu is None else _p(_f64(mu), _dp)
+    nb = lib().orc_encode_keys_aug(_p(k, _dp), n, d, mup, _p(W, _fp), _p(w, _fp), float(r), K, L,
+                                   _p(codes, _u16p))
+    return codes, int(nb)
 
 
 # ------------------------------------------------ whole-unit convenience

@@ -157,6 +157,69 @@ int64_t orc_encode_keys(const double *keys, int64_t n, int d, const double *mu,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Inner-product-to-cosine augmentation ([P2] method details, variance        */
+/* reduction with LSH): with r the largest key norm, every key is lifted to   */
+/* [x, sqrt(r^2 - |x|^2)] (norm r) and the query to [q, 0], so the cosine of  */
+/* the lifted pair is q.x / (|q| r), monotone in q.x.  Here x = k - mu, the  */
+/* centered key (centering is applied first, as for the plain path).  The     */
+/* extra hyperplane coordinate j is normal number R*d + j of the same stream  */
+/* (R = K*L): the lifted hyperplane j is [W_j, w_j].                          */
+/* ------------------------------------------------------------------------ */
+
+/* r = max_i |k_i - mu| (mu == NULL: raw keys). */
+double orc_aug_radius(const double *keys, int64_t n, int d, const double *mu)
+{
+    double r2 = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int c = 0; c < d; ++c) {
+            double x = keys[i * d + c] - (mu ? mu[c] : 0.0);
+            s += x * x;
+        }
+        if (s > r2) r2 = s;
+    }
+    return sqrt(r2);
+}
+
+/* The extra coordinate of the R lifted hyperplanes, rounded to fp32. */
+void orc_hyperplane_extra(uint64_t seed, int64_t R, int d, float *w)
+{
+    for (int64_t j = 0; j < R; ++j) w[j] = (float)orc_gauss(seed, (uint64_t)(R * d + j));
+}
+
+/* Table-major codes of the lifted keys [k_i - mu, sqrt(r^2 - |k_i - mu|^2)]
+ * against the lifted hyperplanes [W_j, w_j]; returns the band count (the band
+ * taken on the lifted vectors). */
+int64_t orc_encode_keys_aug(const double *keys, int64_t n, int d, const double *mu,
+                            const float *W, const float *w, double r, int K, int L,
+                            uint16_t *codes)
+{
+    int64_t R = (int64_t)K * L;
+    float *Wl = (float *)malloc(sizeof(float) * (size_t)((R > 0 ? R : 1) * (d + 1)));
+    for (int64_t j = 0; j < R; ++j) {
+        for (int c = 0; c < d; ++c) Wl[j * (d + 1) + c] = W[j * d + c];
+        Wl[j * (d + 1) + d] = w[j];
+    }
+    double *x = (double *)malloc(sizeof(double) * (size_t)(d + 1));
+    uint16_t *code = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(L > 0 ? L : 1));
+    int64_t nb = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int c = 0; c < d; ++c) {
+            x[c] = keys[i * d + c] - (mu ? mu[c] : 0.0);
+            s += x[c] * x[c];
+        }
+        x[d] = r * r > s ? sqrt(r * r - s) : 0.0;
+        nb += orc_encode(x, d + 1, Wl, K, L, code, NULL);
+        for (int l = 0; l < L; ++l) codes[(int64_t)l * n + i] = code[l];
+    }
+    free(Wl);
+    free(x);
+    free(code);
+    return nb;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Sampling rule ([P2] method details; [P1] section 5): a key is sampled     */
 /* iff it shares the query's bucket in at least two of the L tables, and the */
 /* sampled set S leaves out the exact (sink + local) set T.                  */
@@ -252,6 +315,7 @@ double orc_collision_p(const double *a, const double *b, int d)
 
 #define ORC_SCORE_CENTERED 1   /* scores use q.(k - mu): centering-invariance check */
 #define ORC_CONST_LOG_U    2   /* every key of S gets log u = const_log_u            */
+#define ORC_AUGMENTED      4   /* p_i from the lifted pair [q, 0], [x_i, sqrt(r^2 - |x_i|^2)] */
 
 /* out[d] = sum_{i in S u T} e^{z_i - M} v_i / sum e^{z_i - M}, where
  * z_i = scale q.k_i - log u_i on S and scale q.k_i on T, M = max z.
@@ -261,16 +325,19 @@ double orc_collision_p(const double *a, const double *b, int d)
 int orc_estimate(const double *q, const double *keys, const double *values,
                  const double *mu, int64_t n, int d, int K, int L,
                  const int32_t *S, int64_t s_len, int64_t n_sink, int64_t n_local,
-                 double scale, int flags, double const_log_u, double *out)
+                 double scale, int flags, double const_log_u, double aug_r, double *out)
 {
     int64_t t_lo = n_sink < n ? n_sink : n;
     int64_t t_hi = n - n_local > t_lo ? n - n_local : t_lo;   /* T = [0,t_lo) u [t_hi,n) */
     int64_t m = s_len + t_lo + (n - t_hi);
     double *z = (double *)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1));
     int64_t *row = (int64_t *)malloc(sizeof(int64_t) * (size_t)(m > 0 ? m : 1));
-    double *x = (double *)malloc(sizeof(double) * (size_t)d);
+    double *x = (double *)malloc(sizeof(double) * (size_t)(d + 1));
+    double *ql = (double *)malloc(sizeof(double) * (size_t)(d + 1));
     int rc = 0;
     int64_t j = 0;
+    for (int c = 0; c < d; ++c) ql[c] = q[c];
+    ql[d] = 0.0;
 
     for (int64_t s = 0; s < s_len; ++s) {
         int64_t i = S[s];
@@ -284,6 +351,12 @@ int orc_estimate(const double *q, const double *keys, const double *values,
         double lu;
         if (flags & ORC_CONST_LOG_U) {
             lu = const_log_u;
+        } else if (flags & ORC_AUGMENTED) {
+            double s = 0.0;
+            for (int c = 0; c < d; ++c) s += x[c] * x[c];
+            x[d] = aug_r * aug_r > s ? sqrt(aug_r * aug_r - s) : 0.0;
+            lu = orc_log_u(orc_collision_p(ql, x, d + 1), K, L);
+            if (!(lu > -INFINITY)) { rc = -1; goto done; }
         } else {
             lu = orc_log_u(orc_collision_p(q, x, d), K, L);
             if (!(lu > -INFINITY)) { rc = -1; goto done; }
@@ -321,5 +394,6 @@ done:
     free(z);
     free(row);
     free(x);
+    free(ql);
     return rc;
 }

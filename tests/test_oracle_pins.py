@@ -402,3 +402,105 @@ def test_estimate_rejects_out_of_range_index():
     k, v, q = _tiny_inputs(1)
     with pytest.raises(ValueError):
         oracle.estimate(q, k, v, oracle.mean(k), np.array([5, 4000], np.int32), 4, 16, 1, 16)
+
+
+# ---- inner-product-to-cosine augmentation ([P2] method details) ----
+def test_augmentation_with_keys_on_a_sphere_changes_nothing():
+    """Keys all at distance r from their mean lift with a zero extra
+    coordinate: the lifted codes are the plain codes and the lifted cosine is
+    the plain one, so codes, sets and the estimate agree exactly."""
+    rng = np.random.default_rng(41)
+    K, L, n = 4, 16, 700
+    mu = rng.standard_normal(128) * 0.5
+    x = rng.standard_normal((n // 2, 128))
+    x *= 3.0 / np.linalg.norm(x, axis=1, keepdims=True)
+    k = mu + np.concatenate([x, -x])                   # pairs +x, -x: the mean is mu
+    mu = oracle.mean(k)
+    v = rng.standard_normal((n, 128))
+    q = rng.standard_normal(128)
+    W = oracle.hyperplanes(41, K * L, 128)
+    w = oracle.hyperplane_extra(41, K * L, 128)
+    r = oracle.aug_radius(k, mu)
+    assert r == pytest.approx(3.0, rel=1e-9)
+    plain, _ = oracle.encode_keys(k, W, K, L, mu)
+    lifted, _ = oracle.encode_keys_aug(k, W, w, K, L, mu, r)
+    # the extra coordinate is sqrt(r^2 - |x|^2) ~ 1e-7 r here; a flip needs a
+    # projection within that of zero
+    assert (plain != lifted).sum() <= 2
+    qc, _ = oracle.encode(q, W, K, L)
+    S = oracle.select(oracle.collision_counts(plain, qc), 1, 16)
+    a = oracle.estimate(q, k, v, mu, S, K, L, 1, 16)
+    b = oracle.estimate(q, k, v, mu, S, K, L, 1, 16, aug_r=r)
+    assert np.max(np.abs(a - b)) <= 1e-6 * np.max(np.abs(a))
+
+
+def test_augmented_agreement_rate_is_one_minus_lifted_angle_over_pi():
+    """Monte Carlo over 20000 one-bit tables: a key of norm r/3 agrees with the
+    query in a fraction 1 - theta/pi of them, theta the angle of the lifted
+    pair (cos = q.x / (|q| r)), not of the plain pair."""
+    rng = np.random.default_rng(42)
+    d, L = 128, 20000
+    q = rng.standard_normal(d)
+    q /= np.linalg.norm(q)
+    e = rng.standard_normal(d)
+    e -= (e @ q) * q
+    e /= np.linalg.norm(e)
+    r = 3.0
+    x_small = (0.9 * q + math.sqrt(1 - 0.81) * e) * (r / 3)    # plain cos 0.9, lifted 0.3
+    x_far = -q * r                                             # sets r; lifted = plain
+    keys = np.stack([x_small, x_far])
+    W = oracle.hyperplanes(42, L, d)
+    w = oracle.hyperplane_extra(42, L, d)
+    assert oracle.aug_radius(keys, None) == pytest.approx(r)
+    codes, _ = oracle.encode_keys_aug(keys, W, w, 1, L, None, r)
+    qc, _ = oracle.encode(q, W, 1, L)
+    agree = (codes[:, 0] == qc).mean()
+    lifted = 1 - math.acos(0.3) / math.pi
+    plain = 1 - math.acos(0.9) / math.pi
+    sigma = math.sqrt(lifted * (1 - lifted) / L)
+    assert abs(agree - lifted) < 5 * sigma, (agree, lifted, plain)
+    assert abs(agree - plain) > 20 * sigma
+    assert (codes[:, 1] == qc).mean() == pytest.approx(0.0, abs=1e-12)   # antiparallel
+
+
+def test_augmented_p_orders_keys_by_inner_product():
+    """The point of the lift: p_i grows with q.x_i whatever |x_i| is."""
+    rng = np.random.default_rng(43)
+    k = rng.standard_normal((300, 128)) * rng.uniform(0.2, 3.0, (300, 1))
+    q = rng.standard_normal(128)
+    mu = oracle.mean(k)
+    r = oracle.aug_radius(k, mu)
+    x = k - mu
+    lifted_k = np.concatenate([x, np.sqrt(np.maximum(r * r - (x * x).sum(1), 0))[:, None]], 1)
+    lifted_q = np.concatenate([q, [0.0]])
+    p = np.array([oracle.collision_p(lifted_q, lk) for lk in lifted_k])
+    order = np.argsort(x @ q)
+    assert np.all(np.diff(p[order]) >= -1e-12)
+    p_plain = np.array([oracle.collision_p(q, xi) for xi in x])
+    assert not np.all(np.diff(p_plain[order]) >= -1e-12)     # the plain cosine does not
+
+
+def test_augmented_estimate_weighs_equal_inner_products_equally():
+    """Two sampled keys with the same q.k and q.(k - mu) but different norms:
+    under the lift their u are equal, so the estimate is the plain mean of
+    their values; under the plain cosine it is not."""
+    rng = np.random.default_rng(44)
+    d = 128
+    q = rng.standard_normal(d)
+    qh = q / np.linalg.norm(q)
+    e1, e2 = rng.standard_normal(d), rng.standard_normal(d)
+    for e in (e1, e2):
+        e -= (e @ qh) * qh
+        e /= np.linalg.norm(e)
+    mu = rng.standard_normal(d) * 0.1
+    x1 = 0.8 * qh + 0.3 * e1
+    x2 = 0.8 * qh + 1.7 * e2
+    x3 = -2.5 * qh                                         # only sets the radius
+    k = mu + np.stack([x1, x2, x3])
+    v = rng.standard_normal((3, d))
+    r = oracle.aug_radius(k, mu)
+    S = np.array([0, 1], dtype=np.int32)
+    lifted = oracle.estimate(q, k, v, mu, S, 6, 30, 0, 0, aug_r=r)
+    assert np.max(np.abs(lifted - (v[0] + v[1]) / 2)) <= 1e-12
+    plain = oracle.estimate(q, k, v, mu, S, 6, 30, 0, 0)
+    assert np.max(np.abs(plain - (v[0] + v[1]) / 2)) > 1e-3
