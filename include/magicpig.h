@@ -102,6 +102,34 @@ mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t 
                          void *workspace, size_t workspace_bytes, void *stream,
                          mp_index **out);
 
+/* Build flags of mp_build_index_ex.
+ * MP_INDEX_MIPS: the inner-product-to-cosine lift of page "MagicPIG: LSH
+ *   Sampling for Efficient LLM Generation", method details (variance
+ *   reduction with LSH): with x_i = k_i - mu the centered key and
+ *   r = max_i |x_i|, each key is hashed as [x_i, sqrt(r^2 - |x_i|^2)] and the
+ *   query as [q, 0], against hyperplanes [W_j, w_j] whose extra coordinate
+ *   w_j is normal number K*L*128 + j of the hyperplane stream; p_i then uses
+ *   the lifted cosine q.x_i / (|q| r).  |x_i|^2 and r^2 are formed in fp64.
+ *   Such an index cannot grow (r would move): mp_index_append refuses it. */
+#define MP_INDEX_MIPS 1
+
+/* Workspace bytes of an index built with `flags` (mp_index_workspace_bytes
+ * is flags = 0); 0 if invalid. */
+size_t mp_index_workspace_bytes_ex(int32_t B, int32_t H_kv, int32_t n, int32_t d, int32_t K,
+                                   int32_t L, int32_t flags);
+
+/* mp_build_index_cap with build flags (MP_INDEX_*); the workspace must hold
+ * mp_index_workspace_bytes_ex(B, H_kv, n_cap, 128, K, L, flags) bytes.
+ * MP_E_ARG for unknown flags. */
+mp_status mp_build_index_ex(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t seed,
+                            int32_t n_cap, int32_t flags, void *workspace,
+                            size_t workspace_bytes, void *stream, mp_index **out);
+
+/* Device pointers to the lift of an MP_INDEX_MIPS index: w_extra [K*L] fp32
+ * (the hyperplanes' extra coordinate), r [B][H_kv] fp32 (the lift radius of
+ * each unit).  MP_E_ARG for an index built without the lift. */
+mp_status mp_index_lift_views(const mp_index *idx, const float **w_extra, const float **r);
+
 /* mp_build_index over the n keys of `keys` into an index that
  * mp_index_append can later grow to n_cap keys (n <= n_cap): the workspace
  * must hold mp_index_workspace_bytes(B, H_kv, n_cap, 128, K, L) bytes.
@@ -127,7 +155,8 @@ mp_status mp_build_index_cap(const mp_kv_view *keys, int32_t K, int32_t L, uint6
  * detached (the table calls then return MP_E_ARG until mp_build_tables runs
  * again with a workspace for the new n).
  * MP_E_HANDLE for a dead handle, MP_E_DTYPE / MP_E_SHAPE for keys that do not
- * fit, MP_E_ARG when called on another device than the index's. */
+ * fit, MP_E_ARG when called on another device than the index's or for an
+ * index built with MP_INDEX_MIPS. */
 mp_status mp_index_append(mp_index *idx, const mp_kv_view *keys, void *stream);
 
 /* Bytes of device scratch one mp_decode_attn / mp_decode_debug call needs

@@ -49,11 +49,12 @@ class MagicPIGIndex:
     W, mu and the key codes (as bit planes)."""
 
     def __init__(self, handle: int, workspace: torch.Tensor, keys_shape, K: int, L: int,
-                 seed: int, dtype, capacity: int = 0):
+                 seed: int, dtype, capacity: int = 0, mips: bool = False):
         self.handle = handle
         self.workspace = workspace
         self.B, self.H_kv, self.n, self.d = keys_shape
         self.capacity = max(capacity, self.n)
+        self.mips = mips
         self.K, self.L, self.seed, self.dtype = K, L, seed, dtype
         self.tables = None      # table workspace, once build_tables ran
 
@@ -88,6 +89,14 @@ class MagicPIGIndex:
         pt = self._slice(planes, self.B * self.H_kv * nc_cap * rows * words, torch.int32)
         return Wt, mut, pt.view(self.B, self.H_kv, nc_cap, rows, words)[:, :, :nc]
 
+    def lift_views(self):
+        """The lift of an index built with mips=True: the hyperplanes' extra
+        coordinate [K*L] and the radius r of each unit [B][H_kv] (fp32)."""
+        w, r = capi.mp_index_lift_views(self.handle)
+        R = self.K * self.L
+        return (self._slice(w, R, torch.float32),
+                self._slice(r, self.B * self.H_kv, torch.float32).view(self.B, self.H_kv))
+
     def scratch_bytes(self, H_q: int, tables: bool = False) -> int:
         if tables:
             return capi.mp_decode_tables_scratch_bytes(self.handle, H_q)
@@ -110,22 +119,27 @@ class MagicPIGIndex:
 
 
 def build_index(keys: torch.Tensor, K: int, L: int, seed: int, stream=None,
-                capacity: int | None = None) -> MagicPIGIndex:
+                capacity: int | None = None, mips: bool = False) -> MagicPIGIndex:
     """Index of `keys` [B][H_kv][n][128]; with `capacity` (>= n) it can later
-    grow to that many keys by append_index (see mp_build_index_cap)."""
+    grow to that many keys by append_index (see mp_build_index_cap); with
+    mips=True keys are lifted to a sphere before hashing (MP_INDEX_MIPS)."""
     view = kv_view(keys)
     n_cap = view.n if capacity is None else capacity
-    nbytes = capi.mp_index_workspace_bytes(view.B, view.H, n_cap, view.d, K, L)
+    flags = capi.MP_INDEX_MIPS if mips else 0
+    nbytes = capi.mp_index_workspace_bytes_ex(view.B, view.H, n_cap, view.d, K, L, flags)
     if nbytes == 0:
         raise ValueError(f"invalid index sizes B={view.B} H={view.H} n={n_cap} d={view.d} "
                          f"K={K} L={L}")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=keys.device)
-    if capacity is None:
+    if mips:
+        h = capi.mp_build_index_ex(view, K, L, seed, n_cap, flags, ws.data_ptr(), nbytes,
+                                   _stream(stream))
+    elif capacity is None:
         h = capi.mp_build_index(view, K, L, seed, ws.data_ptr(), nbytes, _stream(stream))
     else:
         h = capi.mp_build_index_cap(view, K, L, seed, n_cap, ws.data_ptr(), nbytes,
                                     _stream(stream))
-    return MagicPIGIndex(h, ws, tuple(keys.shape), K, L, seed, keys.dtype, n_cap)
+    return MagicPIGIndex(h, ws, tuple(keys.shape), K, L, seed, keys.dtype, n_cap, mips)
 
 
 def append_index(index: MagicPIGIndex, keys: torch.Tensor, stream=None) -> MagicPIGIndex:

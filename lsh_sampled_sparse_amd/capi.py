@@ -16,13 +16,15 @@ LIB_PATH = os.path.join(_HERE, "libmagicpig.so")
 MP_OK, MP_E_ARG, MP_E_SHAPE, MP_E_DTYPE, MP_E_WORKSPACE, MP_E_HIP, MP_E_HANDLE = range(7)
 MP_F32, MP_BF16 = 0, 1
 MP_CHUNK = 512
+MP_INDEX_MIPS = 1
 
 EXPORTED = [
     "mp_index_workspace_bytes", "mp_build_index", "mp_decode_scratch_bytes", "mp_decode_attn",
     "mp_decode_attn_timed", "mp_decode_debug", "mp_index_views", "mp_index_destroy", "mp_status_str", "mp_last_error",
     "mp_tables_workspace_bytes", "mp_build_tables", "mp_decode_tables_scratch_bytes",
     "mp_decode_attn_tables", "mp_decode_attn_tables_timed", "mp_decode_tables_debug",
-    "mp_tables_views", "mp_build_index_cap", "mp_index_append",
+    "mp_tables_views", "mp_build_index_cap", "mp_index_append", "mp_index_workspace_bytes_ex",
+    "mp_build_index_ex", "mp_index_lift_views",
 ]
 
 
@@ -61,6 +63,13 @@ def lib():
         L.mp_build_index_cap.restype = C.c_int
         L.mp_build_index_cap.argtypes = [C.POINTER(mp_kv_view), i32, i32, C.c_uint64, i32, vp, sz,
                                          vp, C.POINTER(vp)]
+        L.mp_index_workspace_bytes_ex.restype = sz
+        L.mp_index_workspace_bytes_ex.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.mp_build_index_ex.restype = C.c_int
+        L.mp_build_index_ex.argtypes = [C.POINTER(mp_kv_view), i32, i32, C.c_uint64, i32, i32, vp,
+                                        sz, vp, C.POINTER(vp)]
+        L.mp_index_lift_views.restype = C.c_int
+        L.mp_index_lift_views.argtypes = [vp, C.POINTER(vp), C.POINTER(vp)]
         L.mp_index_append.restype = C.c_int
         L.mp_index_append.argtypes = [vp, C.POINTER(mp_kv_view), vp]
         L.mp_decode_scratch_bytes.restype = sz
@@ -135,6 +144,26 @@ def mp_build_index_cap(keys: mp_kv_view, K: int, L: int, seed: int, n_cap: int, 
                                   workspace_bytes, stream, C.byref(out))
     _check(st, "mp_build_index_cap")
     return out.value
+
+
+def mp_index_workspace_bytes_ex(B, H_kv, n, d, K, L, flags) -> int:
+    return int(lib().mp_index_workspace_bytes_ex(B, H_kv, n, d, K, L, flags))
+
+
+def mp_build_index_ex(keys: mp_kv_view, K: int, L: int, seed: int, n_cap: int, flags: int,
+                      workspace: int, workspace_bytes: int, stream: int) -> int:
+    """mp_build_index_cap with build flags (MP_INDEX_*); returns the handle."""
+    out = C.c_void_p()
+    st = lib().mp_build_index_ex(C.byref(keys), K, L, seed & (2**64 - 1), n_cap, flags, workspace,
+                                 workspace_bytes, stream, C.byref(out))
+    _check(st, "mp_build_index_ex")
+    return out.value
+
+
+def mp_index_lift_views(idx: int):
+    w, r = C.c_void_p(), C.c_void_p()
+    _check(lib().mp_index_lift_views(idx, C.byref(w), C.byref(r)), "mp_index_lift_views")
+    return w.value, r.value
 
 
 def mp_index_append(idx: int, keys: mp_kv_view, stream: int) -> None:

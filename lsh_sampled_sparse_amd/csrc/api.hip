@@ -34,7 +34,8 @@ static void set_index_keys(IndexLayout &y, int32_t n)
     y.n_mean_blocks = ceil_div(n, kMeanRows);
 }
 
-IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t L, int32_t n_cap)
+IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t L, int32_t n_cap,
+                         int32_t flags)
 {
     if (n_cap < n) n_cap = n;
     IndexLayout y{};
@@ -58,6 +59,15 @@ IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t 
     y.off_mu = off;      off = align256(off + BH * kD * 4);
     y.off_mu_part = off; off = align256(off + BH * y.n_mean_blocks * kD * 8);
     y.off_planes = off;  off = align256(off + BH * y.nc_cap * int64_t(L) * y.Kr * kWords * 4);
+    y.flags = flags;
+    if (flags & MP_INDEX_MIPS) {
+        y.off_wx = off;      off = align256(off + int64_t(y.R_pad) * 4);
+        y.off_mu64 = off;    off = align256(off + BH * kD * 8);
+        y.off_xx = off;      off = align256(off + BH * int64_t(n_cap) * 8);
+        y.off_xmax = off;    off = align256(off + BH * y.n_mean_blocks * 8);
+        y.off_r2 = off;      off = align256(off + BH * 8);
+        y.off_rn = off;      off = align256(off + BH * 4);
+    }
     y.total = off;
     set_index_keys(y, n);
     return y;
@@ -188,6 +198,7 @@ static mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx,
     a.scale = scale > 0.0f ? scale : 1.0f / sqrtf(float(kD));
     a.W = idx->W;
     a.mu = idx->mu;
+    a.rnorm = idx->rnorm;
     a.planes = idx->planes;
     a.Kr = lay.Kr;
     a.nc_cap = lay.nc_cap;
@@ -226,15 +237,21 @@ using namespace mp;
 
 extern "C" {
 
+size_t mp_index_workspace_bytes_ex(int32_t B, int32_t H_kv, int32_t n, int32_t d, int32_t K,
+                                   int32_t L, int32_t flags)
+{
+    if (!sizes_ok(B, H_kv, n, d, K, L) || (flags & ~MP_INDEX_MIPS)) return 0;
+    return size_t(index_layout(B, H_kv, n, K, L, n, flags).total);
+}
+
 size_t mp_index_workspace_bytes(int32_t B, int32_t H_kv, int32_t n, int32_t d, int32_t K, int32_t L)
 {
-    if (!sizes_ok(B, H_kv, n, d, K, L)) return 0;
-    return size_t(index_layout(B, H_kv, n, K, L).total);
+    return mp_index_workspace_bytes_ex(B, H_kv, n, d, K, L, 0);
 }
 
 static mp_status build_index_impl(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t seed,
-                                  int32_t n_cap, void *workspace, size_t workspace_bytes,
-                                  void *stream, mp_index **out)
+                                  int32_t n_cap, int32_t flags, void *workspace,
+                                  size_t workspace_bytes, void *stream, mp_index **out)
 {
     g_err[0] = 0;
     if (!out) return fail(MP_E_ARG, "out is NULL");
@@ -245,10 +262,11 @@ static mp_status build_index_impl(const mp_kv_view *keys, int32_t K, int32_t L, 
     if (L < 2 || L > 255) return fail(MP_E_ARG, "L = %d outside [2, 255]", L);
     if (int64_t(keys->B) * keys->H > 65535)
         return fail(MP_E_SHAPE, "B*H_kv = %lld is too large", (long long)keys->B * keys->H);
+    if (flags & ~MP_INDEX_MIPS) return fail(MP_E_ARG, "unknown build flags 0x%x", flags);
     if (n_cap < keys->n) return fail(MP_E_ARG, "capacity %d is below the %d keys", n_cap, keys->n);
     if (mp_index_workspace_bytes(keys->B, keys->H, n_cap, keys->d, K, L) == 0)
         return fail(MP_E_ARG, "capacity %d is not a valid key count", n_cap);
-    const IndexLayout lay = index_layout(keys->B, keys->H, keys->n, K, L, n_cap);
+    const IndexLayout lay = index_layout(keys->B, keys->H, keys->n, K, L, n_cap, flags);
     if (!workspace) return fail(MP_E_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) & 255)
         return fail(MP_E_WORKSPACE, "workspace must be 256-byte aligned");
@@ -271,20 +289,35 @@ static mp_status build_index_impl(const mp_kv_view *keys, int32_t K, int32_t L, 
     idx->mu = reinterpret_cast<float *>(wp + lay.off_mu);
     idx->mu_part = reinterpret_cast<double *>(wp + lay.off_mu_part);
     idx->planes = reinterpret_cast<uint32_t *>(wp + lay.off_planes);
+    const bool lift = flags & MP_INDEX_MIPS;
+    if (lift) {
+        idx->wx = reinterpret_cast<float *>(wp + lay.off_wx);
+        idx->mu64 = reinterpret_cast<double *>(wp + lay.off_mu64);
+        idx->xx = reinterpret_cast<double *>(wp + lay.off_xx);
+        idx->xmax = reinterpret_cast<double *>(wp + lay.off_xmax);
+        idx->r2 = reinterpret_cast<double *>(wp + lay.off_r2);
+        idx->rnorm = reinterpret_cast<float *>(wp + lay.off_rn);
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const KVRows rows{keys->data, keys->stride_b, keys->stride_h, keys->stride_n, keys->H};
     hipError_t e = launch_wgen(seed, lay.R, lay.R_pad, idx->W, idx->Wp, s);
+    if (e == hipSuccess && lift) e = launch_wgen_extra(seed, lay.R, lay.R_pad, idx->wx, s);
     if (e == hipSuccess)
         e = launch_mean(rows, keys->dtype, lay.B, lay.H_kv, lay.n, lay.n_mean_blocks, idx->mu_part,
-                        idx->mu, s);
+                        idx->mu, idx->mu64, s);
+    if (e == hipSuccess && lift)
+        e = launch_lift_norms(rows, keys->dtype, lay.B, lay.H_kv, lay.n, lay.n_cap,
+                              lay.n_mean_blocks, idx->mu64, idx->xx, idx->xmax, idx->r2,
+                              idx->rnorm, s);
     if (e == hipSuccess) {
         const int64_t nwords = int64_t(lay.B) * lay.H_kv * lay.nc_cap * int64_t(L) * lay.Kr * kWords;
         if (K == 0)
             e = launch_fill_u32(idx->planes, nwords, s);   // every code is 0: one zero row per table
         else
             e = launch_encode_keys(rows, keys->dtype, lay.B, lay.H_kv, lay.n, lay.nc_cap, idx->mu,
-                                   idx->Wp, K, L, lay.R_pad, idx->planes, 0, s);
+                                   idx->Wp, K, L, lay.R_pad, idx->planes, 0, idx->wx, idx->xx,
+                                   idx->r2, lay.n_cap, s);
     }
     if (e != hipSuccess) {
         idx->magic = 0;
@@ -298,7 +331,7 @@ static mp_status build_index_impl(const mp_kv_view *keys, int32_t K, int32_t L, 
 mp_status mp_build_index(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t seed,
                          void *workspace, size_t workspace_bytes, void *stream, mp_index **out)
 {
-    return build_index_impl(keys, K, L, seed, keys ? keys->n : 0, workspace, workspace_bytes,
+    return build_index_impl(keys, K, L, seed, keys ? keys->n : 0, 0, workspace, workspace_bytes,
                             stream, out);
 }
 
@@ -306,16 +339,36 @@ mp_status mp_build_index_cap(const mp_kv_view *keys, int32_t K, int32_t L, uint6
                              int32_t n_cap, void *workspace, size_t workspace_bytes, void *stream,
                              mp_index **out)
 {
-    return build_index_impl(keys, K, L, seed, n_cap, workspace, workspace_bytes, stream, out);
+    return build_index_impl(keys, K, L, seed, n_cap, 0, workspace, workspace_bytes, stream, out);
+}
+
+mp_status mp_build_index_ex(const mp_kv_view *keys, int32_t K, int32_t L, uint64_t seed,
+                            int32_t n_cap, int32_t flags, void *workspace, size_t workspace_bytes,
+                            void *stream, mp_index **out)
+{
+    return build_index_impl(keys, K, L, seed, n_cap, flags, workspace, workspace_bytes, stream,
+                            out);
+}
+
+mp_status mp_index_lift_views(const mp_index *idx, const float **w_extra, const float **r)
+{
+    g_err[0] = 0;
+    if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
+    if (!(idx->lay.flags & MP_INDEX_MIPS)) return fail(MP_E_ARG, "the index has no lift");
+    if (w_extra) *w_extra = idx->wx;
+    if (r) *r = idx->rnorm;
+    return MP_OK;
 }
 
 mp_status mp_index_append(mp_index *idx, const mp_kv_view *keys, void *stream)
 {
     g_err[0] = 0;
     if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
+    IndexLayout &lay = idx->lay;
+    if (lay.flags & MP_INDEX_MIPS)
+        return fail(MP_E_ARG, "a lifted index cannot grow: its radius covers the built keys");
     mp_status st = check_view(keys, "keys");
     if (st != MP_OK) return st;
-    IndexLayout &lay = idx->lay;
     if (keys->dtype != idx->key_dtype) return fail(MP_E_DTYPE, "keys dtype differs from the index's");
     if (keys->B != lay.B || keys->H != lay.H_kv)
         return fail(MP_E_SHAPE, "keys are [%d][%d][...], the index covers [%d][%d]", keys->B,
@@ -335,7 +388,8 @@ mp_status mp_index_append(mp_index *idx, const mp_kv_view *keys, void *stream)
         const KVRows rows{keys->data, keys->stride_b, keys->stride_h, keys->stride_n, keys->H};
         const hipError_t e =
             launch_encode_keys(rows, keys->dtype, lay.B, lay.H_kv, keys->n, lay.nc_cap, idx->mu,
-                               idx->Wp, lay.K, lay.L, lay.R_pad, idx->planes, lay.n / 256, s);
+                               idx->Wp, lay.K, lay.L, lay.R_pad, idx->planes, lay.n / 256,
+                               nullptr, nullptr, nullptr, lay.n_cap, s);
         if (e != hipSuccess)
             return fail(MP_E_HIP, "append launch failed: %s", hipGetErrorString(e));
     }

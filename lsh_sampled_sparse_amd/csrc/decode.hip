@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     __shared__ uint32_t ulist[kChunk];       // key | headmask << 16 | exact << 24
     __shared__ int wsum[4];
     __shared__ __align__(16) float sq[2][G][kD];   // per staged unit: the group's queries
-    __shared__ float sqn[2][2 * G];          // their norms, then q_g.mu
+    __shared__ float sqn[2][2 * G + 1];      // their norms, q_g.mu, the lift radius
     __shared__ __align__(16) float smu[2][kD];   // mean of the unit's keys
     __shared__ GatherLds<G, T> gl;           // one gather round
 
@@ -257,6 +257,7 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
                 for (int i = t; i < G * kD; i += 256)
                     sq[slot][i / kD][i % kD] = a.q[int64_t(bhq0) * kD + i];
                 if (t < G) sqn[slot][t] = a.qnorm[bhq0 + t];
+                if (t == 0) sqn[slot][2 * G] = a.rnorm ? a.rnorm[bkv] : 0.0f;
                 if (t < kD) smu[slot][t] = a.mu[int64_t(bkv) * kD + t];
                 cur_unit = bkv;
             }

@@ -231,8 +231,9 @@ __device__ __forceinline__ void load_rows(const DecodeArgs &a, const T *kb, cons
 }
 
 // One round over list entries [base, base + ne), ne <= kRound, whose K/V
-// words are kr / vr.  sq: the G queries; sqn: their norms |q_g|, then q_g.mu;
-// smu: mu.  Three steps:
+// words are kr / vr.  sq: the G queries; sqn: their norms |q_g|, then q_g.mu,
+// then the unit's lift radius r (an index built with the lift); smu: mu.
+// Three steps:
 //   c1: 16 groups of 16 lanes, lane = 8 dims; group gi takes rows gi, gi+16,
 //       ... of the round, stages its V rows in LDS and reduces q_g.k and
 //       |k - mu|^2 over its lanes (q_g.(k - mu) is q_g.k - q_g.mu);
@@ -311,8 +312,8 @@ __device__ __forceinline__ void gather_z(const DecodeArgs &a, GatherLds<G, T> &s
             if (exact || ((ent >> (16 + g)) & 1u)) {
                 z = s.srow[e][g] * a.scale;
                 if (!exact) {
-                    // q.(k - mu) = q.k - q.mu
-                    const float den = sqn[g] * sqrtf(s.srow[e][G]);
+                    // q.(k - mu) = q.k - q.mu; a lifted key has norm r
+                    const float den = sqn[g] * (a.rnorm ? sqn[2 * G] : sqrtf(s.srow[e][G]));
                     float cs = den > 0.0f ? (s.srow[e][g] - sqn[G + g]) / den : 0.0f;
                     cs = fminf(fmaxf(cs, -1.0f), 1.0f);
                     const float pc = 1.0f - acos_over_pi(cs);

@@ -28,8 +28,18 @@ __device__ __forceinline__ uint64_t splitmix_output(uint64_t seed, uint64_t k)
     return z ^ (z >> 31);
 }
 
-// Element e of W is the cosine branch of the Box-Muller transform of the
-// uniforms made from outputs 2e+1 and 2e+2.  Also writes the MFMA B-fragment
+// Normal number e of the stream: the cosine branch of the Box-Muller
+// transform of the uniforms made from outputs 2e+1 and 2e+2.
+__device__ __forceinline__ float normal_at(uint64_t seed, int64_t e)
+{
+    const uint64_t z1 = splitmix_output(seed, 2 * uint64_t(e) + 1);
+    const uint64_t z2 = splitmix_output(seed, 2 * uint64_t(e) + 2);
+    const double u1 = (double(z1 >> 11) + 1.0) * 0x1.0p-53;
+    const double u2 = double(z2 >> 11) * 0x1.0p-53;
+    return float(sqrt(-2.0 * log(u1)) * cos(2.0 * 3.141592653589793 * u2));
+}
+
+// Element e of W is normal number e of the stream.  Also writes the MFMA B-fragment
 // copy: for column tile t (16 hyperplanes), lane = (j % 16) + 16 * (c / 32)
 // and k-step s = c % 32 live at Wp[((t*8 + s/4)*64 + lane)*4 + s%4], so one
 // float4 per lane per 4 k-steps is a contiguous 1 KB wave load.
@@ -39,17 +49,19 @@ __global__ __launch_bounds__(256) void wgen_kernel(uint64_t seed, int32_t R, int
     const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (e >= int64_t(R_pad) * kD) return;
     const int32_t j = int32_t(e / kD), c = int32_t(e % kD);
-    float g = 0.0f;
-    if (j < R) {
-        const uint64_t z1 = splitmix_output(seed, 2 * uint64_t(e) + 1);
-        const uint64_t z2 = splitmix_output(seed, 2 * uint64_t(e) + 2);
-        const double u1 = (double(z1 >> 11) + 1.0) * 0x1.0p-53;
-        const double u2 = double(z2 >> 11) * 0x1.0p-53;
-        g = float(sqrt(-2.0 * log(u1)) * cos(2.0 * 3.141592653589793 * u2));
-    }
+    const float g = j < R ? normal_at(seed, e) : 0.0f;
     W[e] = g;
     const int32_t t = j >> 4, lane = (j & 15) + 16 * (c >> 5), s = c & 31;
     Wp[((int64_t(t) * 8 + (s >> 2)) * 64 + lane) * 4 + (s & 3)] = g;
+}
+
+// The lift's extra coordinate of hyperplane j: normal number R*128 + j, the
+// numbers right after those of W.
+__global__ __launch_bounds__(256) void wgen_extra_kernel(uint64_t seed, int32_t R, int32_t R_pad,
+                                                         float *__restrict__ wx)
+{
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < R_pad) wx[j] = j < R ? normal_at(seed, int64_t(R) * kD + j) : 0.0f;
 }
 
 // ---------------------------------------------------------------- loads
@@ -112,12 +124,72 @@ __global__ __launch_bounds__(256) void mean_partial_kernel(const T *__restrict__
 
 __global__ __launch_bounds__(kD) void mean_final_kernel(const double *__restrict__ mu_part,
                                                         int32_t nmb, int32_t n,
-                                                        float *__restrict__ mu)
+                                                        float *__restrict__ mu,
+                                                        double *__restrict__ mu64)
 {
     const int bh = blockIdx.x, t = threadIdx.x;
     double s = 0.0;
     for (int c = 0; c < nmb; ++c) s += mu_part[(int64_t(bh) * nmb + c) * kD + t];
     mu[int64_t(bh) * kD + t] = float(s / double(n));
+    if (mu64) mu64[int64_t(bh) * kD + t] = s / double(n);
+}
+
+// ---------------------------------------------------------------- lift norms
+// |k_i - mu|^2 in fp64 for the kMeanRows keys of a block: a 16-lane group per
+// key (lane = 8 dims), fp64 sums over the group by shuffles; the block's max
+// goes to xmax.  The lift's extra coordinate sqrt(r^2 - |x|^2) cancels for
+// keys near the largest norm, so these sums stay in fp64 throughout.
+template <typename T>
+__global__ __launch_bounds__(256) void lift_norm_kernel(const T *__restrict__ keys, int64_t sb,
+                                                        int64_t sh, int64_t sn, int32_t H,
+                                                        int32_t n, int32_t n_cap, int32_t nmb,
+                                                        const double *__restrict__ mu64,
+                                                        double *__restrict__ xx,
+                                                        double *__restrict__ xmax)
+{
+    __shared__ double red[16];
+    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int t = threadIdx.x, gi = t >> 4, li = t & 15;
+    double m[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = mu64[int64_t(bh) * kD + 8 * li + e];
+    const T *base = keys + b * sb + h * sh + 8 * li;
+    const int64_t r0 = int64_t(blockIdx.x) * kMeanRows;
+    const int64_t r1 = r0 + kMeanRows < n ? r0 + kMeanRows : n;
+    double best = 0.0;
+    for (int64_t i = r0 + gi; i < r1; i += 16) {
+        float v[8];
+        Row8<T>::load(base + i * sn, v);
+        double s = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double x = double(v[e]) - m[e];
+            s = fma(x, x, s);
+        }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+        if (li == 0) xx[int64_t(bh) * n_cap + i] = s;
+        best = s > best ? s : best;
+    }
+    if (li == 0) red[gi] = best;
+    __syncthreads();
+    if (t == 0) {
+        double mx = 0.0;
+        for (int g = 0; g < 16; ++g) mx = red[g] > mx ? red[g] : mx;
+        xmax[int64_t(bh) * nmb + blockIdx.x] = mx;
+    }
+}
+
+__global__ __launch_bounds__(64) void lift_final_kernel(const double *__restrict__ xmax,
+                                                        int32_t nmb, double *__restrict__ r2,
+                                                        float *__restrict__ rnorm)
+{
+    const int bh = blockIdx.x;
+    if (threadIdx.x != 0) return;
+    double mx = 0.0;
+    for (int c = 0; c < nmb; ++c) mx = xmax[int64_t(bh) * nmb + c] > mx ? xmax[int64_t(bh) * nmb + c] : mx;
+    r2[bh] = mx;
+    rnorm[bh] = float(sqrt(mx));
 }
 
 // ---------------------------------------------------------------- encode
@@ -140,7 +212,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void encode_keys_kernel(
     const T *__restrict__ keys, int64_t sb, int64_t sh, int64_t sn, int32_t H, int32_t n,
     int32_t nc_cap, const float *__restrict__ mu, const float *__restrict__ Wp, int32_t K,
-    int32_t L, int32_t NT, uint32_t *__restrict__ planes, int32_t kb0)
+    int32_t L, int32_t NT, uint32_t *__restrict__ planes, int32_t kb0,
+    const float *__restrict__ wx, const double *__restrict__ xx, const double *__restrict__ r2,
+    int32_t n_cap)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     float4 *wbuf = reinterpret_cast<float4 *>(smem);                       // [2][512] float4
@@ -180,6 +254,20 @@ __global__ __launch_bounds__(256) void encode_keys_kernel(
         }
     }
 
+    // The lift (wx non-NULL): key row il of tile rt gains the coordinate
+    // sqrt(r^2 - |x|^2) (0 for padding keys), projection j the term wx[j] times it.
+    float lifted[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (wx) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int64_t row = k0 + 16 * rt + il;
+            if (row < n) {
+                const double d2 = r2[bh] - xx[int64_t(bh) * n_cap + row];
+                lifted[rt] = float(d2 > 0.0 ? sqrt(d2) : 0.0);
+            }
+        }
+    }
+
     const float4 *wp4 = reinterpret_cast<const float4 *>(Wp);
     float4 pre0 = wp4[t], pre1 = wp4[256 + t];
     wbuf[t] = pre0;
@@ -199,12 +287,21 @@ __global__ __launch_bounds__(256) void encode_keys_kernel(
             const float4 v = cur[q * 64 + lane];
             bf[4 * q] = v.x; bf[4 * q + 1] = v.y; bf[4 * q + 2] = v.z; bf[4 * q + 3] = v.w;
         }
+        // lane l's results are hyperplanes 16 ct + 4 g + r
+        const float4 wl = wx ? reinterpret_cast<const float4 *>(wx)[4 * ct + g]
+                             : float4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < 32; ++s)
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[s], a[rt][s], acc, 0, 0, 0);
+            if (wx) {
+                acc[0] = fmaf(wl.x, lifted[rt], acc[0]);
+                acc[1] = fmaf(wl.y, lifted[rt], acc[1]);
+                acc[2] = fmaf(wl.z, lifted[rt], acc[2]);
+                acc[3] = fmaf(wl.w, lifted[rt], acc[3]);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const unsigned long long m = __ballot(acc[r] > 0.0f);
@@ -248,7 +345,7 @@ hipError_t launch_wgen(uint64_t seed, int32_t R, int32_t R_pad, float *W, float 
 }
 
 hipError_t launch_mean(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
-                       int32_t nmb, double *mu_part, float *mu, hipStream_t s)
+                       int32_t nmb, double *mu_part, float *mu, double *mu64, hipStream_t s)
 {
     const dim3 grid(nmb, B * H);
     if (dtype == MP_BF16)
@@ -260,13 +357,39 @@ hipError_t launch_mean(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, 
                                                         mu_part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    mean_final_kernel<<<dim3(B * H), dim3(kD), 0, s>>>(mu_part, nmb, n, mu);
+    mean_final_kernel<<<dim3(B * H), dim3(kD), 0, s>>>(mu_part, nmb, n, mu, mu64);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgen_extra(uint64_t seed, int32_t R, int32_t R_pad, float *wx, hipStream_t s)
+{
+    wgen_extra_kernel<<<dim3(ceil_div(R_pad, 256)), dim3(256), 0, s>>>(seed, R, R_pad, wx);
+    return hipGetLastError();
+}
+
+hipError_t launch_lift_norms(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
+                             int32_t n_cap, int32_t nmb, const double *mu64, double *xx,
+                             double *xmax, double *r2, float *rnorm, hipStream_t s)
+{
+    const dim3 grid(nmb, B * H);
+    if (dtype == MP_BF16)
+        lift_norm_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(keys.data),
+                                                        keys.sb, keys.sh, keys.sn, H, n, n_cap,
+                                                        nmb, mu64, xx, xmax);
+    else
+        lift_norm_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(keys.data), keys.sb,
+                                                     keys.sh, keys.sn, H, n, n_cap, nmb, mu64, xx,
+                                                     xmax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    lift_final_kernel<<<dim3(B * H), dim3(64), 0, s>>>(xmax, nmb, r2, rnorm);
     return hipGetLastError();
 }
 
 hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
                               int32_t nc_cap, const float *mu, const float *Wp, int32_t K,
                               int32_t L, int32_t R_pad, uint32_t *planes, int32_t kb0,
+                              const float *wx, const double *xx, const double *r2, int32_t n_cap,
                               hipStream_t s)
 {
     const int32_t NT = R_pad / 16;
@@ -283,14 +406,16 @@ hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int3
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
         if (e != hipSuccess) return e;
         fn<<<grid, 256, shmem, s>>>(static_cast<const uint16_t *>(keys.data), keys.sb, keys.sh,
-                                    keys.sn, H, n, nc_cap, mu, Wp, K, L, NT, planes, kb0);
+                                    keys.sn, H, n, nc_cap, mu, Wp, K, L, NT, planes, kb0, wx, xx, r2,
+                                    n_cap);
     } else {
         auto fn = encode_keys_kernel<float>;
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
         if (e != hipSuccess) return e;
         fn<<<grid, 256, shmem, s>>>(static_cast<const float *>(keys.data), keys.sb, keys.sh,
-                                    keys.sn, H, n, nc_cap, mu, Wp, K, L, NT, planes, kb0);
+                                    keys.sn, H, n, nc_cap, mu, Wp, K, L, NT, planes, kb0, wx, xx, r2,
+                                    n_cap);
     }
     return hipGetLastError();
 }

@@ -22,12 +22,15 @@ struct IndexLayout {
     int32_t B, H_kv, n, n_pad, n_chunks, n_mean_blocks, K, L, R, R_pad;
     int32_t Kr;        // plane rows per table: K, or 1 (all zero) when K = 0
     int32_t n_cap, nc_cap;   // keys the index may grow to; plane chunks per unit
+    int32_t flags;           // MP_INDEX_* of the build
     int64_t off_W, off_Wp, off_mu, off_mu_part, off_planes, total;
+    // inner-product-to-cosine lift (MP_INDEX_MIPS only; 0 otherwise)
+    int64_t off_wx, off_mu64, off_xx, off_xmax, off_r2, off_rn;
 };
 // Layout of an index over n keys with room for n_cap >= n (regions sized for
 // n_cap; the n-dependent counts describe the n keys).
 IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t L,
-                         int32_t n_cap = 0);
+                         int32_t n_cap = 0, int32_t flags = 0);
 
 struct mp_index_impl {
     uint64_t magic;
@@ -41,6 +44,13 @@ struct mp_index_impl {
     double *mu_part; // [B*H_kv][n_mean_blocks][128]
     uint32_t *planes; // [B*H_kv][n_chunks][L*Kr][kWords]: bit j of word w of row
                       // l*Kr + b is bit b of the code of key 32w + j in table l
+    // inner-product-to-cosine lift (NULL unless built with MP_INDEX_MIPS)
+    float *wx;       // [R_pad] lifted coordinate of each hyperplane
+    double *mu64;    // [B*H_kv][128] mean in fp64
+    double *xx;      // [B*H_kv][n_cap] |k_i - mu|^2 in fp64
+    double *xmax;    // [B*H_kv][n_mean_blocks] per-block max of xx
+    double *r2;      // [B*H_kv] r^2 = max_i xx_i
+    float *rnorm;    // [B*H_kv] r
     // bucketed tables, once built (NULL until then)
     uint32_t *tab_off; // [B*H_kv][L][2^K + 1] bucket starts
     uint32_t *tab_ent; // [B*H_kv][L][n] keys, grouped by bucket
@@ -72,14 +82,23 @@ struct KVRows {
 // ---- launchers (return hipSuccess or the launch error) ----
 hipError_t launch_wgen(uint64_t seed, int32_t R, int32_t R_pad, float *W, float *Wp, hipStream_t s);
 hipError_t launch_mean(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
-                       int32_t n_mean_blocks, double *mu_part, float *mu, hipStream_t s);
+                       int32_t n_mean_blocks, double *mu_part, float *mu, double *mu64,
+                       hipStream_t s);
 // Encodes keys [256 kb0, n) (whole 256-key blocks; keys >= n are zero rows)
-// into planes whose units are nc_cap chunks apart.
+// into planes whose units are nc_cap chunks apart.  With wx non-NULL the
+// keys are lifted: projection j gains wx[j] sqrt(r2 - xx_i).
 hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
                               int32_t nc_cap, const float *mu, const float *Wp, int32_t K,
                               int32_t L, int32_t R_pad, uint32_t *planes, int32_t kb0,
+                              const float *wx, const double *xx, const double *r2, int32_t n_cap,
                               hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int64_t count, hipStream_t s);
+// The lift: wx from the hyperplane stream; xx, r^2 and r of every unit (mu64
+// must hold the fp64 mean).
+hipError_t launch_wgen_extra(uint64_t seed, int32_t R, int32_t R_pad, float *wx, hipStream_t s);
+hipError_t launch_lift_norms(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
+                             int32_t n_cap, int32_t nmb, const double *mu64, double *xx,
+                             double *xmax, double *r2, float *rnorm, hipStream_t s);
 
 struct DecodeArgs {
     const float *q;          // [BHq][128]
@@ -89,6 +108,7 @@ struct DecodeArgs {
     float scale;
     const float *W;          // [R][128]
     const float *mu;         // [B*H_kv][128]
+    const float *rnorm;      // [B*H_kv] lift radius r (lifted index) or NULL
     const uint32_t *planes;  // index code planes
     const uint32_t *tab_off; // bucketed tables (table path only)
     const uint32_t *tab_ent;

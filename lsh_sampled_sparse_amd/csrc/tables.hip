@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int3
     __shared__ uint32_t ulist[kChunk];
     __shared__ int wsum[4];
     __shared__ __align__(16) float sq[G][kD];
-    __shared__ float sqn[2 * G];   // |q_g|, then q_g.mu
+    __shared__ float sqn[2 * G + 1];   // |q_g|, q_g.mu, the lift radius
     __shared__ __align__(16) float smu[kD];
     __shared__ GatherLds<G, T> gl;
     const int gc = blockIdx.x;
@@ -202,6 +202,7 @@ __global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int3
     const int t = threadIdx.x, gi = t >> 4, li = t & 15;
     for (int i = t; i < G * kD; i += 256) sq[i / kD][i % kD] = a.q[int64_t(bhq0) * kD + i];
     if (t < G) sqn[t] = a.qnorm[bhq0 + t];
+    if (t == 0) sqn[2 * G] = a.rnorm ? a.rnorm[bkv] : 0.0f;
     if (t < kD) smu[t] = a.mu[int64_t(bkv) * kD + t];
 
     // Thread t owns keys 2t and 2t+1: one 4-bit field of a bitmap word.

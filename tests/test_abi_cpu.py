@@ -145,3 +145,24 @@ def test_capacity_build_and_append_check_their_arguments_on_the_host():
         assert L.mp_index_append(h, C.byref(v), None) == capi.MP_E_HANDLE
     with pytest.raises(capi.MPError, match="MP_E_HANDLE"):
         capi.mp_index_append(None, v, 0)
+
+
+def test_lift_build_checks_flags_and_sizes_on_the_host():
+    f = capi.mp_index_workspace_bytes_ex
+    plain = f(1, 8, 98304, 128, 10, 150, 0)
+    lifted = f(1, 8, 98304, 128, 10, 150, capi.MP_INDEX_MIPS)
+    assert plain == capi.mp_index_workspace_bytes(1, 8, 98304, 128, 10, 150)
+    # the lift adds the fp64 key norms (8 B per key) and small per-unit arrays
+    assert 8 * 98304 * 8 <= lifted - plain < 8 * 98304 * 8 + (1 << 20)
+    assert f(1, 8, 98304, 128, 10, 150, 2) == 0                  # unknown flag
+    L = capi.lib()
+    out = C.c_void_p(123)
+    v = _view()
+    need = f(1, 2, 1000, 128, 10, 150, capi.MP_INDEX_MIPS)
+    st = L.mp_build_index_ex(C.byref(v), 10, 150, 0, 1000, 6, 0x100000, need, None, C.byref(out))
+    assert st == capi.MP_E_ARG and "flags" in capi.mp_last_error()
+    st = L.mp_build_index_ex(C.byref(v), 10, 150, 0, 1000, capi.MP_INDEX_MIPS, 0x100000, need - 1,
+                             None, C.byref(out))
+    assert st == capi.MP_E_WORKSPACE
+    with pytest.raises(capi.MPError, match="MP_E_HANDLE"):
+        capi.mp_index_lift_views(None)
