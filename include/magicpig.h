@@ -207,7 +207,10 @@ mp_status mp_decode_attn_timed(const float *q, int32_t H_q, const mp_index *idx,
  * at least two buckets are sampled; page "MagicPIG: don't pick the tallest",
  * section 6: one 32-bit token index per key and table).  They give the same
  * sampled sets and outputs as mp_decode_attn, reading the query's L buckets
- * instead of every key's codes.  Supported for K <= 12 and n <= 622,592. ---- */
+ * instead of every key's codes.  Supported for K <= 12 and
+ * ceil(n/512)*128 + 4*(2L + 1) <= 162,816 bytes (a head's 2-bit-per-key
+ * collision bitmap and its bucket bounds in one workgroup's LDS), which holds
+ * for every L up to n = 643,072. ---- */
 
 /* Bytes of the table workspace of an index (256-byte aligned):
  *   offsets [B*H_kv][L][2^K + 1] uint32: bucket b of table l of unit u holds

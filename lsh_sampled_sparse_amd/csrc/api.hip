@@ -101,7 +101,8 @@ constexpr size_t kLdsLimit = 160 * 1024 - 1024;     // per workgroup, less the s
 static const char *tables_unsupported(const IndexLayout &lay)
 {
     if (lay.K > kMaxTableK) return "tables need K <= 12 (2^K bucket counters in LDS)";
-    if (collide_lds_bytes(lay) > kLdsLimit) return "tables need n <= 622,592 (2 bits per key in LDS)";
+    if (collide_lds_bytes(lay) > kLdsLimit)
+        return "tables need ceil(n/512)*128 + 4*(2L+1) <= 162,816 (2 bits per key in LDS)";
     return nullptr;
 }
 

@@ -189,3 +189,22 @@ def test_rejections():
             idx2.scratch_bytes(4, tables=True), dtype=torch.uint8, device=DEV))
     with pytest.raises(mp.MPError, match="MP_E_WORKSPACE"):
         mp.capi.mp_build_tables(idx2.handle, small.data_ptr(), small.numel(), 0)
+
+
+def test_largest_n_the_tables_take_at_L255():
+    """The collision bitmap of a head (2 bits per key) must fit in a
+    workgroup's LDS beside 2L + 1 bucket words: at L = 255 that allows
+    n_pad / 4 + 2044 <= 162,816 bytes, i.e. 1256 chunks (643,072 keys).  The
+    largest such n decodes exactly like the code scan; one key more is
+    refused."""
+    n = 1256 * 512
+    k, v, q = _inputs(1, 4, 1, n, torch.bfloat16, seed=71)
+    r = run_tables_case(k, v, q, 10, 255, seed=71, n_sink=4, n_local=64,
+                        heads=[(0, 0), (0, 3)], table_rows=[0, 254])
+    print("n = 643,072 at L = 255:", r, flush=True)
+    del k, v, q
+    k, v, q = _inputs(1, 4, 1, n + 1, torch.bfloat16, seed=72)
+    idx = mp.build_index(k, 10, 255, 72)
+    assert mp.capi.mp_tables_workspace_bytes(idx.handle) == 0
+    with pytest.raises(ValueError):
+        mp.build_tables(idx)
