@@ -70,10 +70,12 @@ __device__ __forceinline__ uint32_t and_xnor(uint32_t acc, uint32_t p, uint32_t 
 }
 
 // ---------------------------------------------------------------- query codes
-// Block: TB = 64/K whole tables (<= 64 hyperplanes) x 4 query heads.  Lane =
-// hyperplane, wave = query head: the lane keeps its W row in registers and
-// reads the head's query from LDS (a broadcast).  Sign bits meet in LDS and
-// are packed per (head, table).
+// Block: TB = 64/K whole tables (<= 64 hyperplanes) x kQueryHeads query
+// heads.  Thread = (hyperplane, quarter of the dims): four lanes read one W
+// row together (coalesced) and keep their 32 dims in registers for all the
+// block's heads, whose queries are LDS broadcasts; two shuffles add the
+// quarters.  Sign bits meet in LDS and are packed per (head, table).
+constexpr int kQueryHeads = 8;
 __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restrict__ q,
                                                            int32_t BHq,
                                                            const float *__restrict__ W, int32_t K,
@@ -82,43 +84,53 @@ __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restri
                                                            uint32_t *__restrict__ qq,
                                                            float *__restrict__ qnorm)
 {
-    __shared__ float4 sQ[4][kD / 4];
-    __shared__ uint8_t sbit[4][64];
-    const int t = threadIdx.x;
+    __shared__ float4 sQ[kQueryHeads][kD / 4];
+    __shared__ uint8_t sbit[kQueryHeads][64];
+    const int t = threadIdx.x, hp = t >> 2, dq = t & 3;
     const int TB = K > 0 ? 64 / K : 64;
     const int l0 = blockIdx.x * TB;
     const int nt = min(TB, L - l0);
     const int nh = nt * K;
-    const int q0 = blockIdx.y * 4;
-    const int nq = min(4, BHq - q0);
+    const int q0 = blockIdx.y * kQueryHeads;
+    const int nq = min(kQueryHeads, BHq - q0);
     const float4 *q4 = reinterpret_cast<const float4 *>(q + int64_t(q0) * kD);
     if (t < nq * (kD / 4)) sQ[t / (kD / 4)][t % (kD / 4)] = q4[t];
-    const int hp = t & 63, qi = uniform(t >> 6);
-    float4 wr[kD / 4];
+    float4 wr[8];
     if (hp < nh) {
-        const float4 *w4 = reinterpret_cast<const float4 *>(W + (int64_t(l0) * K + hp) * kD);
+        const float4 *w4 = reinterpret_cast<const float4 *>(W + (int64_t(l0) * K + hp) * kD) + 8 * dq;
 #pragma unroll
-        for (int c = 0; c < kD / 4; ++c) wr[c] = w4[c];
+        for (int c = 0; c < 8; ++c) wr[c] = w4[c];
     }
     __syncthreads();
-    if (blockIdx.x == 0 && qi < nq) {       // |q| of this wave's head, for the cosines
-        const float4 v = sQ[qi][hp & 31];
-        float s2 = hp < 32 ? v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w : 0.0f;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) s2 += __shfl_xor(s2, off);
-        if (hp == 0) qnorm[q0 + qi] = sqrtf(s2);
-    }
-    if (hp < nh && qi < nq) {
-        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;   // four chains, dims c mod 4
-#pragma unroll
-        for (int c = 0; c < kD / 4; ++c) {
-            const float4 qv = sQ[qi][c];
-            a0 = fmaf(wr[c].x, qv.x, a0);
-            a1 = fmaf(wr[c].y, qv.y, a1);
-            a2 = fmaf(wr[c].z, qv.z, a2);
-            a3 = fmaf(wr[c].w, qv.w, a3);
+    if (blockIdx.x == 0) {         // |q| of the block's heads, for the cosines
+        const int j = t >> 5, c4 = t & 31;
+        float s2 = 0.0f;
+        if (j < nq) {
+            const float4 v = sQ[j][c4];
+            s2 = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
         }
-        sbit[qi][hp] = ((a0 + a1) + (a2 + a3)) > 0.0f ? 1 : 0;
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) s2 += __shfl_xor(s2, off, 32);
+        if (j < nq && c4 == 0) qnorm[q0 + j] = sqrtf(s2);
+    }
+    for (int j = 0; j < nq; ++j) {
+        float a0 = 0.0f, a1 = 0.0f;   // two chains over the quarter's 32 dims
+#pragma unroll
+        for (int c = 0; c < 8; c += 2) {
+            const float4 qa = sQ[j][8 * dq + c], qb = sQ[j][8 * dq + c + 1];
+            a0 = fmaf(wr[c].x, qa.x, a0);
+            a0 = fmaf(wr[c].y, qa.y, a0);
+            a0 = fmaf(wr[c].z, qa.z, a0);
+            a0 = fmaf(wr[c].w, qa.w, a0);
+            a1 = fmaf(wr[c + 1].x, qb.x, a1);
+            a1 = fmaf(wr[c + 1].y, qb.y, a1);
+            a1 = fmaf(wr[c + 1].z, qb.z, a1);
+            a1 = fmaf(wr[c + 1].w, qb.w, a1);
+        }
+        float sdot = a0 + a1;
+        sdot += __shfl_xor(sdot, 1, 4);
+        sdot += __shfl_xor(sdot, 2, 4);
+        if (dq == 0 && hp < nh) sbit[j][hp] = sdot > 0.0f ? 1 : 0;
     }
     __syncthreads();
     if (t < nq * nt) {
@@ -547,7 +559,7 @@ hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s)
 {
     const int BHq = a.B * a.H_q;
     const int TB = a.K > 0 ? 64 / a.K : 64;
-    encode_query_kernel<<<dim3(ceil_div(a.L, TB), ceil_div(BHq, 4)), 256, 0, s>>>(
+    encode_query_kernel<<<dim3(ceil_div(a.L, TB), ceil_div(BHq, kQueryHeads)), 256, 0, s>>>(
         a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
     return hipGetLastError();
 }
