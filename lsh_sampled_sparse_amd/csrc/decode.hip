@@ -427,8 +427,10 @@ __global__ __launch_bounds__(256) void counts_kernel(DecodeArgs a)
 // ---------------------------------------------------------------- merge
 // Block = one (KV head unit, query head g of its group, quarter of the dims);
 // thread = (dim c of 32, chunk lane j of 32).  Lane j folds chunks j, j+32,
-// ... into a running (max, sum, acc) in one pass; the 32 lanes are then
-// combined in lane order, so the result is deterministic.
+// ... into a running (max, sum, acc) in one pass, loading kMergeBatch chunks
+// before folding them so their loads overlap; the 32 lanes are then combined
+// in lane order, so the result is deterministic.
+constexpr int kMergeBatch = 8;
 template <int G>
 __global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ part,
                                                     int32_t n_chunks, int32_t H_kv, int32_t H_q,
@@ -440,19 +442,30 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ p
     const int c = 32 * blockIdx.y + cl;
     const float *p = part + int64_t(bkv) * n_chunks * (G * kPart) + g * kPart;
     float m = -INFINITY, l = 0.0f, acc = 0.0f;
-#pragma unroll 2
-    for (int ch = j; ch < n_chunks; ch += 32) {
-        const float *pc = p + int64_t(ch) * (G * kPart);
-        const float mc = pc[0], lc = pc[1], ac = pc[2 + c];
-        if (mc > m) {
-            const float f = __expf(m - mc);      // 0 while m = -inf
-            l = fmaf(l, f, lc);
-            acc = fmaf(acc, f, ac);
-            m = mc;
-        } else if (mc != -INFINITY) {
-            const float f = __expf(mc - m);
-            l = fmaf(lc, f, l);
-            acc = fmaf(ac, f, acc);
+    for (int base = j; base < n_chunks; base += 32 * kMergeBatch) {
+        float mb[kMergeBatch], lb[kMergeBatch], ab[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const int ch = base + 32 * u;
+            const float *pc = p + int64_t(min(ch, n_chunks - 1)) * (G * kPart);
+            mb[u] = pc[0];
+            lb[u] = pc[1];
+            ab[u] = pc[2 + c];
+            if (ch >= n_chunks) mb[u] = -INFINITY;   // past the last chunk: nothing
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const float mc = mb[u], lc = lb[u], ac = ab[u];
+            if (mc > m) {
+                const float f = __expf(m - mc);      // 0 while m = -inf
+                l = fmaf(l, f, lc);
+                acc = fmaf(acc, f, ac);
+                m = mc;
+            } else if (mc != -INFINITY) {
+                const float f = __expf(mc - m);
+                l = fmaf(lc, f, l);
+                acc = fmaf(ac, f, acc);
+            }
         }
     }
     sm[j][cl] = m;
