@@ -259,6 +259,64 @@ def tables_leg(args, cfg, state, layers, sh):
     }
 
 
+def stream_read_peak(device) -> dict:
+    """A streaming-read reference on this GPU: mp_stream_read (grid-stride
+    16-byte loads, four in flight per thread) over 4 GiB, the best over a few
+    grid sizes and repetitions."""
+    import torch
+    from lsh_sampled_sparse_amd import capi
+    nbytes = 4 << 30
+    x = torch.ones(nbytes // 4, dtype=torch.int32, device=device)
+    sink = torch.zeros(4, dtype=torch.int32, device=device)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    best, best_blocks = 0.0, 0
+    for blocks in (2048, 4096, 8192, 16384):
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            capi.mp_stream_read(x.data_ptr(), nbytes, sink.data_ptr(), blocks, sh)
+            e1.record()
+            torch.cuda.synchronize()
+            gbps = nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
+            if gbps > best:
+                best, best_blocks = gbps, blocks
+    del x
+    torch.cuda.empty_cache()
+    return {"gbps": round(best, 1),
+            "kernel": f"mp_stream_read over 4 GiB, {best_blocks} workgroups of 256, best of 12"}
+
+
+def estimator_error_256k(device) -> dict:
+    """Mean over the 64 query heads of |o_hat - o| / |o| against exact
+    attention (plain PyTorch fp32) on the 256K workload (B=1, 64/8 heads,
+    K=9) at L = 60, 120, 240, with the mean sampled-set size per head."""
+    import torch
+    import lsh_sampled_sparse_amd as mp
+    import synth
+    cfg = synth.CONFIGS["llama70b_256k"]
+    inp = synth.config_inputs(cfg, device=device)
+    k, v, q = inp["k"], inp["v"], inp["q"].contiguous()
+    del inp
+    G = cfg.H_q // cfg.H_kv
+    ref = torch.empty(cfg.H_q, cfg.d, device=device)
+    for h in range(cfg.H_kv):
+        kf, vf = k[0, h].float(), v[0, h].float()
+        for g in range(G):
+            w = torch.softmax(kf @ q[0, h * G + g] / math.sqrt(cfg.d), dim=0)
+            ref[h * G + g] = w @ vf
+    res = {}
+    for L in cfg.l_sweep:
+        idx = mp.build_index(k, cfg.K, L, cfg.hyperplane_seed(0))
+        r = mp.decode_debug(q, idx, k, v, cfg.n_sink, cfg.n_local)
+        torch.cuda.synchronize()
+        e = ((r["out"][0] - ref).norm(dim=-1) / ref.norm(dim=-1)).mean().item()
+        res[f"L{L}"] = {"rel_err": round(e, 4), "mean_S": round(float(r["s_len"].float().mean()), 1)}
+        del idx, r
+    del k, v, q
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +327,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tables", action="store_true",
                     help="skip the bucketed-table leg")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the streaming-read reference and the 256K estimator-error sweep")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--source-hashes", action="store_true",
                     help="print the source hash of each timed kernel and exit")
@@ -369,6 +429,14 @@ def main():
         k, v, q = state[0][0], state[0][1], state[0][2]
         cpu = cpu_baseline(cfg, k, v, q, cfg.hyperplane_seed(0), args.cpu_threads)
 
+    # references outside the timed work, after the layers are freed
+    stream_peak = err256 = None
+    if not args.no_extras:
+        del state, k, v, q
+        torch.cuda.empty_cache()
+        stream_peak = stream_read_peak(dev)
+        err256 = estimator_error_256k(dev)
+
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -404,6 +472,10 @@ def main():
                         "frac_fp32_mfma_peak": round(flops_build / (build_avg / 1e3) / 1e12
                                                      / FP32_MFMA_PEAK_TFLOPS, 4)},
         "tables": tables,
+        "stream_read_peak": stream_peak,
+        "pct_stream_read_peak": (round(100.0 * scan_gbs / stream_peak["gbps"], 1)
+                                 if stream_peak else None),
+        "estimator_error_256k": err256,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -275,6 +275,14 @@ mp_status mp_tables_views(const mp_index *idx, const uint32_t **offsets, const u
 mp_status mp_index_views(const mp_index *idx, const float **W, const float **mu,
                          const uint32_t **planes, int32_t *n_pad);
 
+/* ---- Measurement aid (no part of the decode path) ----
+ * A plain streaming read of `bytes` (16-byte aligned device memory) by
+ * `blocks` workgroups of 256 threads: the HBM read rate of this device, the
+ * reference the benchmark reports beside its kernels' rates.  `sink` is a
+ * device word that is practically never written.  MP_E_ARG on bad arguments. */
+mp_status mp_stream_read(const void *data, int64_t bytes, uint32_t *sink, int32_t blocks,
+                         void *stream);
+
 /* Free the host handle (not the workspace).  NULL is ignored. */
 void mp_index_destroy(mp_index *idx);
 

@@ -24,7 +24,7 @@ EXPORTED = [
     "mp_tables_workspace_bytes", "mp_build_tables", "mp_decode_tables_scratch_bytes",
     "mp_decode_attn_tables", "mp_decode_attn_tables_timed", "mp_decode_tables_debug",
     "mp_tables_views", "mp_build_index_cap", "mp_index_append", "mp_index_workspace_bytes_ex",
-    "mp_build_index_ex", "mp_index_lift_views",
+    "mp_build_index_ex", "mp_index_lift_views", "mp_stream_read",
 ]
 
 
@@ -70,6 +70,8 @@ def lib():
                                         sz, vp, C.POINTER(vp)]
         L.mp_index_lift_views.restype = C.c_int
         L.mp_index_lift_views.argtypes = [vp, C.POINTER(vp), C.POINTER(vp)]
+        L.mp_stream_read.restype = C.c_int
+        L.mp_stream_read.argtypes = [vp, C.c_int64, vp, i32, vp]
         L.mp_index_append.restype = C.c_int
         L.mp_index_append.argtypes = [vp, C.POINTER(mp_kv_view), vp]
         L.mp_decode_scratch_bytes.restype = sz
@@ -164,6 +166,10 @@ def mp_index_lift_views(idx: int):
     w, r = C.c_void_p(), C.c_void_p()
     _check(lib().mp_index_lift_views(idx, C.byref(w), C.byref(r)), "mp_index_lift_views")
     return w.value, r.value
+
+
+def mp_stream_read(data: int, nbytes: int, sink: int, blocks: int, stream: int) -> None:
+    _check(lib().mp_stream_read(data, nbytes, sink, blocks, stream), "mp_stream_read")
 
 
 def mp_index_append(idx: int, keys: mp_kv_view, stream: int) -> None:

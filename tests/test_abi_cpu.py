@@ -166,3 +166,12 @@ def test_lift_build_checks_flags_and_sizes_on_the_host():
     assert st == capi.MP_E_WORKSPACE
     with pytest.raises(capi.MPError, match="MP_E_HANDLE"):
         capi.mp_index_lift_views(None)
+
+
+def test_stream_read_probe_checks_arguments_on_the_host():
+    L = capi.lib()
+    assert L.mp_stream_read(None, 1 << 20, 0x2000, 1024, None) == capi.MP_E_ARG
+    assert L.mp_stream_read(0x1000, 8, 0x2000, 1024, None) == capi.MP_E_ARG
+    assert L.mp_stream_read(0x1004, 1 << 20, 0x2000, 1024, None) == capi.MP_E_ARG
+    assert L.mp_stream_read(0x1000, 1 << 20, None, 1024, None) == capi.MP_E_ARG
+    assert L.mp_stream_read(0x1000, 1 << 20, 0x2000, 0, None) == capi.MP_E_ARG
