@@ -245,108 +245,91 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     int cur_unit = -1, slot = 1;
 
 #pragma unroll 1
-    for (int it = 0; it <= nrun; ++it) {
+    for (int it = 0; it < nrun; ++it) {
         // Per-thread offsets are recomputed each chunk from an opaque copy
         // of the thread index: hoisted out of the loop they would hold
         // registers through it.
         int t = threadIdx.x;
         asm volatile("" : "+v"(t));
         const int gi = t >> 4, li = t & 15;
-        const bool scan = it < nrun;
         const int gc = gc_begin + it;
-        const int bkv = scan ? gc / a.n_chunks : 0;
-        const int chunk = scan ? gc - bkv * a.n_chunks : 0;
+        const int bkv = gc / a.n_chunks;
+        const int chunk = gc - bkv * a.n_chunks;
         const int bhq0 = (bkv / a.H_kv) * a.H_q + (bkv % a.H_kv) * G;
-        if (scan) {
-            const bool staged = bkv != cur_unit;
-            if (staged) {
-                // A new (sequence, KV head) unit: its query codes for the scan
-                // ([table][head]) and, in the other slot, the queries, norms
-                // and mean for its gathers (the pending chunk still reads the
-                // current slot).
-                slot ^= 1;
-                for (int i = t; i < G * L; i += 256) sqq[i % L][i / L] = a.qq[int64_t(bhq0) * L + i];
-                for (int i = t; i < G * kD; i += 256)
-                    sq[slot][i / kD][i % kD] = a.q[int64_t(bhq0) * kD + i];
-                if (t < G) sqn[slot][t] = a.qnorm[bhq0 + t];
-                if (t == 0) sqn[slot][2 * G] = a.rnorm ? a.rnorm[bkv] : 0.0f;
-                if (t < kD) smu[slot][t] = a.mu[int64_t(bkv) * kD + t];
-                cur_unit = bkv;
-            }
-            if (t < 2 * G * kWords) (&seen[0][0][0])[t] = 0u;
-            __syncthreads();
-            if (staged && t < G) {   // q_g.mu of the new unit, read by its gathers
-                float qm = 0.0f;
-                for (int c = 0; c < kD; ++c) qm = fmaf(sq[slot][t][c], smu[slot][c], qm);
-                sqn[slot][G + t] = qm;
-            }
+        const bool staged = bkv != cur_unit;
+        if (staged) {
+            // A new (sequence, KV head) unit: its query codes for the scan
+            // ([table][head]) and, in the other slot, the queries, norms
+            // and mean for its gathers (the pending chunk still reads the
+            // current slot).
+            slot ^= 1;
+            for (int i = t; i < G * L; i += 256) sqq[i % L][i / L] = a.qq[int64_t(bhq0) * L + i];
+            for (int i = t; i < G * kD; i += 256)
+                sq[slot][i / kD][i % kD] = a.q[int64_t(bhq0) * kD + i];
+            if (t < G) sqn[slot][t] = a.qnorm[bhq0 + t];
+            if (t == 0) sqn[slot][2 * G] = a.rnorm ? a.rnorm[bkv] : 0.0f;
+            if (t < kD) smu[slot][t] = a.mu[int64_t(bkv) * kD + t];
+            cur_unit = bkv;
+        }
+        if (t < 2 * G * kWords) (&seen[0][0][0])[t] = 0u;
+        __syncthreads();
+        if (staged) stage_qmu<G>(sq[slot], smu[slot], sqn[slot], t);   // read by the unit's gathers
 
-            // ---- (a) collision masks ----
-            const int tslot = t / kWords, tword = t % kWords;
-            uint32_t once[G], twice[G];
+        // ---- (a) collision masks ----
+        const int tslot = t / kWords, tword = t % kWords;
+        uint32_t once[G], twice[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) once[g] = twice[g] = 0u;
-            auto count_batch = [&](const uint32_t(&buf)[kTB][KP], int sb) {
+        for (int g = 0; g < G; ++g) once[g] = twice[g] = 0u;
+        auto count_batch = [&](const uint32_t(&buf)[kTB][KP], int sb) {
 #pragma unroll
-                for (int u = 0; u < kTB; ++u) {
-                    const int l = tslot + (sb * kTB + u) * kSlots;
-                    const uint32_t live = l < L ? ~0u : 0u;   // padding tables match nothing
-                    const int lu = min(l, L - 1);
+            for (int u = 0; u < kTB; ++u) {
+                const int l = tslot + (sb * kTB + u) * kSlots;
+                const uint32_t live = l < L ? ~0u : 0u;   // padding tables match nothing
+                const int lu = min(l, L - 1);
 #pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const uint32_t qv = sqq[lu][g];
-                        uint32_t eq = live;
+                for (int g = 0; g < G; ++g) {
+                    const uint32_t qv = sqq[lu][g];
+                    uint32_t eq = live;
 #pragma unroll
-                        for (int r = 0; r < KP; ++r)
-                            eq = and_xnor(eq, buf[u][r], bit_mask(qv, min(r, Kr - 1)));
-                        twice[g] |= once[g] & eq;
-                        once[g] |= eq;
-                    }
+                    for (int r = 0; r < KP; ++r)
+                        eq = and_xnor(eq, buf[u][r], bit_mask(qv, min(r, Kr - 1)));
+                    twice[g] |= once[g] & eq;
+                    once[g] |= eq;
                 }
-            };
-            // The first pair is peeled: entering it, the previous chunk's
-            // round-0 rows are younger than bufA and bufB and need not be
-            // waited for; inside the loop only the other buffer is younger.
-            count_batch(bufA, 0);
+            }
+        };
+        // The first pair is peeled: entering it, the previous chunk's
+        // round-0 rows are younger than bufA and bufB and need not be
+        // waited for; inside the loop only the other buffer is younger.
+        count_batch(bufA, 0);
+        load_next(bufA);
+        count_batch(bufB, 1);
+        load_next(bufB);
+        for (int sb = 2; sb < nb; sb += 2) {
+            count_batch(bufA, sb);
             load_next(bufA);
-            count_batch(bufB, 1);
+            count_batch(bufB, sb + 1);
             load_next(bufB);
-            for (int sb = 2; sb < nb; sb += 2) {
-                count_batch(bufA, sb);
-                load_next(bufA);
-                count_batch(bufB, sb + 1);
-                load_next(bufB);
-            }
-            // Merge the 16 slots of each word: a key is seen twice if some
-            // slot saw it twice or two slots saw it once.
+        }
+        // Merge the 16 slots of each word: a key is seen twice if some
+        // slot saw it twice or two slots saw it once.
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const uint32_t before = atomicOr(&seen[0][g][tword], once[g]);
-                atomicOr(&seen[1][g][tword], twice[g] | (once[g] & before));
-            }
+        for (int g = 0; g < G; ++g) {
+            const uint32_t before = atomicOr(&seen[0][g][tword], once[g]);
+            atomicOr(&seen[1][g][tword], twice[g] | (once[g] & before));
         }
 
-        if (!scan && pend) {
-            // Past the run the rows are the youngest loads: wait for them on
-            // this path alone, so that where the paths meet the rows count
-            // as older than the two batches in flight.
-#pragma unroll
-            for (int r = 0; r < kRowsPerGroup; ++r)
-#pragma unroll
-                for (int j = 0; j < Row8<T>::kLoads; ++j)
-                    asm volatile("" ::"v"(kraw[r].w[j]), "v"(vraw[r].w[j]));
-        }
         if (pend) {
             // ---- (c) gather-SNIS of the pending chunk (its round-0 rows were
             // loaded before this scan)
             gather_chunk<G, T>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot], sqn[p_slot],
                                smu[p_slot], kraw, vraw, t, gi, li);
+        } else {
+            retire_rows<T>(kraw, vraw);   // nothing in flight: returns at once
         }
         // the masks in seen are complete; the pending chunk's list is no
         // longer read
         __syncthreads();
-        pend = false;
-        if (!scan) break;
 
         // ---- (b) sampled / exact sets and ascending compaction ----
         // Thread t owns keys 2t and 2t+1 of the chunk: bits 2(t%16), +1 of
@@ -387,6 +370,19 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         p_chunk = chunk;
         p_total = total;
         p_slot = slot;
+    }
+
+    // The run's last chunk.  Its gather has its own copy here, after the
+    // loop, so that inside the loop every path to a gather has come through
+    // a scan: there the rows are older than the plane batches in flight, and
+    // reading them does not wait for those batches (the compiler merges its
+    // count of loads in flight over the paths that meet).  Here the rows are
+    // the youngest loads.
+    retire_rows<T>(kraw, vraw);
+    if (pend) {
+        const int t = threadIdx.x;
+        gather_chunk<G, T>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot], sqn[p_slot],
+                           smu[p_slot], kraw, vraw, t, t >> 4, t & 15);
     }
 }
 

@@ -176,6 +176,22 @@ __device__ __forceinline__ float wave_sum(float v)
 }
 
 
+// q_g.mu of the G staged queries into sqn[G + g], for q_g.(k - mu) =
+// q_g.k - q_g.mu: wave w of the 256 threads takes heads w, w + 4, ..., each
+// lane two dims, then a sum over the wave.
+template <int G>
+__device__ __forceinline__ void stage_qmu(const float (*sq)[kD], const float *smu, float *sqn,
+                                          int t)
+{
+    const int lane = t & 63;
+    for (int g = uniform(t >> 6); g < G; g += 4) {
+        const float2 qv = reinterpret_cast<const float2 *>(sq[g])[lane];
+        const float2 mv = reinterpret_cast<const float2 *>(smu)[lane];
+        const float qm = wave_sum(fmaf(qv.x, mv.x, qv.y * mv.y));
+        if (lane == 0) sqn[G + g] = qm;
+    }
+}
+
 // LDS of one gather round: per listed row the three reduced products, per
 // (row, head) z and the weight exp(z - running max), and the row's V.
 template <int G, typename T> struct GatherLds {
@@ -228,6 +244,21 @@ __device__ __forceinline__ void load_rows(const DecodeArgs &a, const T *kb, cons
         kr[r] = Row8<T>::load_raw(kb + i * a.k.sn);
         vr[r] = Row8<T>::load_raw(vb + i * a.v.sn);
     }
+}
+
+// Marks a round's row registers as read on every path.  A load whose
+// register is never read (rows past the list) stays pending in the
+// compiler's count, and later code that reuses the register must first wait
+// for it, which with in-order counting means waiting for every younger load
+// too: the plane batches issued ahead of the next chunk.
+template <typename T>
+__device__ __forceinline__ void retire_rows(const typename Row8<T>::raw (&kr)[kRowsPerGroup],
+                                            const typename Row8<T>::raw (&vr)[kRowsPerGroup])
+{
+#pragma unroll
+    for (int r = 0; r < kRowsPerGroup; ++r)
+#pragma unroll
+        for (int j = 0; j < Row8<T>::kLoads; ++j) asm volatile("" ::"v"(kr[r].w[j]), "v"(vr[r].w[j]));
 }
 
 // One round over list entries [base, base + ne), ne <= kRound, whose K/V
@@ -356,7 +387,10 @@ __device__ __forceinline__ void gather_c2(GatherLds<G, T> &s, int ne, GatherAcc<
     }
 }
 
-template <int G, typename T>
+// kLate: a round after the first, whose rows are the youngest loads: all of
+// them are marked read before c1 (where they are live in any case), rows
+// past the list included.
+template <int G, typename T, bool kLate>
 __device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T> &s,
                                              const uint32_t *ulist, int base, int ne,
                                              const float (*sq)[kD], const float *sqn,
@@ -365,6 +399,7 @@ __device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T
                                              const typename Row8<T>::raw (&vr_)[kRowsPerGroup],
                                              GatherAcc<G> &acc, int t, int gi, int li)
 {
+    if (kLate) retire_rows<T>(kr_, vr_);
     gather_c1<G, T>(s, ne, sq, smu, kr_, vr_, gi, li, 0, kRowsPerGroup);
     gather_z<G, T>(a, s, ulist, base, ne, sqn, gi, li);
     __syncthreads();
@@ -389,7 +424,7 @@ __device__ __forceinline__ void gather_rest(const DecodeArgs &a, GatherLds<G, T>
         const int ne = min(kRound, total - base);
         typename Row8<T>::raw kr[kRowsPerGroup], vr[kRowsPerGroup];
         load_rows<T>(a, kb, vb, ulist, base, ne, chunk, gi, kr, vr);
-        gather_round<G, T>(a, s, ulist, base, ne, sq, sqn, smu, kr, vr, acc, t, gi, li);
+        gather_round<G, T, true>(a, s, ulist, base, ne, sq, sqn, smu, kr, vr, acc, t, gi, li);
     }
 }
 
@@ -428,8 +463,9 @@ __device__ __forceinline__ void gather_chunk(const DecodeArgs &a, GatherLds<G, T
 {
     GatherAcc<G> acc;
     acc.reset();
-    if (total > 0) gather_round<G, T>(a, s, ulist, 0, min(kRound, total), sq, sqn, smu, kr0, vr0,
-                                      acc, t, gi, li);
+    if (total > 0)
+        gather_round<G, T, false>(a, s, ulist, 0, min(kRound, total), sq, sqn, smu, kr0, vr0, acc,
+                                  t, gi, li);
     gather_rest<G, T>(a, s, ulist, total, chunk, bkv, sq, sqn, smu, acc, t, gi, li);
     gather_store<G>(a, acc, chunk, bkv, t);
 }

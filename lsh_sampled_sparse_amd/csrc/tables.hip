@@ -252,11 +252,7 @@ __global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int3
         }
         write_seg_lists<G>(a, hm[0], hm[1], key0, bhq0, chunk, wsum, t);
     }
-    if (t < G) {   // q_g.mu (the staged queries are visible past the compaction's barriers)
-        float qm = 0.0f;
-        for (int c = 0; c < kD; ++c) qm = fmaf(sq[t][c], smu[c], qm);
-        sqn[G + t] = qm;
-    }
+    stage_qmu<G>(sq, smu, sqn, t);   // the staged queries are visible past the compaction's barriers
     __syncthreads();   // ulist, the staged queries and q.mu complete
 
     typename Row8<T>::raw kr[kRowsPerGroup], vr[kRowsPerGroup];
