@@ -228,11 +228,58 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
             ++lc;
         }
     };
+    // A new (sequence, KV head) unit: its query codes for the scan
+    // ([table][head]) and, in the other slot, the queries, norms and mean
+    // for its gathers (a pending chunk still reads the current slot).  All
+    // loads are issued before the first LDS write, so a unit costs one round
+    // trip (L <= 255: at most G code words a thread).  q_g.mu follows after
+    // the next barrier.
+    int cur_unit = -1, slot = 1;
+    bool qmu_due = false;
+    auto stage_unit = [&](int bkv, int bhq0, int t) {
+        slot ^= 1;
+        constexpr int kQ = (G * kD + 255) / 256;
+        uint32_t qqv[G];
+        float qv[kQ];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int i = t + 256 * j;
+            qqv[j] = i < G * L ? a.qq[int64_t(bhq0) * L + i] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kQ; ++j) {
+            const int i = t + 256 * j;
+            qv[j] = i < G * kD ? a.q[int64_t(bhq0) * kD + i] : 0.0f;
+        }
+        const float qn = t < G ? a.qnorm[bhq0 + t] : 0.0f;
+        const float rn = t == 0 && a.rnorm ? a.rnorm[bkv] : 0.0f;
+        const float mv = t < kD ? a.mu[int64_t(bkv) * kD + t] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int i = t + 256 * j;
+            if (i < G * L) sqq[i % L][i / L] = qqv[j];
+        }
+#pragma unroll
+        for (int j = 0; j < kQ; ++j) {
+            const int i = t + 256 * j;
+            if (i < G * kD) sq[slot][i / kD][i % kD] = qv[j];
+        }
+        if (t < G) sqn[slot][t] = qn;
+        if (t == 0) sqn[slot][2 * G] = rn;
+        if (t < kD) smu[slot][t] = mv;
+        cur_unit = bkv;
+        qmu_due = true;
+    };
+
     load_next(bufA);
     load_next(bufB);
-    // Wait for both here (nothing else is in flight yet), so that at the top
-    // of the chunk loop only the steady-state order of loads is possible:
-    // bufA, bufB, then the previous chunk's rows.
+    {   // the first unit, its loads in flight with the first two batches
+        const int t = threadIdx.x, bkv = gc_begin / a.n_chunks;
+        stage_unit(bkv, (bkv / a.H_kv) * a.H_q + (bkv % a.H_kv) * G, t);
+    }
+    // Wait for both here (only the staging was in flight besides), so that
+    // at the top of the chunk loop only the steady-state order of loads is
+    // possible: bufA, bufB, then the previous chunk's rows.
 #pragma unroll
     for (int u = 0; u < kTB; ++u)
 #pragma unroll
@@ -242,7 +289,6 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     bool pend = false;
     int p_bkv = 0, p_chunk = 0, p_total = 0, p_slot = 0;
     typename Row8<T>::raw kraw[kRowsPerGroup], vraw[kRowsPerGroup];
-    int cur_unit = -1, slot = 1;
 
 #pragma unroll 1
     for (int it = 0; it < nrun; ++it) {
@@ -257,23 +303,11 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         const int chunk = gc - bkv * a.n_chunks;
         const int bhq0 = (bkv / a.H_kv) * a.H_q + (bkv % a.H_kv) * G;
         const bool staged = bkv != cur_unit;
-        if (staged) {
-            // A new (sequence, KV head) unit: its query codes for the scan
-            // ([table][head]) and, in the other slot, the queries, norms
-            // and mean for its gathers (the pending chunk still reads the
-            // current slot).
-            slot ^= 1;
-            for (int i = t; i < G * L; i += 256) sqq[i % L][i / L] = a.qq[int64_t(bhq0) * L + i];
-            for (int i = t; i < G * kD; i += 256)
-                sq[slot][i / kD][i % kD] = a.q[int64_t(bhq0) * kD + i];
-            if (t < G) sqn[slot][t] = a.qnorm[bhq0 + t];
-            if (t == 0) sqn[slot][2 * G] = a.rnorm ? a.rnorm[bkv] : 0.0f;
-            if (t < kD) smu[slot][t] = a.mu[int64_t(bkv) * kD + t];
-            cur_unit = bkv;
-        }
+        if (staged) stage_unit(bkv, bhq0, t);
         if (t < 2 * G * kWords) (&seen[0][0][0])[t] = 0u;
         __syncthreads();
-        if (staged) stage_qmu<G>(sq[slot], smu[slot], sqn[slot], t);   // read by the unit's gathers
+        if (qmu_due) stage_qmu<G>(sq[slot], smu[slot], sqn[slot], t);   // read by the unit's gathers
+        qmu_due = false;
 
         // ---- (a) collision masks ----
         const int tslot = t / kWords, tword = t % kWords;
