@@ -356,8 +356,8 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         if (pend) {
             // ---- (c) gather-SNIS of the pending chunk (its round-0 rows were
             // loaded before this scan)
-            gather_chunk<G, T>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot], sqn[p_slot],
-                               smu[p_slot], kraw, vraw, t, gi, li);
+            gather_chunk<G, T, false>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot],
+                                      sqn[p_slot], smu[p_slot], kraw, vraw, t, gi, li);
         } else {
             retire_rows<T>(kraw, vraw);   // nothing in flight: returns at once
         }
@@ -415,8 +415,9 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     retire_rows<T>(kraw, vraw);
     if (pend) {
         const int t = threadIdx.x;
-        gather_chunk<G, T>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot], sqn[p_slot],
-                           smu[p_slot], kraw, vraw, t, t >> 4, t & 15);
+        // the plane buffers are dead here: the second round's rows go ahead
+        gather_chunk<G, T, true>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot], sqn[p_slot],
+                                 smu[p_slot], kraw, vraw, t, t >> 4, t & 15);
     }
 }
 

@@ -387,8 +387,8 @@ __device__ __forceinline__ void gather_c2(GatherLds<G, T> &s, int ne, GatherAcc<
     }
 }
 
-// kLate: a round after the first, whose rows are the youngest loads: all of
-// them are marked read before c1 (where they are live in any case), rows
+// kLate: a round after the first, whose rows may be the youngest loads: all
+// of them are marked read before c1 (where they are live in any case), rows
 // past the list included.
 template <int G, typename T, bool kLate>
 __device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T> &s,
@@ -405,27 +405,6 @@ __device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T
     __syncthreads();
     gather_c2<G, T>(s, ne, acc, t);
     __syncthreads();   // srow, sz, sw, sv are rewritten by the next round
-}
-
-// Rounds after the first of a chunk's list (each loads its own rows); the
-// first round may have ended without its trailing barrier.
-template <int G, typename T>
-__device__ __forceinline__ void gather_rest(const DecodeArgs &a, GatherLds<G, T> &s,
-                                            const uint32_t *ulist, int total, int chunk, int bkv,
-                                            const float (*sq)[kD], const float *sqn,
-                                            const float *smu, GatherAcc<G> &acc, int t, int gi,
-                                            int li)
-{
-    if (total <= kRound) return;
-    __syncthreads();   // the first round's c2 may still read its LDS
-    const T *kb, *vb;
-    row_bases<T>(a, bkv, li, kb, vb);
-    for (int base = kRound; base < total; base += kRound) {
-        const int ne = min(kRound, total - base);
-        typename Row8<T>::raw kr[kRowsPerGroup], vr[kRowsPerGroup];
-        load_rows<T>(a, kb, vb, ulist, base, ne, chunk, gi, kr, vr);
-        gather_round<G, T, true>(a, s, ulist, base, ne, sq, sqn, smu, kr, vr, acc, t, gi, li);
-    }
 }
 
 // The chunk's partial softmax (max, sum, unnormalised accumulator) per head.
@@ -451,8 +430,10 @@ __device__ __forceinline__ void gather_store(const DecodeArgs &a, const GatherAc
 
 // The whole list of one chunk: round 0 from rows already loaded (kr0 / vr0),
 // later rounds load theirs; then the chunk's partial softmax (max, sum,
-// unnormalised accumulator) per head goes to `part`.
-template <int G, typename T>
+// unnormalised accumulator) per head goes to `part`.  kAhead: the second
+// round's rows are issued before the first round runs, so that their
+// latency overlaps it (for callers with the registers to spare).
+template <int G, typename T, bool kAhead>
 __device__ __forceinline__ void gather_chunk(const DecodeArgs &a, GatherLds<G, T> &s,
                                              const uint32_t *ulist, int total, int chunk,
                                              int bkv, const float (*sq)[kD], const float *sqn,
@@ -463,10 +444,22 @@ __device__ __forceinline__ void gather_chunk(const DecodeArgs &a, GatherLds<G, T
 {
     GatherAcc<G> acc;
     acc.reset();
+    const T *kb, *vb;
+    row_bases<T>(a, bkv, li, kb, vb);
+    typename Row8<T>::raw kr[kRowsPerGroup], vr[kRowsPerGroup];
+    if (kAhead && total > kRound)
+        load_rows<T>(a, kb, vb, ulist, kRound, min(kRound, total - kRound), chunk, gi, kr, vr);
     if (total > 0)
         gather_round<G, T, false>(a, s, ulist, 0, min(kRound, total), sq, sqn, smu, kr0, vr0, acc,
                                   t, gi, li);
-    gather_rest<G, T>(a, s, ulist, total, chunk, bkv, sq, sqn, smu, acc, t, gi, li);
+    if (total > kRound) {
+        __syncthreads();   // the first round's c2 may still read its LDS
+        for (int base = kRound; base < total; base += kRound) {
+            const int ne = min(kRound, total - base);
+            if (!kAhead || base > kRound) load_rows<T>(a, kb, vb, ulist, base, ne, chunk, gi, kr, vr);
+            gather_round<G, T, true>(a, s, ulist, base, ne, sq, sqn, smu, kr, vr, acc, t, gi, li);
+        }
+    }
     gather_store<G>(a, acc, chunk, bkv, t);
 }
 

@@ -259,7 +259,10 @@ __global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int3
     const T *kb, *vb;
     row_bases<T>(a, bkv, li, kb, vb);
     load_rows<T>(a, kb, vb, ulist, 0, min(kRound, total), chunk, gi, kr, vr);
-    gather_chunk<G, T>(a, gl, ulist, total, chunk, bkv, sq, sqn, smu, kr, vr, t, gi, li);
+    // bf16 rows: the second round's rows are issued ahead (fp32 rows would
+    // cost a wave per SIMD)
+    gather_chunk<G, T, sizeof(T) == 2>(a, gl, ulist, total, chunk, bkv, sq, sqn, smu, kr, vr, t,
+                                       gi, li);
 }
 
 template <int G, typename T>
