@@ -195,7 +195,17 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     __shared__ GatherLds<G, T> gl;           // one gather round
 
     const int L = a.L, Kr = a.Kr;
-    const int gc_begin = blockIdx.x * cpb;
+    // Where runs align with units, workgroup b takes unit b % units and,
+    // counting from the unit's end, its run b / units: the runs that hold a
+    // sequence's last chunk (its exact local window, the longest list) go
+    // to the workgroups dispatched first, which the wave scheduler, oldest
+    // first, serves first.  Otherwise runs are in order.
+    int run = blockIdx.x;
+    if (a.n_chunks % cpb == 0) {
+        const int units = a.B * a.H_kv, per_unit = a.n_chunks / cpb;
+        run = (run % units) * per_unit + (per_unit - 1 - run / units);
+    }
+    const int gc_begin = run * cpb;
     const int nrun = min(cpb, a.B * a.H_kv * a.n_chunks - gc_begin);
     // batches per chunk for every thread: even, and at least 2
     const int nt = (L + kSlots - 1) / kSlots;
