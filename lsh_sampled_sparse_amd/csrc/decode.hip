@@ -75,7 +75,7 @@ __device__ __forceinline__ uint32_t and_xnor(uint32_t acc, uint32_t p, uint32_t 
 // row together (coalesced) and keep their 32 dims in registers for all the
 // block's heads, whose queries are LDS broadcasts; two shuffles add the
 // quarters.  Sign bits meet in LDS and are packed per (head, table).
-constexpr int kQueryHeads = 8;
+constexpr int kQueryHeads = 4;
 __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restrict__ q,
                                                            int32_t BHq,
                                                            const float *__restrict__ W, int32_t K,
