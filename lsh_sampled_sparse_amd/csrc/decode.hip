@@ -466,21 +466,23 @@ __global__ __launch_bounds__(256) void counts_kernel(DecodeArgs a)
 }
 
 // ---------------------------------------------------------------- merge
-// Block = one (KV head unit, query head g of its group, quarter of the dims);
-// thread = (dim c of 32, chunk lane j of 32).  Lane j folds chunks j, j+32,
-// ... into a running (max, sum, acc) in one pass, loading kMergeBatch chunks
-// before folding them so their loads overlap; the 32 lanes are then combined
-// in lane order, so the result is deterministic.
+// Block = one (KV head unit, query head g of its group, kMergeDims dims);
+// thread = (dim c of kMergeDims, chunk lane j of 32).  Lane j folds chunks
+// j, j+32, ... into a running (max, sum, acc) in one pass, loading
+// kMergeBatch chunks before folding them so their loads overlap; the 32 lanes
+// are then combined in lane order, so the result is deterministic.  16 dims
+// a block (256 blocks at 32 query heads) spread the launch over the CUs.
 constexpr int kMergeBatch = 8;
+constexpr int kMergeDims = 16;
 template <int G>
-__global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ part,
+__global__ __launch_bounds__(32 * kMergeDims) void merge_kernel(const float *__restrict__ part,
                                                     int32_t n_chunks, int32_t H_kv, int32_t H_q,
                                                     float *__restrict__ out)
 {
-    __shared__ float sm[32][33], sl[32][33], sa[32][33];
+    __shared__ float sm[32][kMergeDims + 1], sl[32][kMergeDims + 1], sa[32][kMergeDims + 1];
     const int bkv = blockIdx.x / G, g = blockIdx.x % G;
-    const int t = threadIdx.x, cl = t & 31, j = t >> 5;
-    const int c = 32 * blockIdx.y + cl;
+    const int t = threadIdx.x, cl = t % kMergeDims, j = t / kMergeDims;
+    const int c = kMergeDims * blockIdx.y + cl;
     const float *p = part + int64_t(bkv) * n_chunks * (G * kPart) + g * kPart;
     float m = -INFINITY, l = 0.0f, acc = 0.0f;
     for (int base = j; base < n_chunks; base += 32 * kMergeBatch) {
@@ -513,7 +515,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ p
     sl[j][cl] = l;
     sa[j][cl] = acc;
     __syncthreads();
-    if (t < 32) {
+    if (t < kMergeDims) {
         float M = -INFINITY;
         for (int r = 0; r < 32; ++r) M = fmaxf(M, sm[r][t]);
         float ls = 0.0f, as = 0.0f;
@@ -620,12 +622,12 @@ hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s)
 
 hipError_t launch_merge(const DecodeArgs &a, hipStream_t s)
 {
-    const dim3 grid(a.B * a.H_kv * a.G, kD / 32);
+    const dim3 grid(a.B * a.H_kv * a.G, kD / kMergeDims);
     switch (a.G) {
-    case 1: merge_kernel<1><<<grid, 1024, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
-    case 2: merge_kernel<2><<<grid, 1024, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
-    case 4: merge_kernel<4><<<grid, 1024, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
-    case 8: merge_kernel<8><<<grid, 1024, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
+    case 1: merge_kernel<1><<<grid, 32 * kMergeDims, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
+    case 2: merge_kernel<2><<<grid, 32 * kMergeDims, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
+    case 4: merge_kernel<4><<<grid, 32 * kMergeDims, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
+    case 8: merge_kernel<8><<<grid, 32 * kMergeDims, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
