@@ -118,6 +118,34 @@ def test_rejects_mismatched_caches():
         mp.decode_attn(q, idx, k, v, 4, 64, scratch=small)
 
 
+def test_runs_of_two_chunks_every_head():
+    """8 KV heads x 98 chunks = 784 chunks, more than the 768 workgroups that
+    256 CUs hold at 3 a CU: workgroups take runs of two chunks (the gather of
+    one chunk after the next one's scan), and with runs aligned to the KV
+    heads each head's last run goes to the first workgroups.  Codes on 2,048
+    sampled keys per head; counts, sets and outputs on every query head."""
+    n = 98 * 512 - 37
+    k, v, q = _inputs(1, 32, 8, n, torch.bfloat16, seed=71)
+    rows = np.sort(np.random.default_rng(1).choice(n, 2048, replace=False))
+    r = run_case(k, v, q, 8, 40, seed=8, n_sink=4, n_local=64, key_rows=rows,
+                 check_all_codes=False)
+    print("runs of two", r, flush=True)
+
+
+def test_runs_crossing_kv_heads_every_head():
+    """8 KV heads x 97 chunks = 776 chunks: runs of two in order, so some runs
+    start in one KV head's chunks and end in the next one's.  The next head's
+    queries are staged mid-run while the previous head's chunk is still to be
+    gathered (the two staging slots), and a head's last chunk (the exact local
+    window, a list of more than one round) is gathered inside the run."""
+    n = 97 * 512 - 100
+    k, v, q = _inputs(1, 32, 8, n, torch.bfloat16, seed=73)
+    rows = np.sort(np.random.default_rng(2).choice(n, 2048, replace=False))
+    r = run_case(k, v, q, 8, 40, seed=9, n_sink=4, n_local=64, key_rows=rows,
+                 check_all_codes=False)
+    print("runs crossing heads", r, flush=True)
+
+
 def test_forty_thousand_keys_sampled_codes():
     """n = 40,000 (79 chunks, 5 merge groups) at K=10, L=150; key codes are
     checked on 2,048 sampled keys, counts/sets/outputs on all heads."""
