@@ -195,6 +195,7 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     __shared__ GatherLds<G, T> gl;           // one gather round
 
     const int L = a.L, Kr = a.Kr;
+    constexpr bool kSplitGather = sizeof(T) == 2;
     // Where runs align with units, workgroup b takes unit b % units and,
     // counting from the unit's end, its run b / units: the runs that hold a
     // sequence's last chunk (its exact local window, the longest list) go
@@ -349,6 +350,18 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         load_next(bufA);
         count_batch(bufB, 1);
         load_next(bufB);
+        // ---- (c), first part (bf16 rows): c1 and z of the pending chunk's
+        // first round, wave-local, while the two batches just issued are in
+        // flight (its rows were loaded before this scan and are older than
+        // those batches).  With fp32 rows the registers this needs would
+        // cost a wave per SIMD, and the gather runs whole after the scan.
+        if (kSplitGather) {
+            if (pend)
+                gather_head<G, T>(a, gl, ulist, p_total, sq[p_slot], sqn[p_slot], smu[p_slot],
+                                  kraw, vraw, gi, li);
+            else
+                retire_rows<T>(kraw, vraw);   // nothing in flight: returns at once
+        }
         for (int sb = 2; sb < nb; sb += 2) {
             count_batch(bufA, sb);
             load_next(bufA);
@@ -363,17 +376,26 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
             atomicOr(&seen[1][g][tword], twice[g] | (once[g] & before));
         }
 
-        if (pend) {
-            // ---- (c) gather-SNIS of the pending chunk (its round-0 rows were
-            // loaded before this scan)
-            gather_chunk<G, T, false>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot],
-                                      sqn[p_slot], smu[p_slot], kraw, vraw, t, gi, li);
+        if (kSplitGather) {
+            // the masks in seen are complete, and so is the pending chunk's z
+            __syncthreads();
+            if (pend) {
+                // ---- (c), the rest: c2 of the first round, later rounds,
+                // the partial; then the pending chunk's list and LDS are free
+                gather_tail<G, T>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot],
+                                  sqn[p_slot], smu[p_slot], t, gi, li);
+                __syncthreads();
+            }
         } else {
-            retire_rows<T>(kraw, vraw);   // nothing in flight: returns at once
+            if (pend)   // ---- (c) gather-SNIS of the pending chunk
+                gather_chunk<G, T, false>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot],
+                                          sqn[p_slot], smu[p_slot], kraw, vraw, t, gi, li);
+            else
+                retire_rows<T>(kraw, vraw);   // nothing in flight: returns at once
+            // the masks in seen are complete; the pending chunk's list is no
+            // longer read
+            __syncthreads();
         }
-        // the masks in seen are complete; the pending chunk's list is no
-        // longer read
-        __syncthreads();
 
         // ---- (b) sampled / exact sets and ascending compaction ----
         // Thread t owns keys 2t and 2t+1 of the chunk: bits 2(t%16), +1 of
@@ -426,8 +448,10 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     if (pend) {
         const int t = threadIdx.x;
         // the plane buffers are dead here: the second round's rows go ahead
-        gather_chunk<G, T, true>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot], sqn[p_slot],
-                                 smu[p_slot], kraw, vraw, t, t >> 4, t & 15);
+        // (bf16 rows; fp32 rows would not fit the registers)
+        gather_chunk<G, T, sizeof(T) == 2>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot],
+                                           sqn[p_slot], smu[p_slot], kraw, vraw, t, t >> 4,
+                                           t & 15);
     }
 }
 

@@ -407,6 +407,52 @@ __device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T
     __syncthreads();   // srow, sz, sw, sv are rewritten by the next round
 }
 
+// A chunk's gather in two parts, for a caller that runs the first inside
+// other work.  gather_head: round 0's c1 and z, which touch only LDS of the
+// calling wave and need no barrier; then, after a barrier, gather_tail: round
+// 0's c2, the later rounds, and the chunk's partial.
+template <int G, typename T>
+__device__ __forceinline__ void gather_head(const DecodeArgs &a, GatherLds<G, T> &s,
+                                            const uint32_t *ulist, int total,
+                                            const float (*sq)[kD], const float *sqn,
+                                            const float *smu,
+                                            const typename Row8<T>::raw (&kr0)[kRowsPerGroup],
+                                            const typename Row8<T>::raw (&vr0)[kRowsPerGroup],
+                                            int gi, int li)
+{
+    if (total <= 0) return;
+    const int ne = min(kRound, total);
+    gather_c1<G, T>(s, ne, sq, smu, kr0, vr0, gi, li, 0, kRowsPerGroup);
+    gather_z<G, T>(a, s, ulist, 0, ne, sqn, gi, li);
+}
+
+template <int G>
+__device__ __forceinline__ void gather_store(const DecodeArgs &a, const GatherAcc<G> &acc,
+                                             int chunk, int bkv, int t);
+
+template <int G, typename T>
+__device__ __forceinline__ void gather_tail(const DecodeArgs &a, GatherLds<G, T> &s,
+                                            const uint32_t *ulist, int total, int chunk, int bkv,
+                                            const float (*sq)[kD], const float *sqn,
+                                            const float *smu, int t, int gi, int li)
+{
+    GatherAcc<G> acc;
+    acc.reset();
+    if (total > 0) gather_c2<G, T>(s, min(kRound, total), acc, t);
+    if (total > kRound) {
+        __syncthreads();   // round 0's c2 may still read its LDS
+        const T *kb, *vb;
+        row_bases<T>(a, bkv, li, kb, vb);
+        typename Row8<T>::raw kr[kRowsPerGroup], vr[kRowsPerGroup];
+        for (int base = kRound; base < total; base += kRound) {
+            const int ne = min(kRound, total - base);
+            load_rows<T>(a, kb, vb, ulist, base, ne, chunk, gi, kr, vr);
+            gather_round<G, T, true>(a, s, ulist, base, ne, sq, sqn, smu, kr, vr, acc, t, gi, li);
+        }
+    }
+    gather_store<G>(a, acc, chunk, bkv, t);
+}
+
 // The chunk's partial softmax (max, sum, unnormalised accumulator) per head.
 template <int G>
 __device__ __forceinline__ void gather_store(const DecodeArgs &a, const GatherAcc<G> &acc,
