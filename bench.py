@@ -43,26 +43,35 @@ KERNEL_SOURCES = {   # the files whose text fixes each timed kernel's code
 # and WRITE_SIZE in two separate --pmc runs of this script with --calib-copy),
 # each counter scaled by the factor that makes it read the known bytes of the
 # 256 MiB fp32 negation that --calib-copy runs in the same process.  Valid only
-# for the kernel source they were taken on: reported as null once the sources
-# no longer hash to sources_sha256.
+# for the kernel source they were taken on: reported as null once the sources,
+# comments and whitespace aside, no longer hash to sources_sha256.
 MEASURED_TRAFFIC = {
     "scan_gather": {
-        "sources_sha256": "e600312936991ae0f6565a527b6df4adbb6c1a2d2c148f40dd4652a87a839f30",
+        "sources_sha256": "1941c2ca327ac6e4c6aae97cd3f02b3a145a9b3c61e9172fa7c8989cf4b4157a",
         "fetch_kib": 83852.7, "fetch_scale": 1.9999, "write_kib": 3155.7, "write_scale": 1.0000,
         "bytes_per_launch": 174949320},
     "table_gather": {
-        "sources_sha256": "bb0915af7c538d0417f0385d3c7fbac6cfcc7e068c0b34585ac1c8d2df215a95",
+        "sources_sha256": "aac5a27d659f20377536064f937ee212ffa33a97161af871cdf129ac6b665c68",
         "fetch_kib": 13288.9, "fetch_scale": 1.9999, "write_kib": 3316.4, "write_scale": 1.0000,
         "bytes_per_launch": 30609688},
 }
+
+
+def code_text(src: str) -> str:
+    """Source text without comments, whitespace runs collapsed: what the
+    compiler sees, so that a comment edit keeps a measurement valid."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
 
 
 def sources_sha256(kernel: str) -> str:
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

@@ -172,9 +172,10 @@ inline int plane_rows_class(int Kr)
 //       theirs through LDS atomics;
 //   (b) the union of sampled and exact keys is compacted into an ascending
 //       LDS list, and the K/V rows of its first kRound entries are loaded;
-//   (c) gather-SNIS over the list, run one chunk late: after the next
-//       chunk's scan, when the rows have long arrived.  The chunk's partial
-//       softmax goes to `part`.
+//   (c) gather-SNIS over the list, run one chunk late, when the rows have
+//       long arrived: with bf16 rows the first round's dots and z inside the
+//       next chunk's scan and the rest after it, with fp32 rows all of it
+//       after the scan.  The chunk's partial softmax goes to `part`.
 // Each thread reads its tables of all chunks of the run as one stream, one
 // table (KP plane words) per batch, in two alternating register buffers
 // issued two batches ahead across chunk boundaries.  Every load on the main
