@@ -196,8 +196,11 @@ __global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int3
     __shared__ float sqn[2 * G + 1];   // |q_g|, q_g.mu, the lift radius
     __shared__ __align__(16) float smu[kD];
     __shared__ GatherLds<G, T> gl;
-    const int gc = blockIdx.x;
-    const int bkv = gc / a.n_chunks, chunk = gc - bkv * a.n_chunks;
+    // Workgroup b takes unit b % units and, counting back from the unit's
+    // end, chunk b / units: each sequence's last chunk (its exact local
+    // window, the longest list) goes to the workgroups dispatched first.
+    const int units = a.B * a.H_kv;
+    const int bkv = blockIdx.x % units, chunk = a.n_chunks - 1 - blockIdx.x / units;
     const int bhq0 = (bkv / a.H_kv) * a.H_q + (bkv % a.H_kv) * G;
     const int t = threadIdx.x, gi = t >> 4, li = t & 15;
     for (int i = t; i < G * kD; i += 256) sq[i / kD][i % kD] = a.q[int64_t(bhq0) * kD + i];
