@@ -349,9 +349,9 @@ def main():
         print(json.dumps({k: sources_sha256(k) for k in KERNEL_SOURCES}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the per-(sequence, KV head) units would shard across GPUs with no exchange; "
-              "see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(its per-(sequence, KV head) units would shard across GPUs with no exchange "
+              "between them)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -19,7 +19,7 @@
  * All arithmetic is IEEE fp64 (build without -ffast-math).  Inputs given as
  * bf16/fp32 are converted to fp64 exactly by the caller.
  *
- * Readings where the pages are silent (every one is listed in the design notes):
+ * Readings where the pages are silent:
  *   - hyperplanes: element e of the row-major [R][d] matrix W is a standard
  *     normal made by the Box-Muller transform (Box & Muller 1958) from the
  *     outputs 2e+1 and 2e+2 of SplitMix64 (Steele, Lea & Flood, OOPSLA 2014)
