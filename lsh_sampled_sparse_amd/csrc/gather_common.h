@@ -18,6 +18,8 @@ constexpr int kPart = kD + 2;     // partial softmax: m, l, acc[128]
 #endif
 constexpr int kRowsPerGroup = MP_ROWS_PER_GROUP;  // listed rows a 16-lane group holds per round
 constexpr int kRound = 16 * kRowsPerGroup;
+// c2 takes a round's rows one per lane of a wave.
+static_assert(kRound <= 64, "a gather round holds at most 64 rows (4 per 16-lane group)");
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
