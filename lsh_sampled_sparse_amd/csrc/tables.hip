@@ -77,7 +77,18 @@ __device__ __forceinline__ uint32_t key_code(const uint32_t *pl, int64_t chunk_s
     return c;
 }
 
-// Block = one (unit, table).  hist: nbins counters, then cursors.
+// Keys per staged tile of the scatter: its entries are grouped by bucket in
+// LDS, then written out as one run per bucket (key index and code packed in
+// a word: n < 2^20 and K <= 12 where tables are built).
+constexpr int kStageTile = 16384;
+constexpr int kStageKeys = kStageTile / kBuildThreads;   // per thread
+// tables are built only where the collide bitmap (2 bits a key) fits in the
+// 160 KB of LDS: n < 160 KB * 4 keys a byte < 2^20
+static_assert(int64_t(160 * 1024) * 4 < (int64_t(1) << 20), "key indices must fit in 20 bits");
+static_assert(kMaxTableK <= 12, "codes must fit in 12 bits");
+
+// Block = one (unit, table).  LDS: hist (nbins counters, then cursors), the
+// tile's counts and starts per bucket, the staged tile.
 __global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
     const uint32_t *__restrict__ planes, int32_t n, int32_t nc_cap, int32_t L, int32_t K,
     int32_t Kr, int32_t nbins, uint32_t *__restrict__ off, uint32_t *__restrict__ ent)
@@ -116,9 +127,55 @@ __global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
     if (t == 0) o[nbins] = uint32_t(n);
     __syncthreads();
     uint32_t *e = ent + (int64_t(u) * L + l) * n;
-    for (int i = t; i < n; i += kBuildThreads) {
-        const uint32_t c = key_code(pl, cstride, K, i);
-        e[atomicAdd(&hist[c], 1u)] = uint32_t(i);
+    uint32_t *tcount = hist + nbins, *tstart = tcount + nbins, *stage = tstart + nbins;
+    for (int t0 = 0; t0 < n; t0 += kStageTile) {
+        const int tn = min(kStageTile, n - t0);
+        for (int b = t; b < nbins; b += kBuildThreads) tcount[b] = 0u;
+        __syncthreads();
+        // each key's bucket and its rank among the tile's keys of that bucket
+        uint32_t pk[kStageKeys], rk[kStageKeys];
+#pragma unroll
+        for (int k = 0; k < kStageKeys; ++k) {
+            const int j = t + k * kBuildThreads;
+            pk[k] = rk[k] = 0u;
+            if (j < tn) {
+                const uint32_t c = key_code(pl, cstride, K, t0 + j);
+                pk[k] = uint32_t(t0 + j) | (c << 20);
+                rk[k] = atomicAdd(&tcount[c], 1u);
+            }
+        }
+        __syncthreads();
+        // the tile's start of each bucket (same bin ownership as above)
+        uint32_t tl[4], ts = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int b = t * per + k;
+            tl[k] = (k < per && b < nbins) ? tcount[b] : 0u;
+            ts += tl[k];
+        }
+        uint32_t tall;
+        uint32_t tb = block_exclusive_scan(ts, wtot, tall);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int b = t * per + k;
+            if (k < per && b < nbins) {
+                tstart[b] = tb;
+                tb += tl[k];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kStageKeys; ++k)
+            if (t + k * kBuildThreads < tn) stage[tstart[pk[k] >> 20] + rk[k]] = pk[k];
+        __syncthreads();
+        // one run per bucket, consecutive entries to consecutive words
+        for (int j = t; j < tn; j += kBuildThreads) {
+            const uint32_t v = stage[j], c = v >> 20;
+            e[hist[c] + (uint32_t(j) - tstart[c])] = v & 0xFFFFFu;
+        }
+        __syncthreads();
+        for (int b = t; b < nbins; b += kBuildThreads) hist[b] += tcount[b];
+        __syncthreads();
     }
 }
 
@@ -303,7 +360,7 @@ hipError_t launch_build_tables(const mp_index_impl &idx, hipStream_t s)
 {
     const IndexLayout &lay = idx.lay;
     const int nbins = 1 << lay.K;
-    const size_t lds = size_t(nbins) * 4;
+    const size_t lds = (size_t(3) * nbins + kStageTile) * 4;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(build_tables_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
