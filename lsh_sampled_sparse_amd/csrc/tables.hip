@@ -65,16 +65,22 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *w
     return base + x - v;
 }
 
-// Code of key i in the table whose plane rows start at `pl` (rows of one
-// chunk are L*Kr apart in whole chunks): its K bits, one per row.
-__device__ __forceinline__ uint32_t key_code(const uint32_t *pl, int64_t chunk_stride, int K,
-                                             int i)
+// Codes of the 16 keys i0 .. i0 + 15 (i0 a multiple of 16) in the table whose
+// plane rows start at `pl` (a table's rows recur every chunk_stride words,
+// one chunk of 512 keys apart): its K bits per key, one per plane row.  The
+// K plane words that hold the 16 keys are loaded once.
+__device__ __forceinline__ void key_codes16(const uint32_t *pl, int64_t chunk_stride, int K, int i0,
+                                            uint32_t (&c)[16])
 {
-    const uint32_t *w = pl + int64_t(i / kChunk) * chunk_stride + (i % kChunk) / 32;
-    const int bit = i % 32;
-    uint32_t c = 0u;
-    for (int b = 0; b < K; ++b) c |= ((w[b * kWords] >> bit) & 1u) << b;
-    return c;
+    const uint32_t *w = pl + int64_t(i0 / kChunk) * chunk_stride + (i0 % kChunk) / 32;
+    const int sh = i0 % 32;   // 0 or 16
+#pragma unroll
+    for (int k = 0; k < 16; ++k) c[k] = 0u;
+    for (int b = 0; b < K; ++b) {
+        const uint32_t x = w[b * kWords] >> sh;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) c[k] |= ((x >> k) & 1u) << b;
+    }
 }
 
 // Keys per staged tile of the scatter: its entries are grouped by bucket in
@@ -86,6 +92,7 @@ constexpr int kStageKeys = kStageTile / kBuildThreads;   // per thread
 // 160 KB of LDS: n < 160 KB * 4 keys a byte < 2^20
 static_assert(int64_t(160 * 1024) * 4 < (int64_t(1) << 20), "key indices must fit in 20 bits");
 static_assert(kMaxTableK <= 12, "codes must fit in 12 bits");
+static_assert(kStageKeys == 16, "a thread stages the 16 keys whose codes it reads together");
 
 // Block = one (unit, table).  LDS: hist (nbins counters, then cursors), the
 // tile's counts and starts per bucket, the staged tile.
@@ -101,7 +108,14 @@ __global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
     const uint32_t *pl = planes + int64_t(u) * nc_cap * cstride + int64_t(l) * Kr * kWords;
     for (int b = t; b < nbins; b += kBuildThreads) hist[b] = 0u;
     __syncthreads();
-    for (int i = t; i < n; i += kBuildThreads) atomicAdd(&hist[key_code(pl, cstride, K, i)], 1u);
+    // 16 consecutive keys a thread: their K plane words are loaded once
+    for (int i0 = 16 * t; i0 < n; i0 += 16 * kBuildThreads) {
+        uint32_t c[16];
+        key_codes16(pl, cstride, K, i0, c);
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (i0 + k < n) atomicAdd(&hist[c[k]], 1u);
+    }
     __syncthreads();
     // thread t owns bins [t per, (t+1) per)
     const int per = (nbins + kBuildThreads - 1) / kBuildThreads;   // <= 4 for K <= 12
@@ -133,15 +147,19 @@ __global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
         for (int b = t; b < nbins; b += kBuildThreads) tcount[b] = 0u;
         __syncthreads();
         // each key's bucket and its rank among the tile's keys of that bucket
+        // thread t takes the tile's keys 16 t .. 16 t + 15
         uint32_t pk[kStageKeys], rk[kStageKeys];
+        {
+            uint32_t c[16];
+            if (16 * t < tn) key_codes16(pl, cstride, K, t0 + 16 * t, c);
 #pragma unroll
-        for (int k = 0; k < kStageKeys; ++k) {
-            const int j = t + k * kBuildThreads;
-            pk[k] = rk[k] = 0u;
-            if (j < tn) {
-                const uint32_t c = key_code(pl, cstride, K, t0 + j);
-                pk[k] = uint32_t(t0 + j) | (c << 20);
-                rk[k] = atomicAdd(&tcount[c], 1u);
+            for (int k = 0; k < kStageKeys; ++k) {
+                const int j = 16 * t + k;
+                pk[k] = rk[k] = 0u;
+                if (j < tn) {
+                    pk[k] = uint32_t(t0 + j) | (c[k] << 20);
+                    rk[k] = atomicAdd(&tcount[c[k]], 1u);
+                }
             }
         }
         __syncthreads();
@@ -166,7 +184,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < kStageKeys; ++k)
-            if (t + k * kBuildThreads < tn) stage[tstart[pk[k] >> 20] + rk[k]] = pk[k];
+            if (16 * t + k < tn) stage[tstart[pk[k] >> 20] + rk[k]] = pk[k];
         __syncthreads();
         // one run per bucket, consecutive entries to consecutive words
         for (int j = t; j < tn; j += kBuildThreads) {
