@@ -60,6 +60,9 @@ def lib():
         L.orc_encode.argtypes = [_dp, C.c_int, _fp, C.c_int, C.c_int, _u16p, _u8p]
         L.orc_encode_keys.restype = C.c_int64
         L.orc_encode_keys.argtypes = [_dp, C.c_int64, C.c_int, _dp, _fp, C.c_int, C.c_int, _u16p]
+        L.orc_encode_keys_band.restype = C.c_int64
+        L.orc_encode_keys_band.argtypes = [_dp, C.c_int64, C.c_int, _dp, _fp, C.c_int, C.c_int,
+                                           _u16p, _u16p]
         L.orc_collision_counts.restype = None
         L.orc_collision_counts.argtypes = [_u16p, C.c_int64, C.c_int, _u16p, _i32p]
         L.orc_select.restype = C.c_int64
@@ -175,6 +178,39 @@ def encode_keys_parallel(keys, W, K, L, mu=None, threads=None):
                             range(threads)))
     codes = np.concatenate([p[0] for p in parts], axis=1)
     return codes, sum(p[1] for p in parts)
+
+
+def encode_keys_band(keys, W, K, L, mu=None):
+    """Table-major codes [L][n] of k_i - mu and the band masks [L][n] (bit b of
+    band[l][i] set where hyperplane l*K + b projects key i inside the 1e-5
+    band); band count."""
+    k = _f64(keys)
+    n, d = k.shape
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    codes = np.empty((L, n), dtype=np.uint16)
+    band = np.empty((L, n), dtype=np.uint16)
+    mup = None
+    if mu is not None:
+        mu = _f64(mu)
+        mup = _p(mu, _dp)
+    nb = lib().orc_encode_keys_band(_p(k, _dp), n, d, mup, _p(W, _fp), K, L, _p(codes, _u16p),
+                                    _p(band, _u16p))
+    return codes, band, int(nb)
+
+
+def encode_keys_band_parallel(keys, W, K, L, mu=None, threads=None):
+    """encode_keys_band split over row blocks in threads (ctypes drops the GIL)."""
+    k = _f64(keys)
+    n = k.shape[0]
+    threads = threads or os.cpu_count() or 1
+    if threads <= 1 or n < 256:
+        return encode_keys_band(k, W, K, L, mu)
+    bounds = np.linspace(0, n, threads + 1).astype(np.int64)
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda t: encode_keys_band(k[bounds[t]:bounds[t + 1]], W, K, L, mu),
+                            range(threads)))
+    return (np.concatenate([p[0] for p in parts], axis=1),
+            np.concatenate([p[1] for p in parts], axis=1), sum(p[2] for p in parts))
 
 
 # ----------------------------------------------------------- sampling rule

@@ -156,6 +156,51 @@ int64_t orc_encode_keys(const double *keys, int64_t n, int d, const double *mu,
     return nb;
 }
 
+/* orc_encode_keys plus, per table and key, the mask of the code's bits that
+ * lie in the band |w_j . x| < 1e-5 |w_j||x| (bit b of band[l*n + i] belongs
+ * to hyperplane l*K + b): a sign that close to 0 depends on the order in
+ * which the projection is summed, so a comparison may accept either value
+ * there.  The projections, norms and band test are those of
+ * orc_project_signs, with |w_j| (which does not depend on the key) computed
+ * once per hyperplane.  Returns the band count. */
+int64_t orc_encode_keys_band(const double *keys, int64_t n, int d, const double *mu,
+                             const float *W, int K, int L, uint16_t *codes, uint16_t *band)
+{
+    int64_t R = (int64_t)K * L;
+    double *x = (double *)malloc(sizeof(double) * (size_t)d);
+    double *wn = (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    for (int64_t j = 0; j < R; ++j) {
+        double ww = 0.0;
+        for (int c = 0; c < d; ++c) ww += (double)W[j * d + c] * (double)W[j * d + c];
+        wn[j] = sqrt(ww);
+    }
+    int64_t nb = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        double xx = 0.0;
+        for (int c = 0; c < d; ++c) {
+            x[c] = keys[i * d + c] - (mu ? mu[c] : 0.0);
+            xx += x[c] * x[c];
+        }
+        double xn = sqrt(xx);
+        for (int l = 0; l < L; ++l) {
+            unsigned code = 0, m = 0;
+            for (int b = 0; b < K; ++b) {
+                const float *w = W + ((int64_t)l * K + b) * d;
+                double proj = 0.0;
+                for (int c = 0; c < d; ++c) proj += (double)w[c] * x[c];
+                code |= (unsigned)(proj > 0.0) << b;
+                m |= (unsigned)(fabs(proj) < 1e-5 * wn[(int64_t)l * K + b] * xn) << b;
+            }
+            codes[(int64_t)l * n + i] = (uint16_t)code;
+            band[(int64_t)l * n + i] = (uint16_t)m;
+            nb += __builtin_popcount(m);
+        }
+    }
+    free(x);
+    free(wn);
+    return nb;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Inner-product-to-cosine augmentation ([P2] method details, variance        */
 /* reduction with LSH): with r the largest key norm, every key is lifted to   */

@@ -293,6 +293,90 @@ def test_horvitz_thompson_inclusion_and_sums():
     assert 0.02 < uvec[mid].min() and uvec[mid].max() < 0.98   # probabilities genuinely vary
 
 
+def _u_closed_form(p, K, L):
+    """P[Binomial(L, p^K) >= 2] in exact rationals (no oracle call)."""
+    P = Fraction(p) ** K
+    return float(1 - (1 - P) ** L - L * P * (1 - P) ** (L - 1))
+
+
+def _mirrored_keys(rng, m, d, n_center):
+    """2m keys in mirrored pairs c +- delta plus n_center copies of c: every
+    value is a multiple of 2^-10 below 1 in magnitude, so the fp64 sums are
+    exact and the mean is exactly c."""
+    c = rng.choice([-0.5, 0.5], size=d)
+    delta = np.round(rng.uniform(-0.49, 0.49, size=(m, d)) * 1024) / 1024
+    k = np.concatenate([c + delta, c - delta, np.tile(c, (n_center, 1))])
+    return k[rng.permutation(len(k))], c
+
+
+def test_zero_length_vectors_are_included_with_u_of_one_half():
+    """The zero-length reading (page "MagicPIG: don't pick the tallest",
+    section 5: zero-length vectors need a rule): a vector of length 0 has
+    every projection exactly 0, so with sign(0) = 0 its code is 0 in every
+    table; a random hyperplane puts a fixed other vector on either side with
+    probability 1/2, so one table matches with probability 2^-K and the pair
+    collides in >= 2 of L tables with probability u(p = 1/2).  The oracle's
+    cosine-0 rule (p = 1/2) is therefore the true inclusion probability, for a
+    centered key equal to the mean and for a zero query alike."""
+    rng = np.random.default_rng(21)
+    d, K, L, R = 16, 2, 6, 4000
+    k, c = _mirrored_keys(rng, 4, d, 1)
+    mu = oracle.mean(k)
+    assert np.array_equal(mu, c)
+    i0 = int(np.nonzero((k == c).all(1))[0][0])
+    q = rng.standard_normal(d)
+    zero = np.zeros(d)
+    u_half = _u_closed_form(Fraction(1, 2), K, L)
+    assert oracle.collision_p(q, k[i0] - mu) == 0.5
+    assert oracle.collision_p(zero, k[3] - mu) == 0.5
+    assert oracle.u(0.5, K, L) == pytest.approx(u_half, rel=1e-13)
+    j0 = (i0 + 3) % len(k)                     # a key of nonzero centered length
+    hit_key = hit_q = 0
+    for s in range(R):
+        W = oracle.hyperplanes(seed=7_000_000 + s, R=K * L, d=d)
+        codes, _ = oracle.encode_keys(k, W, K, L, mu)
+        assert not codes[:, i0].any()          # the zero vector's code is 0 everywhere
+        qc, _ = oracle.encode(q, W, K, L)
+        hit_key += int(np.count_nonzero(codes[:, i0] == qc) >= 2)
+        qz, _ = oracle.encode(zero, W, K, L)
+        assert not qz.any()
+        hit_q += int(np.count_nonzero(codes[:, j0] == qz) >= 2)
+    tol = 5 * math.sqrt(u_half * (1 - u_half) / R)
+    assert abs(hit_key / R - u_half) <= tol, (hit_key / R, u_half)
+    assert abs(hit_q / R - u_half) <= tol, (hit_q / R, u_half)
+
+
+def test_zero_query_estimate_is_the_closed_form():
+    """q = 0: every score is 0 and every sampled key has p = 1/2, so the
+    estimate is (sum_S v_i / u(1/2) + sum_T v_i) / (|S| / u(1/2) + |T|)."""
+    rng = np.random.default_rng(5)
+    n, d, K, L = 40, 128, 3, 10
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    S = np.array([2, 5, 6, 11, 30], dtype=np.int32)
+    T = [0, 1] + list(range(n - 4, n))
+    u = _u_closed_form(Fraction(1, 2), K, L)
+    ref = (v[S].sum(0) / u + v[T].sum(0)) / (len(S) / u + len(T))
+    out = oracle.estimate(np.zeros(d), k, v, oracle.mean(k), S, K, L, 2, 4)
+    assert np.max(np.abs(out - ref)) <= 1e-13 * np.max(np.abs(ref))
+    # a centered key equal to the mean gets p = 1/2 as well: with q != 0 its
+    # weight is exp(q.k/sqrt(d)) / u(1/2)
+    k2, c = _mirrored_keys(rng, 6, d, 1)
+    i0 = int(np.nonzero((k2 == c).all(1))[0][0])
+    v2 = rng.standard_normal((len(k2), d))
+    q = rng.standard_normal(d)
+    j = (i0 + 1) % len(k2)
+    mu2 = oracle.mean(k2)
+    uj = _u_closed_form(Fraction(1) - Fraction(math.acos(
+        float(np.dot(q, k2[j] - mu2) / np.linalg.norm(q) / np.linalg.norm(k2[j] - mu2))) / math.pi),
+        K, L)
+    z = np.array([q @ k2[i0] / math.sqrt(d) - math.log(u), q @ k2[j] / math.sqrt(d) - math.log(uj)])
+    w = np.exp(z - z.max())
+    ref2 = (w[0] * v2[i0] + w[1] * v2[j]) / w.sum()
+    out2 = oracle.estimate(q, k2, v2, mu2, np.array(sorted([i0, j]), np.int32), K, L, 0, 0)
+    assert np.max(np.abs(out2 - ref2)) <= 1e-9 * np.max(np.abs(ref2))
+
+
 def test_centering_is_score_invariant_and_needed():
     k, v, q = _tiny_inputs(5)
     K, L = 4, 16
