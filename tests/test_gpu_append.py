@@ -24,7 +24,8 @@ import torch
 import lsh_sampled_sparse_amd as mp
 import oracle
 import synth
-from parity_util import OUT_TOL, check_codes, gpu_codes_table_major, row_rel_err
+from parity_util import (OUT_TOL, check_codes, check_unit_codes, gpu_codes_table_major,
+                         oracle_threads, row_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +39,7 @@ def _cache(B, H_q, H_kv, n, dtype, seed):
     return inp["k"], inp["v"], inp["q"].contiguous()
 
 
-def check_index(idx, k, v, q, n, n0, K, L, seed, n_sink, n_local, heads=None, key_rows=None):
+def check_index(idx, k, v, q, n, n0, K, L, seed, n_sink, n_local):
     B, H_kv = k.shape[:2]
     H_q = q.shape[1]
     G = H_q // H_kv
@@ -62,14 +63,12 @@ def check_index(idx, k, v, q, n, n0, K, L, seed, n_sink, n_local, heads=None, ke
             kh = k[b, h, :n].cpu().double().numpy()
             vh = v[b, h, :n].cpu().double().numpy()
             mu0 = oracle.mean(k[b, h, :n0].cpu().double().numpy())     # frozen at build
-            rows = np.arange(n) if key_rows is None else key_rows(n)
-            m_, _, b_ = check_codes(kh[rows] - mu0, W, K, L, codes[b, h][:, rows].T, "key")
+            ref, band, _ = oracle.encode_keys_band_parallel(kh, W, K, L, mu0, oracle_threads())
+            m_, _ = check_unit_codes(ref, band, codes[b, h], f"key codes ({b},{h}), n={n}")
             mism += m_
-            bits += b_
+            bits += n * K * L
             for g in range(G):
                 hq = h * G + g
-                if heads is not None and (b, hq) not in heads:
-                    continue
                 qh = q[b, hq].cpu().double().numpy()
                 check_codes(qh[None], W, K, L, qcodes[b, hq][None], "query")
                 cnt = oracle.collision_counts(codes[b, h], qcodes[b, hq])
@@ -124,21 +123,15 @@ def test_grow_K0_every_key_collides():
         print("K0 growth", r, flush=True)
 
 
-def test_grow_96k_one_layer_sampled():
+@pytest.mark.timeout(600)
+def test_grow_96k_one_layer():
     """The timed workload's shape: built 300 keys short of 96K, grown in two
-    steps; keys sampled for the code check, a few heads for the outputs."""
+    steps; every key's codes and every head's counts, set and output after
+    each step."""
     cfg = synth.CONFIGS["llama8b_96k"]
     n1 = cfg.n
-    heads = [(0, hq) for hq in range(0, cfg.H_q, 9)]
-    rng = np.random.default_rng(5)
-
-    def key_rows(n):
-        return np.unique(np.concatenate([rng.choice(n - 400, 300, replace=False),
-                                         np.arange(n - 400, n)]))
-
     for r in run_growth(1, cfg.H_q, cfg.H_kv, cfg.dtype, cfg.K, cfg.L, n1 - 300,
-                        [n1 - 211, n1], cfg.n_sink, cfg.n_local, seed=cfg.hyperplane_seed(2),
-                        heads=heads, key_rows=key_rows):
+                        [n1 - 211, n1], cfg.n_sink, cfg.n_local, seed=cfg.hyperplane_seed(2)):
         print("96k growth", r, flush=True)
 
 

@@ -1,18 +1,20 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times.  The oracle checks what it can afford at this size:
-  * key codes of a random sample of keys per (sequence, KV head), exact
-    outside the 1e-5 band;
+benchmark times.  Every (sequence, KV head) unit and every query head is
+checked against the oracle:
+  * the codes of every key, exact outside the 1e-5 band (and mismatches
+    under 0.01% of bits);
   * query codes, collision counts and sampled sets of every query head
     (integer steps, run by the oracle on the GPU's codes);
-  * outputs of every checked head, against the oracle's estimator on the GPU's
-    sampled set.
+  * the output of every query head, against the oracle's estimator on the
+    GPU's sampled set;
+  * reported beside: S against the oracle's own codes, and the output error
+    on that S.
 The 256K workload also runs the L sweep 60/120/240 (nested hyperplanes, so
 nested sampled sets) and reports the estimator error against exact attention
 computed with plain PyTorch fp32 ops."""
 
 import math
 
-import numpy as np
 import pytest
 import torch
 
@@ -24,48 +26,44 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _rows(n, m, seed):
-    r = np.random.default_rng(seed).choice(n, min(m, n), replace=False)
-    r.sort()
-    return r
-
-
 def _cfg_inputs(name, layer=0):
     cfg = synth.CONFIGS[name]
     inp = synth.config_inputs(cfg, layer=layer, device=DEV)
     return cfg, inp["k"], inp["v"], inp["q"].contiguous()
 
 
+@pytest.mark.timeout(600)
 def test_llama8b_16k_full():
     cfg, k, v, q = _cfg_inputs("llama8b_16k")
     r = run_case(k, v, q, cfg.K, cfg.L, cfg.hyperplane_seed(0), cfg.n_sink, cfg.n_local,
-                 key_rows=_rows(cfg.n, 512, 1), check_all_codes=False)
+                 name="llama8b_16k")
     print("llama8b_16k", r, flush=True)
     assert 0.005 < r["mean_S"] / cfg.n < 0.05
 
 
+@pytest.mark.timeout(600)
 def test_llama8b_96k_one_layer_full():
     cfg, k, v, q = _cfg_inputs("llama8b_96k", layer=3)
     r = run_case(k, v, q, cfg.K, cfg.L, cfg.hyperplane_seed(3), cfg.n_sink, cfg.n_local,
-                 key_rows=_rows(cfg.n, 384, 2), check_all_codes=False)
+                 name="llama8b_96k")
     print("llama8b_96k", r, flush=True)
 
 
+@pytest.mark.timeout(900)
 def test_batch16_32k_full():
     cfg, k, v, q = _cfg_inputs("batch16_32k")
-    heads = [(b, hq) for b in range(cfg.B) for hq in range(0, cfg.H_q, 3)]
     r = run_case(k, v, q, cfg.K, cfg.L, cfg.hyperplane_seed(0), cfg.n_sink, cfg.n_local,
-                 heads=heads, key_rows=_rows(cfg.n, 96, 3), check_all_codes=False)
+                 name="batch16_32k")
     print("batch16_32k", r, flush=True)
 
 
+@pytest.mark.timeout(900)
 def test_llama70b_256k_full_and_L_sweep():
     import lsh_sampled_sparse_amd as mp
     cfg, k, v, q = _cfg_inputs("llama70b_256k")
     G = cfg.H_q // cfg.H_kv
-    heads = [(0, hq) for hq in range(0, cfg.H_q, 5)]
     r = run_case(k, v, q, cfg.K, cfg.L, cfg.hyperplane_seed(0), cfg.n_sink, cfg.n_local,
-                 heads=heads, key_rows=_rows(cfg.n, 256, 4), check_all_codes=False)
+                 name="llama70b_256k")
     print("llama70b_256k", r, flush=True)
 
     # exact attention, plain PyTorch fp32

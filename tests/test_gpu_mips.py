@@ -28,8 +28,8 @@ import torch
 import lsh_sampled_sparse_amd as mp
 import oracle
 import synth
-from parity_util import (OUT_TOL, check_codes, gpu_codes_table_major, row_rel_err,
-                         ulp_distance_f32)
+from parity_util import (OUT_TOL, check_codes, check_unit_codes, gpu_codes_table_major,
+                         oracle_threads, row_rel_err, ulp_distance_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +43,7 @@ def _inputs(B, H_q, H_kv, n, dtype, seed, tail=0.0):
     return inp["k"], inp["v"], inp["q"].contiguous()
 
 
-def run_lifted_case(k, v, q, K, L, seed, n_sink, n_local, heads=None, key_rows=None):
+def run_lifted_case(k, v, q, K, L, seed, n_sink, n_local):
     B, H_kv, n, d = k.shape
     H_q = q.shape[1]
     G = H_q // H_kv
@@ -75,18 +75,18 @@ def run_lifted_case(k, v, q, K, L, seed, n_sink, n_local, heads=None, key_rows=N
             mu = oracle.mean(kh)
             r = oracle.aug_radius(kh, mu)
             assert abs(float(r_gpu[b, h]) - r) <= 2e-6 * r, (float(r_gpu[b, h]), r)
-            rows = np.arange(n) if key_rows is None else key_rows
-            x = kh[rows] - mu
+            x = kh - mu
             lift = np.sqrt(np.maximum(r * r - (x * x).sum(axis=1), 0.0))
             xl = np.concatenate([x, lift[:, None]], axis=1)
             if K > 0:
-                m_, _, b_ = check_codes(xl, Wl, K, L, codes[b, h][:, rows].T, "lifted key")
+                # the lifted keys against the lifted hyperplanes, band taken on the lifted pair
+                ref, band, _ = oracle.encode_keys_band_parallel(xl, Wl, K, L, None,
+                                                                oracle_threads())
+                m_, _ = check_unit_codes(ref, band, codes[b, h], f"lifted key codes ({b},{h})")
                 mism += m_
-                bits += b_
+                bits += n * K * L
             for g in range(G):
                 hq = h * G + g
-                if heads is not None and (b, hq) not in heads:
-                    continue
                 qh = q[b, hq].cpu().double().numpy()
                 if K > 0:
                     check_codes(qh[None], W, K, L, qcodes[b, hq][None], "query")
@@ -144,14 +144,14 @@ def test_lifted_index_refuses_to_grow_and_plain_views():
         plain.lift_views()
 
 
-def test_llama8b_96k_lifted_sampled():
+@pytest.mark.timeout(600)
+def test_llama8b_96k_lifted():
+    """The timed workload with the lift: every key's lifted codes, every
+    head's counts, set and output."""
     cfg = synth.CONFIGS["llama8b_96k"]
     inp = synth.config_inputs(cfg, layer=3, device=DEV)
-    heads = [(0, hq) for hq in range(0, cfg.H_q, 7)]
-    rows = np.sort(np.random.default_rng(6).choice(cfg.n, 400, replace=False))
     _, r = run_lifted_case(inp["k"], inp["v"], inp["q"].contiguous(), cfg.K, cfg.L,
-                           cfg.hyperplane_seed(3), cfg.n_sink, cfg.n_local, heads=heads,
-                           key_rows=rows)
+                           cfg.hyperplane_seed(3), cfg.n_sink, cfg.n_local)
     print("llama8b_96k lifted", r, flush=True)
 
 

@@ -153,23 +153,25 @@ def test_forty_thousand_keys():
 
 
 def test_llama8b_96k_one_layer():
-    """The timed workload: every head's set against the code scan, outputs of
-    sampled heads against the oracle, and the tables of two units in full."""
+    """The timed workload: every head's set against the code scan and its
+    output against the oracle, and the tables of two units in full."""
     cfg = synth.CONFIGS["llama8b_96k"]
     inp = synth.config_inputs(cfg, layer=5, device=DEV)
-    heads = [(0, hq) for hq in range(0, cfg.H_q, 7)]
     r = run_tables_case(inp["k"], inp["v"], inp["q"].contiguous(), cfg.K, cfg.L,
-                        cfg.hyperplane_seed(5), cfg.n_sink, cfg.n_local, heads=heads,
+                        cfg.hyperplane_seed(5), cfg.n_sink, cfg.n_local,
                         table_units=[(0, 0), (0, 7)])
     print("llama8b_96k tables", r, flush=True)
 
 
-def test_llama70b_256k_sampled():
+@pytest.mark.timeout(600)
+def test_llama70b_256k_every_head():
+    """The 256K workload (G = 8): every head's set against the code scan and
+    its output against the oracle; the tables of one unit, three of them in
+    full."""
     cfg = synth.CONFIGS["llama70b_256k"]
     inp = synth.config_inputs(cfg, device=DEV)
-    heads = [(0, hq) for hq in range(0, cfg.H_q, 13)]
     r = run_tables_case(inp["k"], inp["v"], inp["q"].contiguous(), cfg.K, cfg.L,
-                        cfg.hyperplane_seed(0), cfg.n_sink, cfg.n_local, heads=heads,
+                        cfg.hyperplane_seed(0), cfg.n_sink, cfg.n_local,
                         table_units=[(0, 3)], table_rows=[0, 59, 119])
     print("llama70b_256k tables", r, flush=True)
 
