@@ -28,7 +28,13 @@
  *     queries, outputs, the index workspace and the decode scratch;
  *   - arguments are validated on the host before anything is enqueued; on any
  *     status other than MP_OK nothing has been enqueued (except MP_E_HIP, which
- *     reports a failed launch), and mp_last_error() describes the problem;
+ *     reports that one of the call's own launches failed: launches before it
+ *     in the same call stay enqueued), and mp_last_error() describes the
+ *     problem.  MP_E_HIP comes from the status each launch returns, never from
+ *     an error an earlier, unrelated HIP call left behind;
+ *   - index handles are checked against the library's list of live handles
+ *     before use: a destroyed handle gives MP_E_HANDLE, not a read of freed
+ *     memory;
  *   - device faults surface at the caller's next synchronisation of the stream;
  *   - head dimension d must be 128.
  *
@@ -190,18 +196,6 @@ mp_status mp_decode_debug(const float *q, int32_t H_q, const mp_index *idx,
                           void *scratch, size_t scratch_bytes, void *stream,
                           uint16_t *qcodes, uint8_t *counts, int32_t *s_idx, int32_t *s_len);
 
-/* mp_decode_attn that also stamps two caller-created hipEvent_t (passed as
- * void*, either may be NULL) with the start and the end of the fused
- * collision-scan + gather kernel (they are handed to the kernel's launch, so
- * no other command sits between them and the kernel), so the caller can time
- * that kernel on its own.  Used by the benchmark; the output is that of
- * mp_decode_attn. */
-mp_status mp_decode_attn_timed(const float *q, int32_t H_q, const mp_index *idx,
-                               const mp_kv_view *k, const mp_kv_view *v,
-                               int32_t n_sink, int32_t n_local, float scale, float *out,
-                               void *scratch, size_t scratch_bytes, void *stream,
-                               void *ev_scan_begin, void *ev_scan_end);
-
 /* ---- Bucketed hash tables (the retrieval of the summary page's algorithm
  * steps: the query's code selects one bucket per table, and the keys found in
  * at least two buckets are sampled; page "MagicPIG: don't pick the tallest",
@@ -239,15 +233,6 @@ mp_status mp_decode_attn_tables(const float *q, int32_t H_q, const mp_index *idx
                                 int32_t n_local, float scale, float *out, void *scratch,
                                 size_t scratch_bytes, void *stream);
 
-/* mp_decode_attn_tables that also stamps two caller-created hipEvent_t with
- * the start and end of the gather kernel (as mp_decode_attn_timed does for
- * the scan kernel).  Used by the benchmark. */
-mp_status mp_decode_attn_tables_timed(const float *q, int32_t H_q, const mp_index *idx,
-                                      const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
-                                      int32_t n_local, float scale, float *out, void *scratch,
-                                      size_t scratch_bytes, void *stream, void *ev_gather_begin,
-                                      void *ev_gather_end);
-
 /* mp_decode_tables with the debug views of mp_decode_debug, except that
  * counts2[b][h][i] = min(collision count, 2): the tables only tell whether a
  * key was seen once or at least twice. */
@@ -275,15 +260,8 @@ mp_status mp_tables_views(const mp_index *idx, const uint32_t **offsets, const u
 mp_status mp_index_views(const mp_index *idx, const float **W, const float **mu,
                          const uint32_t **planes, int32_t *n_pad);
 
-/* ---- Measurement aid (no part of the decode path) ----
- * A plain streaming read of `bytes` (16-byte aligned device memory) by
- * `blocks` workgroups of 256 threads: the HBM read rate of this device, the
- * reference the benchmark reports beside its kernels' rates.  `sink` is a
- * device word that is practically never written.  MP_E_ARG on bad arguments. */
-mp_status mp_stream_read(const void *data, int64_t bytes, uint32_t *sink, int32_t blocks,
-                         void *stream);
-
-/* Free the host handle (not the workspace).  NULL is ignored. */
+/* Free the host handle (not the workspace).  NULL and handles that are not
+ * live are ignored. */
 void mp_index_destroy(mp_index *idx);
 
 /* Static description of a status code. */

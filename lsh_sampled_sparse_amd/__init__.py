@@ -29,6 +29,33 @@ def _stream(stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _side_stream(stream, device):
+    """The torch stream object of `stream` (a torch stream or a raw
+    hipStream_t handle) when it is not the current stream of `device`, else
+    None: the library enqueues on the stream it is given, while the tensors
+    made here come from torch's caching allocator on the current stream."""
+    if stream is None:
+        return None
+    cur = torch.cuda.current_stream(device)
+    h = _stream(stream)
+    if h == int(cur.cuda_stream):
+        return None
+    if hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(h, device=device)
+
+
+def _keep_alive_on(side, *tensors):
+    """Mark tensors as used by work on the side stream, so that the caching
+    allocator does not hand their memory out again (after they are freed here)
+    before that work has run."""
+    if side is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(side)
+
+
 def kv_view(t: torch.Tensor) -> capi.mp_kv_view:
     """mp_kv_view of a [B][H][n][128] device tensor (fp32 or bf16, last dim contiguous)."""
     if t.dim() != 4:
@@ -131,6 +158,7 @@ def build_index(keys: torch.Tensor, K: int, L: int, seed: int, stream=None,
         raise ValueError(f"invalid index sizes B={view.B} H={view.H} n={n_cap} d={view.d} "
                          f"K={K} L={L}")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=keys.device)
+    _keep_alive_on(_side_stream(stream, keys.device), ws)
     if mips:
         h = capi.mp_build_index_ex(view, K, L, seed, n_cap, flags, ws.data_ptr(), nbytes,
                                    _stream(stream))
@@ -148,6 +176,8 @@ def append_index(index: MagicPIGIndex, keys: torch.Tensor, stream=None) -> Magic
     bucketed tables."""
     capi.mp_index_append(index.handle, kv_view(keys), _stream(stream))
     index.n = keys.shape[2]
+    # decodes on other streams may still read the old tables: they were marked
+    # on those streams when the decode was enqueued (see _decode)
     index.tables = None
     return index
 
@@ -159,6 +189,7 @@ def build_tables(index: MagicPIGIndex, stream=None) -> MagicPIGIndex:
     if nbytes == 0:
         raise ValueError(f"this index cannot have tables (K={index.K}, n={index.n})")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=index.workspace.device)
+    _keep_alive_on(_side_stream(stream, ws.device), ws)
     capi.mp_build_tables(index.handle, ws.data_ptr(), nbytes, _stream(stream))
     index.tables = ws
     return index
@@ -177,6 +208,10 @@ def _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, debug,
         scratch = torch.empty(need, dtype=torch.uint8, device=q.device)
     kv_k, kv_v = kv_view(k), kv_view(v)
     s = _stream(stream)
+    # on a side stream, the buffers allocated here and the index's workspaces
+    # must outlive this call's kernels, not just this Python call
+    _keep_alive_on(_side_stream(stream, q.device), out, scratch, index.workspace,
+                   index.tables if tables else None)
     if not debug:
         f = capi.mp_decode_attn_tables if tables else capi.mp_decode_attn
         f(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local, float(scale),
@@ -187,6 +222,7 @@ def _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, debug,
     counts = torch.empty(B, H_q, n, dtype=torch.uint8, device=q.device)
     s_idx = torch.empty(B, H_q, n, dtype=torch.int32, device=q.device)
     s_len = torch.empty(B, H_q, dtype=torch.int32, device=q.device)
+    _keep_alive_on(_side_stream(stream, q.device), qcodes, counts, s_idx, s_len)
     f = capi.mp_decode_tables_debug if tables else capi.mp_decode_debug
     f(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local, float(scale), out.data_ptr(),
       scratch.data_ptr(), scratch.numel(), s, qcodes.data_ptr(), counts.data_ptr(),

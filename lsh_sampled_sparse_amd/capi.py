@@ -24,7 +24,7 @@ EXPORTED = [
     "mp_tables_workspace_bytes", "mp_build_tables", "mp_decode_tables_scratch_bytes",
     "mp_decode_attn_tables", "mp_decode_attn_tables_timed", "mp_decode_tables_debug",
     "mp_tables_views", "mp_build_index_cap", "mp_index_append", "mp_index_workspace_bytes_ex",
-    "mp_build_index_ex", "mp_index_lift_views", "mp_stream_read",
+    "mp_build_index_ex", "mp_index_lift_views", "mp_stream_read", "mp_debug_fail_launches",
 ]
 
 
@@ -107,6 +107,8 @@ def lib():
         L.mp_status_str.argtypes = [C.c_int]
         L.mp_last_error.restype = C.c_char_p
         L.mp_last_error.argtypes = []
+        L.mp_debug_fail_launches.restype = None
+        L.mp_debug_fail_launches.argtypes = [i32, i32]
         _lib = L
     return _lib
 
@@ -254,3 +256,8 @@ def mp_index_views(idx: int):
 
 def mp_index_destroy(idx) -> None:
     lib().mp_index_destroy(idx)
+
+
+def mp_debug_fail_launches(skip: int, count: int) -> None:
+    """Test aid: after `skip` launches, the next `count` fail (magicpig_testing.h)."""
+    lib().mp_debug_fail_launches(skip, count)

@@ -6,7 +6,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
+#include <unordered_set>
 
 #include "mp_internal.h"
 
@@ -14,9 +16,11 @@ struct mp_index : mp::mp_index_impl {};
 
 namespace mp {
 
+std::atomic<uint64_t> g_forced_launch_failures{0};
+
 static thread_local char g_err[512] = "";
 
-static mp_status fail(mp_status s, const char *fmt, ...)
+mp_status fail(mp_status s, const char *fmt, ...)
 {
     va_list ap;
     va_start(ap, fmt);
@@ -76,7 +80,7 @@ IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t 
 size_t collide_lds_bytes(const IndexLayout &lay);   // tables.hip
 int collide_slices();                               // tables.hip
 
-DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables)
+DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables, bool debug)
 {
     DecodeLayout y{};
     y.BHq = lay.B * H_q;
@@ -87,21 +91,21 @@ DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables)
     y.off_qq = off;      off = align256(off + BHq * lay.L * 4);
     y.off_qnorm = off;   off = align256(off + BHq * 4);
     y.off_part = off;    off = align256(off + BHq * lay.n_chunks * int64_t(kD + 2) * 4);
-    y.off_seg_idx = off; off = align256(off + BHq * lay.n_chunks * int64_t(kChunk) * 4);
-    y.off_seg_cnt = off; off = align256(off + BHq * lay.n_chunks * 4);
+    y.off_seg_idx = off;
+    if (debug) off = align256(off + BHq * lay.n_chunks * int64_t(kChunk) * 4);
+    y.off_seg_cnt = off;
+    if (debug) off = align256(off + BHq * lay.n_chunks * 4);
     y.off_bits = off;
     if (tables) off = align256(off + BHq * collide_slices() * (lay.n_pad / 16) * 4);
     y.total = off;
     return y;
 }
 
-constexpr size_t kLdsLimit = 160 * 1024 - 1024;     // per workgroup, less the static part
-
 // Why the bucketed tables of an index cannot be used, or NULL.
 static const char *tables_unsupported(const IndexLayout &lay)
 {
     if (lay.K > kMaxTableK) return "tables need K <= 12 (2^K bucket counters in LDS)";
-    if (collide_lds_bytes(lay) > kLdsLimit)
+    if (collide_lds_bytes(lay) > kCollideLdsMax)
         return "tables need ceil(n/512)*128 + 4*(2L+1) <= 162,816 (2 bits per key in LDS)";
     return nullptr;
 }
@@ -130,18 +134,36 @@ static mp_status check_view(const mp_kv_view *v, const char *name)
     return MP_OK;
 }
 
-static const mp_index *live(const mp_index *idx)
+// Live index handles.  A handle is looked up here, never dereferenced, before
+// it is trusted: a destroyed handle is refused without reading freed memory
+// (its address may come back for a later index, which is then the live one).
+static std::mutex g_handles_m;
+static std::unordered_set<const mp_index *> g_handles;
+
+static void register_handle(const mp_index *idx)
 {
-    return (idx && idx->magic == kMagic) ? idx : nullptr;
+    std::lock_guard<std::mutex> g(g_handles_m);
+    g_handles.insert(idx);
 }
 
-static mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx,
-                               const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
-                               int32_t n_local, float scale, float *out, void *scratch,
-                               size_t scratch_bytes, void *stream, bool debug, uint16_t *qcodes,
-                               uint8_t *counts, int32_t *s_idx, int32_t *s_len,
-                               void *ev_begin = nullptr, void *ev_end = nullptr,
-                               bool tables = false)
+static bool unregister_handle(const mp_index *idx)
+{
+    std::lock_guard<std::mutex> g(g_handles_m);
+    return g_handles.erase(idx) > 0;
+}
+
+static const mp_index *live(const mp_index *idx)
+{
+    if (!idx) return nullptr;
+    std::lock_guard<std::mutex> g(g_handles_m);
+    return g_handles.count(idx) ? idx : nullptr;
+}
+
+mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx, const mp_kv_view *k,
+                        const mp_kv_view *v, int32_t n_sink, int32_t n_local, float scale,
+                        float *out, void *scratch, size_t scratch_bytes, void *stream, bool debug,
+                        uint16_t *qcodes, uint8_t *counts, int32_t *s_idx, int32_t *s_len,
+                        void *ev_begin, void *ev_end, bool tables)
 {
     g_err[0] = 0;
     if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
@@ -171,17 +193,17 @@ static mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx,
                     k->B, k->H, k->n, v->B, v->H, v->n, lay.B, lay.H_kv, lay.n);
     if (n_sink < 0 || n_local < 0) return fail(MP_E_ARG, "n_sink and n_local must be >= 0");
     if (!isfinite(scale) || scale < 0.0f) return fail(MP_E_ARG, "scale must be finite and >= 0");
-    const DecodeLayout dl = decode_layout(lay, H_q, tables);
+    const DecodeLayout dl = decode_layout(lay, H_q, tables, debug);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != idx->device)
+        return fail(MP_E_ARG, "current device %d is not the device %d the index lives on", dev,
+                    idx->device);
     if (!scratch) return fail(MP_E_WORKSPACE, "scratch is NULL");
     if (reinterpret_cast<uintptr_t>(scratch) & 255)
         return fail(MP_E_WORKSPACE, "scratch must be 256-byte aligned");
     if (scratch_bytes < size_t(dl.total))
         return fail(MP_E_WORKSPACE, "scratch holds %zu bytes, %lld needed", scratch_bytes,
                     (long long)dl.total);
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev != idx->device)
-        return fail(MP_E_ARG, "current device %d is not the device %d the index lives on", dev,
-                    idx->device);
 
     char *sp = static_cast<char *>(scratch);
     DecodeArgs a{};
@@ -280,7 +302,6 @@ static mp_status build_index_impl(const mp_kv_view *keys, int32_t K, int32_t L, 
     mp_index *idx = new (std::nothrow) mp_index();
     if (!idx) return fail(MP_E_ARG, "host allocation of the handle failed");
     char *wp = static_cast<char *>(workspace);
-    idx->magic = kMagic;
     idx->lay = lay;
     idx->seed = seed;
     idx->key_dtype = keys->dtype;
@@ -321,10 +342,10 @@ static mp_status build_index_impl(const mp_kv_view *keys, int32_t K, int32_t L, 
                                    idx->r2, lay.n_cap, s);
     }
     if (e != hipSuccess) {
-        idx->magic = 0;
         delete idx;
         return fail(MP_E_HIP, "index build launch failed: %s", hipGetErrorString(e));
     }
+    register_handle(idx);
     *out = idx;
     return MP_OK;
 }
@@ -403,7 +424,7 @@ mp_status mp_index_append(mp_index *idx, const mp_kv_view *keys, void *stream)
 size_t mp_decode_scratch_bytes(const mp_index *idx, int32_t H_q)
 {
     if (!live(idx) || H_q < 1 || H_q % idx->lay.H_kv) return 0;
-    return size_t(decode_layout(idx->lay, H_q).total);
+    return size_t(decode_layout(idx->lay, H_q, false, true).total);
 }
 
 mp_status mp_decode_attn(const float *q, int32_t H_q, const mp_index *idx, const mp_kv_view *k,
@@ -411,7 +432,7 @@ mp_status mp_decode_attn(const float *q, int32_t H_q, const mp_index *idx, const
                          float *out, void *scratch, size_t scratch_bytes, void *stream)
 {
     return decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
-                         stream, false, nullptr, nullptr, nullptr, nullptr);
+                         stream, false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false);
 }
 
 mp_status mp_decode_attn_timed(const float *q, int32_t H_q, const mp_index *idx,
@@ -422,7 +443,7 @@ mp_status mp_decode_attn_timed(const float *q, int32_t H_q, const mp_index *idx,
 {
     return decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
                          stream, false, nullptr, nullptr, nullptr, nullptr, ev_scan_begin,
-                         ev_scan_end);
+                         ev_scan_end, false);
 }
 
 mp_status mp_decode_debug(const float *q, int32_t H_q, const mp_index *idx, const mp_kv_view *k,
@@ -431,7 +452,7 @@ mp_status mp_decode_debug(const float *q, int32_t H_q, const mp_index *idx, cons
                           uint16_t *qcodes, uint8_t *counts, int32_t *s_idx, int32_t *s_len)
 {
     return decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
-                         stream, true, qcodes, counts, s_idx, s_len);
+                         stream, true, qcodes, counts, s_idx, s_len, nullptr, nullptr, false);
 }
 
 size_t mp_tables_workspace_bytes(const mp_index *idx)
@@ -470,7 +491,7 @@ mp_status mp_build_tables(mp_index *idx, void *workspace, size_t workspace_bytes
 size_t mp_decode_tables_scratch_bytes(const mp_index *idx, int32_t H_q)
 {
     if (!live(idx) || H_q < 1 || H_q % idx->lay.H_kv || tables_unsupported(idx->lay)) return 0;
-    return size_t(decode_layout(idx->lay, H_q, true).total);
+    return size_t(decode_layout(idx->lay, H_q, true, true).total);
 }
 
 mp_status mp_decode_attn_tables(const float *q, int32_t H_q, const mp_index *idx,
@@ -527,9 +548,13 @@ mp_status mp_index_views(const mp_index *idx, const float **W, const float **mu,
 
 void mp_index_destroy(mp_index *idx)
 {
-    if (!live(idx)) return;
-    idx->magic = 0;
-    delete idx;
+    if (idx && unregister_handle(idx)) delete idx;
+}
+
+void mp_debug_fail_launches(int32_t skip, int32_t count)
+{
+    const uint64_t c = count > 0 ? uint64_t(count) : 0, k = skip > 0 && c ? uint64_t(skip) : 0;
+    g_forced_launch_failures.store(k << 32 | c, std::memory_order_relaxed);
 }
 
 const char *mp_status_str(mp_status s)

@@ -602,16 +602,10 @@ hipError_t launch_scan_gather_t(const DecodeArgs &a, hipStream_t s)
     if (slots <= 0) return hipErrorInvalidDevice;
     const int32_t cpb = ceil_div(chunks, slots);
     const dim3 grid(ceil_div(chunks, cpb));
-    if (a.ev_begin || a.ev_end) {
-        // timed entry point: the runtime stamps the events at this kernel's
-        // own start and end
-        hipExtLaunchKernelGGL(scan_gather_kernel<G, T, KP>, grid, dim3(256), 0, s,
-                              static_cast<hipEvent_t>(a.ev_begin),
-                              static_cast<hipEvent_t>(a.ev_end), 0, a, cpb);
-    } else {
-        scan_gather_kernel<G, T, KP><<<grid, 256, 0, s>>>(a, cpb);
-    }
-    return hipGetLastError();
+    // timed entry point: the runtime stamps the events at this kernel's own
+    // start and end
+    return launch_timed(scan_gather_kernel<G, T, KP>, grid, dim3(256), 0, s, a.ev_begin, a.ev_end,
+                        a, cpb);
 }
 
 template <int G, typename T>
@@ -640,22 +634,21 @@ hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s)
 {
     const int BHq = a.B * a.H_q;
     const int TB = a.K > 0 ? 64 / a.K : 64;
-    encode_query_kernel<<<dim3(ceil_div(a.L, TB), ceil_div(BHq, kQueryHeads)), 256, 0, s>>>(
-        a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
-    return hipGetLastError();
+    return launch(encode_query_kernel, dim3(ceil_div(a.L, TB), ceil_div(BHq, kQueryHeads)),
+                  dim3(256), 0, s, a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
 }
 
 hipError_t launch_merge(const DecodeArgs &a, hipStream_t s)
 {
-    const dim3 grid(a.B * a.H_kv * a.G, kD / kMergeDims);
+    const dim3 grid(a.B * a.H_kv * a.G, kD / kMergeDims), block(32 * kMergeDims);
+    const float *part = a.part;
     switch (a.G) {
-    case 1: merge_kernel<1><<<grid, 32 * kMergeDims, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
-    case 2: merge_kernel<2><<<grid, 32 * kMergeDims, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
-    case 4: merge_kernel<4><<<grid, 32 * kMergeDims, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
-    case 8: merge_kernel<8><<<grid, 32 * kMergeDims, 0, s>>>(a.part, a.n_chunks, a.H_kv, a.H_q, a.out); break;
+    case 1: return launch(merge_kernel<1>, grid, block, 0, s, part, a.n_chunks, a.H_kv, a.H_q, a.out);
+    case 2: return launch(merge_kernel<2>, grid, block, 0, s, part, a.n_chunks, a.H_kv, a.H_q, a.out);
+    case 4: return launch(merge_kernel<4>, grid, block, 0, s, part, a.n_chunks, a.H_kv, a.H_q, a.out);
+    case 8: return launch(merge_kernel<8>, grid, block, 0, s, part, a.n_chunks, a.H_kv, a.H_q, a.out);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_counts(const DecodeArgs &a, hipStream_t s)
@@ -663,21 +656,19 @@ hipError_t launch_counts(const DecodeArgs &a, hipStream_t s)
     if (!a.debug || !a.counts) return hipSuccess;
     const dim3 grid(a.B * a.H_kv * a.n_chunks);
     switch (a.G) {
-    case 1: counts_kernel<1><<<grid, 256, 0, s>>>(a); break;
-    case 2: counts_kernel<2><<<grid, 256, 0, s>>>(a); break;
-    case 4: counts_kernel<4><<<grid, 256, 0, s>>>(a); break;
-    case 8: counts_kernel<8><<<grid, 256, 0, s>>>(a); break;
+    case 1: return launch(counts_kernel<1>, grid, dim3(256), 0, s, a);
+    case 2: return launch(counts_kernel<2>, grid, dim3(256), 0, s, a);
+    case 4: return launch(counts_kernel<4>, grid, dim3(256), 0, s, a);
+    case 8: return launch(counts_kernel<8>, grid, dim3(256), 0, s, a);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_seg_compact(const DecodeArgs &a, hipStream_t s)
 {
     if (!a.debug || (!a.s_idx && !a.s_len)) return hipSuccess;
-    seg_compact_kernel<<<dim3(a.B * a.H_q), 256, 0, s>>>(a.seg_idx, a.seg_cnt, a.n_chunks, a.n,
-                                                         a.s_idx, a.s_len);
-    return hipGetLastError();
+    return launch(seg_compact_kernel, dim3(a.B * a.H_q), dim3(256), 0, s, a.seg_idx, a.seg_cnt,
+                  a.n_chunks, a.n, a.s_idx, a.s_len);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)

@@ -340,31 +340,29 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, int64_t coun
 hipError_t launch_wgen(uint64_t seed, int32_t R, int32_t R_pad, float *W, float *Wp, hipStream_t s)
 {
     const int64_t total = int64_t(R_pad) * kD;
-    wgen_kernel<<<dim3(ceil_div(total, 256)), dim3(256), 0, s>>>(seed, R, R_pad, W, Wp);
-    return hipGetLastError();
+    return launch(wgen_kernel, dim3(ceil_div(total, 256)), dim3(256), 0, s, seed, R, R_pad, W, Wp);
 }
 
 hipError_t launch_mean(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
                        int32_t nmb, double *mu_part, float *mu, double *mu64, hipStream_t s)
 {
     const dim3 grid(nmb, B * H);
-    if (dtype == MP_BF16)
-        mean_partial_kernel<uint16_t><<<grid, 256, 0, s>>>(
-            static_cast<const uint16_t *>(keys.data), keys.sb, keys.sh, keys.sn, H, n, nmb, mu_part);
-    else
-        mean_partial_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(keys.data),
-                                                        keys.sb, keys.sh, keys.sn, H, n, nmb,
-                                                        mu_part);
-    hipError_t e = hipGetLastError();
+    hipError_t e =
+        dtype == MP_BF16
+            ? launch(mean_partial_kernel<uint16_t>, grid, dim3(256), 0, s,
+                     static_cast<const uint16_t *>(keys.data), keys.sb, keys.sh, keys.sn, H, n,
+                     nmb, mu_part)
+            : launch(mean_partial_kernel<float>, grid, dim3(256), 0, s,
+                     static_cast<const float *>(keys.data), keys.sb, keys.sh, keys.sn, H, n, nmb,
+                     mu_part);
     if (e != hipSuccess) return e;
-    mean_final_kernel<<<dim3(B * H), dim3(kD), 0, s>>>(mu_part, nmb, n, mu, mu64);
-    return hipGetLastError();
+    return launch(mean_final_kernel, dim3(B * H), dim3(kD), 0, s, mu_part, nmb, n, mu, mu64);
 }
 
 hipError_t launch_wgen_extra(uint64_t seed, int32_t R, int32_t R_pad, float *wx, hipStream_t s)
 {
-    wgen_extra_kernel<<<dim3(ceil_div(R_pad, 256)), dim3(256), 0, s>>>(seed, R, R_pad, wx);
-    return hipGetLastError();
+    return launch(wgen_extra_kernel, dim3(ceil_div(R_pad, 256)), dim3(256), 0, s, seed, R, R_pad,
+                  wx);
 }
 
 hipError_t launch_lift_norms(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
@@ -372,19 +370,22 @@ hipError_t launch_lift_norms(const KVRows &keys, int32_t dtype, int32_t B, int32
                              double *xmax, double *r2, float *rnorm, hipStream_t s)
 {
     const dim3 grid(nmb, B * H);
-    if (dtype == MP_BF16)
-        lift_norm_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t *>(keys.data),
-                                                        keys.sb, keys.sh, keys.sn, H, n, n_cap,
-                                                        nmb, mu64, xx, xmax);
-    else
-        lift_norm_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(keys.data), keys.sb,
-                                                     keys.sh, keys.sn, H, n, n_cap, nmb, mu64, xx,
-                                                     xmax);
-    hipError_t e = hipGetLastError();
+    hipError_t e =
+        dtype == MP_BF16
+            ? launch(lift_norm_kernel<uint16_t>, grid, dim3(256), 0, s,
+                     static_cast<const uint16_t *>(keys.data), keys.sb, keys.sh, keys.sn, H, n,
+                     n_cap, nmb, mu64, xx, xmax)
+            : launch(lift_norm_kernel<float>, grid, dim3(256), 0, s,
+                     static_cast<const float *>(keys.data), keys.sb, keys.sh, keys.sn, H, n, n_cap,
+                     nmb, mu64, xx, xmax);
     if (e != hipSuccess) return e;
-    lift_final_kernel<<<dim3(B * H), dim3(64), 0, s>>>(xmax, nmb, r2, rnorm);
-    return hipGetLastError();
+    return launch(lift_final_kernel, dim3(B * H), dim3(64), 0, s, xmax, nmb, r2, rnorm);
 }
+
+// Dynamic LDS of encode_keys_kernel: two 512-float key tiles and two W tiles
+// of 16 NT hyperplanes x 4 floats x 4 k-steps; the largest is NT = 255
+// (K L <= 16 x 255).
+static size_t encode_keys_lds(int32_t NT) { return size_t(2) * 512 * 16 + size_t(4) * (16 * NT) * 4 * 2; }
 
 hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n,
                               int32_t nc_cap, const float *mu, const float *Wp, int32_t K,
@@ -392,32 +393,31 @@ hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int3
                               const float *wx, const double *xx, const double *r2, int32_t n_cap,
                               hipStream_t s)
 {
+    static PerDevice attr;
+    hipError_t e = attr.once([](int) {
+        const int most = int(encode_keys_lds(255));
+        hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(encode_keys_kernel<uint16_t>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, most);
+        if (r == hipSuccess)
+            r = hipFuncSetAttribute(reinterpret_cast<const void *>(encode_keys_kernel<float>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, most);
+        return r;
+    });
+    if (e != hipSuccess) return e;
     const int32_t NT = R_pad / 16;
-    const size_t shmem = size_t(2) * 512 * 16 + size_t(4) * (16 * NT) * 4 * 2;
+    const size_t shmem = encode_keys_lds(NT);
     // every 256-key block up to the end of the last chunk, so the padding
     // keys of the last chunk are written too (as zero rows)
     const int32_t nblocks = ceil_div(n, kChunk) * (kChunk / 256) - kb0;
     if (nblocks <= 0) return hipSuccess;
     const dim3 grid(nblocks, B * H);
-    hipError_t e;
-    if (dtype == MP_BF16) {
-        auto fn = encode_keys_kernel<uint16_t>;
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
-        if (e != hipSuccess) return e;
-        fn<<<grid, 256, shmem, s>>>(static_cast<const uint16_t *>(keys.data), keys.sb, keys.sh,
-                                    keys.sn, H, n, nc_cap, mu, Wp, K, L, NT, planes, kb0, wx, xx, r2,
-                                    n_cap);
-    } else {
-        auto fn = encode_keys_kernel<float>;
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
-        if (e != hipSuccess) return e;
-        fn<<<grid, 256, shmem, s>>>(static_cast<const float *>(keys.data), keys.sb, keys.sh,
-                                    keys.sn, H, n, nc_cap, mu, Wp, K, L, NT, planes, kb0, wx, xx, r2,
-                                    n_cap);
-    }
-    return hipGetLastError();
+    if (dtype == MP_BF16)
+        return launch(encode_keys_kernel<uint16_t>, grid, dim3(256), shmem, s,
+                      static_cast<const uint16_t *>(keys.data), keys.sb, keys.sh, keys.sn, H, n,
+                      nc_cap, mu, Wp, K, L, NT, planes, kb0, wx, xx, r2, n_cap);
+    return launch(encode_keys_kernel<float>, grid, dim3(256), shmem, s,
+                  static_cast<const float *>(keys.data), keys.sb, keys.sh, keys.sn, H, n, nc_cap,
+                  mu, Wp, K, L, NT, planes, kb0, wx, xx, r2, n_cap);
 }
 
 hipError_t launch_fill_u32(uint32_t *p, int64_t count, hipStream_t s)
@@ -425,8 +425,7 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t count, hipStream_t s)
     int64_t blocks = (count + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
-    fill_u32_kernel<<<dim3(uint32_t(blocks)), 256, 0, s>>>(p, count);
-    return hipGetLastError();
+    return launch(fill_u32_kernel, dim3(uint32_t(blocks)), dim3(256), 0, s, p, count);
 }
 
 }  // namespace mp

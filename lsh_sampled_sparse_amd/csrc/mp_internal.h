@@ -1,10 +1,18 @@
 // mp_internal.h -- types and launchers shared by the HIP sources of libmagicpig.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+#include <tuple>
+#include <utility>
+
 #include "../../include/magicpig.h"
+#include "../../include/magicpig_bench.h"
+#include "../../include/magicpig_testing.h"
 
 namespace mp {
 
@@ -12,10 +20,87 @@ constexpr int kD = 128;            // head dimension
 constexpr int kChunk = MP_CHUNK;   // keys per scan chunk: 64 lanes x 8 keys
 constexpr int kWords = kChunk / 32;   // 32-key words per chunk and plane row
 constexpr int kMeanRows = 1024;    // keys per partial-sum block of the mean pass
-constexpr uint64_t kMagic = 0x4D50494458303031ULL;  // "MPIDX001"
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 inline int32_t ceil_div(int64_t a, int64_t b) { return int32_t((a + b - 1) / b); }
+
+// ---- kernel launches that report their own status ----
+// Launches fail on request of mp_debug_fail_launches (a test aid): the next
+// `skip` launches run, then each of the following `count` launches returns
+// hipErrorLaunchFailure without launching.  Both counts live in one word
+// (skip << 32 | count) so that concurrent launches take them consistently.
+extern std::atomic<uint64_t> g_forced_launch_failures;
+inline bool take_forced_failure()
+{
+    uint64_t v = g_forced_launch_failures.load(std::memory_order_relaxed);
+    for (;;) {
+        if (v == 0) return false;
+        const uint64_t skip = v >> 32, count = v & 0xFFFFFFFFu;
+        const uint64_t next = skip > 0 ? ((skip - 1) << 32 | count) : (count - 1);
+        if (g_forced_launch_failures.compare_exchange_weak(v, next, std::memory_order_relaxed))
+            return skip == 0;
+    }
+}
+
+template <typename... P, size_t... I>
+hipError_t launch_packed(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                         hipEvent_t ev0, hipEvent_t ev1, std::tuple<P...> &args,
+                         std::index_sequence<I...>)
+{
+    void *argv[sizeof...(P) + 1] = {static_cast<void *>(&std::get<I>(args))..., nullptr};
+    if (take_forced_failure()) return hipErrorLaunchFailure;
+    if (ev0 || ev1)
+        return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, lds, s,
+                                  ev0, ev1, 0);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, lds, s);
+}
+
+// kernel<<<grid, block, lds, s>>>(args...), returning the status of this
+// launch (hipLaunchKernel), not an error left behind by an earlier call.
+template <typename... P, typename... A>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                  A &&...args)
+{
+    std::tuple<P...> t(std::forward<A>(args)...);
+    return launch_packed(kernel, grid, block, lds, s, nullptr, nullptr, t,
+                         std::index_sequence_for<P...>{});
+}
+
+// The same, with two events the runtime stamps at the kernel's own start and
+// end (hipExtLaunchKernel); both NULL is a plain launch.
+template <typename... P, typename... A>
+hipError_t launch_timed(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                        hipEvent_t ev0, hipEvent_t ev1, A &&...args)
+{
+    std::tuple<P...> t(std::forward<A>(args)...);
+    return launch_packed(kernel, grid, block, lds, s, ev0, ev1, t,
+                         std::index_sequence_for<P...>{});
+}
+
+// Runs a set-up step (a kernel attribute, a symbol lookup) once per device:
+// the first call on the current device runs f(), later calls return hipSuccess
+// once it has succeeded (a failed step is tried again next time).
+class PerDevice {
+  public:
+    template <typename F> hipError_t once(F f)
+    {
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+        if (done_[dev].load(std::memory_order_acquire)) return hipSuccess;
+        std::lock_guard<std::mutex> g(m_);
+        if (done_[dev].load(std::memory_order_relaxed)) return hipSuccess;
+        e = f(dev);
+        if (e == hipSuccess) done_[dev].store(true, std::memory_order_release);
+        return e;
+    }
+    static constexpr int kMaxDevices = 64;
+
+  private:
+    std::mutex m_;
+    std::atomic<bool> done_[kMaxDevices] = {};
+};
 
 // Workspace layout of an index (all offsets 256-byte aligned).
 struct IndexLayout {
@@ -33,7 +118,6 @@ IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t 
                          int32_t n_cap = 0, int32_t flags = 0);
 
 struct mp_index_impl {
-    uint64_t magic;
     IndexLayout lay;
     uint64_t seed;
     int32_t key_dtype;
@@ -58,6 +142,9 @@ struct mp_index_impl {
 
 // Workspace layout of the bucketed tables of an index.
 constexpr int kMaxTableK = 12;   // 2^K bucket counters live in LDS while a table is built
+// Largest dynamic LDS of the bucket walk (a head's collision bitmap and its
+// bucket bounds): a workgroup's 160 KB less room for the static part.
+constexpr size_t kCollideLdsMax = 160 * 1024 - 1024;
 struct TablesLayout {
     int32_t nbins;
     int64_t off_offsets, off_entries, total;
@@ -69,8 +156,9 @@ struct DecodeLayout {
     int32_t BHq, n_chunks;
     int64_t off_qcodes, off_qq, off_qnorm, off_part, off_seg_idx, off_seg_cnt, off_bits, total;
 };
-// `tables`: also the per-head collision bitmaps of the bucketed-table path.
-DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables = false);
+// `tables`: also the per-head collision bitmaps of the bucketed-table path;
+// `debug`: also the per-chunk sampled lists of the debug entry points.
+DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables, bool debug);
 
 // Row addressing of a [B][H][n][128] view.
 struct KVRows {
@@ -129,6 +217,16 @@ struct DecodeArgs {
     hipEvent_t ev_begin, ev_end;   // optional, recorded around scan_gather
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+// Records the failure detail for mp_last_error and returns s.
+mp_status fail(mp_status s, const char *fmt, ...);
+// Validation and launch of every decode entry point (scratch laid out by
+// decode_layout(..., tables, debug)).
+mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx, const mp_kv_view *k,
+                        const mp_kv_view *v, int32_t n_sink, int32_t n_local, float scale,
+                        float *out, void *scratch, size_t scratch_bytes, void *stream, bool debug,
+                        uint16_t *qcodes, uint8_t *counts, int32_t *s_idx, int32_t *s_len,
+                        void *ev_begin, void *ev_end, bool tables);
 hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_counts(const DecodeArgs &a, hipStream_t s);

@@ -37,7 +37,8 @@ extern "C" mp_status mp_stream_read(const void *data, int64_t bytes, uint32_t *s
 {
     if (!data || !sink || bytes < 16 || blocks < 1 || (reinterpret_cast<uintptr_t>(data) & 15))
         return MP_E_ARG;
-    stream_read_kernel<<<dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const uint4 *>(data), bytes / 16, sink);
-    return hipGetLastError() == hipSuccess ? MP_OK : MP_E_HIP;
+    return launch(stream_read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                  static_cast<const uint4 *>(data), bytes / 16, sink) == hipSuccess
+               ? MP_OK
+               : MP_E_HIP;
 }

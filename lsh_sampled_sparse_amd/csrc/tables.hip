@@ -347,14 +347,8 @@ template <int G, typename T>
 hipError_t launch_table_gather_t(const DecodeArgs &a, int32_t nwords, hipStream_t s)
 {
     const dim3 grid(a.B * a.H_kv * a.n_chunks);
-    if (a.ev_begin || a.ev_end) {
-        hipExtLaunchKernelGGL(table_gather_kernel<G, T>, grid, dim3(256), 0, s,
-                              static_cast<hipEvent_t>(a.ev_begin),
-                              static_cast<hipEvent_t>(a.ev_end), 0, a, nwords);
-    } else {
-        table_gather_kernel<G, T><<<grid, 256, 0, s>>>(a, nwords);
-    }
-    return hipGetLastError();
+    return launch_timed(table_gather_kernel<G, T>, grid, dim3(256), 0, s, a.ev_begin, a.ev_end, a,
+                        nwords);
 }
 
 template <int G>
@@ -374,31 +368,42 @@ size_t collide_lds_bytes(const IndexLayout &lay)
     return size_t(lay.n_pad / 16) * 4 + size_t(2 * lay.L + 1) * 4;
 }
 
+// Dynamic LDS of build_tables_kernel: 3 x 2^K bucket words and the staged tile.
+static size_t build_tables_lds(int K) { return (size_t(3) * (size_t(1) << K) + kStageTile) * 4; }
+
 hipError_t launch_build_tables(const mp_index_impl &idx, hipStream_t s)
 {
+    static PerDevice attr;
+    hipError_t e = attr.once([](int) {
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(build_tables_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   int(build_tables_lds(kMaxTableK)));
+    });
+    if (e != hipSuccess) return e;
     const IndexLayout &lay = idx.lay;
     const int nbins = 1 << lay.K;
-    const size_t lds = (size_t(3) * nbins + kStageTile) * 4;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(build_tables_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-    build_tables_kernel<<<dim3(lay.B * lay.H_kv * lay.L), kBuildThreads, lds, s>>>(
-        idx.planes, lay.n, lay.nc_cap, lay.L, lay.K, lay.Kr, nbins, idx.tab_off, idx.tab_ent);
-    return hipGetLastError();
+    return launch(build_tables_kernel, dim3(lay.B * lay.H_kv * lay.L), dim3(kBuildThreads),
+                  build_tables_lds(lay.K), s, static_cast<const uint32_t *>(idx.planes), lay.n,
+                  lay.nc_cap, lay.L, lay.K, lay.Kr, nbins, idx.tab_off, idx.tab_ent);
 }
 
 hipError_t launch_decode_tables(const DecodeArgs &a, hipStream_t s)
 {
     hipError_t e = launch_encode_query(a, s);
     if (e != hipSuccess) return e;
+    static PerDevice attr;
+    e = attr.once([](int) {
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(collide_kernel),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, int(kCollideLdsMax));
+    });
+    if (e != hipSuccess) return e;
     const int32_t n_pad = a.n_chunks * kChunk, nwords = n_pad / 16;
     const size_t lds = size_t(nwords) * 4 + size_t(2 * a.L + 1) * 4;   // bounds any slice
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(collide_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    e = launch(collide_kernel, dim3(a.B * a.H_q * kSlices), dim3(kBuildThreads), lds, s,
+               static_cast<const uint16_t *>(a.qcodes), static_cast<const uint32_t *>(a.tab_off),
+               static_cast<const uint32_t *>(a.tab_ent), a.H_q, a.H_kv, a.n, nwords, a.L,
+               1 << a.K, a.bits);
     if (e != hipSuccess) return e;
-    collide_kernel<<<dim3(a.B * a.H_q * kSlices), kBuildThreads, lds, s>>>(
-        a.qcodes, a.tab_off, a.tab_ent, a.H_q, a.H_kv, a.n, nwords, a.L, 1 << a.K, a.bits);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     switch (a.G) {
     case 1: e = launch_table_gather<1>(a, nwords, s); break;
     case 2: e = launch_table_gather<2>(a, nwords, s); break;
