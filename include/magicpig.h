@@ -184,6 +184,25 @@ mp_status mp_decode_attn(const float *q, int32_t H_q, const mp_index *idx,
                          int32_t n_sink, int32_t n_local, float scale, float *out,
                          void *scratch, size_t scratch_bytes, void *stream);
 
+/* Bytes of the static device array behind mp_decode_attn_noalloc. */
+#define MP_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* mp_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * It takes no scratch argument: its scratch is a static device array of the
+ * library, MP_NOALLOC_SCRATCH_BYTES (32 MiB) on each GPU it runs on, held
+ * from the library's load until the process ends; the call itself allocates
+ * nothing.  Arguments, layouts and the output are those of mp_decode_attn
+ * (the same kernels, bit-identical results).  The scratch it needs, 256-byte
+ * aligned pieces of B*H_q*L*2 + B*H_q*L*4 + B*H_q*4 + B*H_q*ceil(n/512)*130*4
+ * bytes (query codes, their packed form, norms, chunk partials), must fit the
+ * array: MP_E_WORKSPACE otherwise, before anything is enqueued.  All calls on
+ * one GPU share that GPU's array, so calls that overlap on one GPU (other
+ * streams or threads) race; order them on one stream. */
+mp_status mp_decode_attn_noalloc(const float *q, int32_t H_q, const mp_index *idx,
+                                 const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
+                                 int32_t n_local, float scale, float *out, void *stream);
+
 /* mp_decode_attn plus the intermediate results, each optional (NULL = skip):
  *   qcodes [B][H_q][L] uint16     query codes
  *   counts [B][H_q][n] uint8      tables in which key i shares the query's bucket

@@ -7,7 +7,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmagicpig.so")
-SOURCES = ["api.hip", "index_build.hip", "decode.hip", "tables.hip", "probe.hip"]
+SOURCES = ["api.hip", "index_build.hip", "decode.hip", "tables.hip", "probe.hip", "noalloc.hip"]
 ARCH = os.environ.get("MP_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -254,6 +254,12 @@ mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx, const 
     return MP_OK;
 }
 
+int64_t decode_scratch_needed(const mp_index *idx, int32_t H_q)
+{
+    if (!live(idx) || H_q < 1 || H_q % idx->lay.H_kv) return -1;
+    return decode_layout(idx->lay, H_q, false, false).total;
+}
+
 }  // namespace mp
 
 using namespace mp;

@@ -227,6 +227,9 @@ mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx, const 
                         float *out, void *scratch, size_t scratch_bytes, void *stream, bool debug,
                         uint16_t *qcodes, uint8_t *counts, int32_t *s_idx, int32_t *s_len,
                         void *ev_begin, void *ev_end, bool tables);
+// Scratch bytes of a code-scan decode without the debug lists, or -1 for a
+// dead handle or an H_q that does not fit the index.
+int64_t decode_scratch_needed(const mp_index *idx, int32_t H_q);
 hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_counts(const DecodeArgs &a, hipStream_t s);
