@@ -61,13 +61,22 @@ def test_stale_hip_error_is_not_this_calls():
     hip = C.CDLL("libamdhip64.so")
     hip.hipSetDevice.restype = C.c_int
     hip.hipGetLastError.restype = C.c_int
+    out = torch.empty_like(q)
+    scr = torch.empty(idx.scratch_bytes(8), dtype=torch.uint8, device=DEV)
+    kv_k, kv_v = mp.kv_view(k), mp.kv_view(v)
+    sh = int(torch.cuda.current_stream().cuda_stream)
+    planted = hip.hipSetDevice(9999)                    # leaves hipErrorInvalidDevice behind
     try:
-        assert hip.hipSetDevice(9999) != 0              # leaves hipErrorInvalidDevice behind
-        out = mp.decode_attn(q, idx, k, v, 4, 64)       # must not report it as its own
-        torch.cuda.synchronize()
-        assert torch.equal(out, ref)
+        assert planted != 0
+        # must not report the planted error as its own (and no torch call in
+        # between, since torch's launch checks would pick it up)
+        mp.capi.mp_decode_attn(q.data_ptr(), 8, idx.handle, kv_k, kv_v, 4, 64, 0.0,
+                               out.data_ptr(), scr.data_ptr(), scr.numel(), sh)
     finally:
-        hip.hipGetLastError()                           # clear it for torch's own checks
+        pending = hip.hipGetLastError()                 # clear it for torch's own checks
+    assert pending == planted                           # it was still there, untouched
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
 
 
 def test_destroyed_handle_is_refused():
