@@ -333,6 +333,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--config", default="llama8b_96k")
     ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--kv-layout", choices=("token", "separate"), default="separate",
+                    help="token: each token's K and V rows side by side ([B][H][n][2][128], "
+                         "a sampled key is one 512-byte read); separate: K and V as two "
+                         "[B][H][n][128] tensors")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tables", action="store_true",
                     help="skip the bucketed-table leg")
@@ -373,6 +377,11 @@ def main():
         inp = synth.config_inputs(cfg, layer=l, device=dev)
         k, v, q = inp["k"], inp["v"], inp["q"].contiguous()
         del inp
+        if args.kv_layout == "token":
+            kv = torch.empty(cfg.B, cfg.H_kv, cfg.n, 2, cfg.d, dtype=k.dtype, device=dev)
+            kv[:, :, :, 0].copy_(k)
+            kv[:, :, :, 1].copy_(v)
+            k, v = kv[:, :, :, 0], kv[:, :, :, 1]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         idx = mp.build_index(k, cfg.K, cfg.L, cfg.hyperplane_seed(l))

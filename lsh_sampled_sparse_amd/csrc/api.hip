@@ -219,6 +219,8 @@ mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx, const 
     a.n_sink = n_sink;
     a.n_local = n_local;
     a.scale = scale > 0.0f ? scale : 1.0f / sqrtf(float(kD));
+    for (int i = 3; i <= 7; ++i)
+        a.ucoef[i - 3] = lay.L - i + 1 > 0 ? float(lay.L - i + 1) / float(i) : 0.0f;
     a.W = idx->W;
     a.mu = idx->mu;
     a.rnorm = idx->rnorm;

@@ -86,13 +86,15 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 // log u for u = P[at least 2 of L tables collide], P = p^K (fp32).
 // Closed form 1 - (1-P)^L - L P (1-P)^(L-1) where L*P > 0.05; below that the
 // two subtractions cancel, so u is the binomial tail
-//   C(L,2) P^2 (1-P)^(L-2) * (1 + sum_{j>=3} prod_{i=2}^{j-1} (L-i)/(i+1) P/(1-P))
-// taken in logs.  p is floored at 1e-30: p = 0 only for an exactly
-// anti-parallel centered key, which cannot collide in exact arithmetic.
-// Plain logs and exponentials use the hardware log2/exp2 (about 1 ulp);
-// log1p(-P) and the expm1 of the closed form, which carry the cancellation,
-// use the full-precision routines.
-__device__ __forceinline__ float log_u_f32(float p, int K, int L)
+//   C(L,2) P^2 (1-P)^(L-2) (1 + c3 r (1 + c4 r (1 + c5 r (1 + c6 r (1 + c7 r))))),
+//   r = P/(1-P), c_i = (L-i+1)/i (uc[i-3], from the host; 0 past L),
+// taken in logs.  There c_i r <= L P / 3 <= 0.0175 for every i, so the terms
+// left out after i = 7 add less than 2e-10 relative: far below fp32.  p is
+// floored at 1e-30: p = 0 only for an exactly anti-parallel centered key,
+// which cannot collide in exact arithmetic.  Plain logs and exponentials use
+// the hardware log2/exp2 (about 1 ulp); log1p(-P) and the expm1 of the
+// closed form, which carry the cancellation, use the full-precision routines.
+__device__ __forceinline__ float log_u_f32(float p, int K, int L, const float *uc)
 {
     if (K == 0) return 0.0f;
     p = fminf(fmaxf(p, 1e-30f), 1.0f);
@@ -106,12 +108,11 @@ __device__ __forceinline__ float log_u_f32(float p, int K, int L)
         return __logf(u);
     }
     const float r = P / (1.0f - P);
-    float term = 1.0f, rest = 0.0f;
-    for (int j = 2; j < L; ++j) {
-        term *= float(L - j) / float(j + 1) * r;
-        rest += term;
-        if (term < 1e-9f * (1.0f + rest)) break;
-    }
+    float f = fmaf(uc[4] * r, 1.0f, 1.0f);
+    f = fmaf(uc[3] * r, f, 1.0f);
+    f = fmaf(uc[2] * r, f, 1.0f);
+    f = fmaf(uc[1] * r, f, 1.0f);
+    const float rest = uc[0] * r * f;   // the tail after the j = 2 term, relative to it
     return __logf(0.5f * float(L) * float(L - 1)) + 2.0f * logP + float(L - 2) * a + log1pf(rest);
 }
 
@@ -350,7 +351,7 @@ __device__ __forceinline__ void gather_z(const DecodeArgs &a, GatherLds<G, T> &s
                     float cs = den > 0.0f ? (s.srow[e][g] - sqn[G + g]) / den : 0.0f;
                     cs = fminf(fmaxf(cs, -1.0f), 1.0f);
                     const float pc = 1.0f - acos_over_pi(cs);
-                    z -= log_u_f32(pc, a.K, a.L);
+                    z -= log_u_f32(pc, a.K, a.L, a.ucoef);
                 }
             }
             s.sz[e][g] = z;

@@ -194,6 +194,7 @@ struct DecodeArgs {
     int32_t nc_cap;          // plane chunks per unit (units are this far apart)
     int32_t n_sink, n_local;
     float scale;
+    float ucoef[5];          // (L - i + 1) / i for i = 3..7 (0 past L): the binomial tail of log u
     const float *W;          // [R][128]
     const float *mu;         // [B*H_kv][128]
     const float *rnorm;      // [B*H_kv] lift radius r (lifted index) or NULL
