@@ -143,42 +143,90 @@ def union_rows_of(cfg, res, device):
     return int(mask.sum()), float(s_len.float().mean())
 
 
+def cpu_info() -> dict:
+    """The host's CPU model and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(cfg, k, v, q, seed, threads):
-    """The fp64 oracle, as it stands, on KV head 0 of sequence 0 and its G
-    query heads (one of B*H_kv identical units), single-threaded decode;
-    the oracle's own index build for that head is timed apart."""
+    """The fp64 oracle, as it stands, timed on the host on one layer of the
+    workload: decode on one thread (one (sequence, KV head) unit with its G
+    query heads, scaled by the number of units) and on `threads` threads
+    (every (unit, query head) of the layer, one task each); the oracle's own
+    index build (hyperplanes, mean, key codes) of one unit timed apart on
+    `threads` threads and scaled to the layer."""
+    from concurrent.futures import ThreadPoolExecutor
     import numpy as np
     import oracle
     G = cfg.H_q // cfg.H_kv
-    kh = k[0, 0].cpu().double().numpy()
-    vh = v[0, 0].cpu().double().numpy()
-    qh = q[0, :G].cpu().double().numpy()
+    units = [(b, h) for b in range(cfg.B) for h in range(cfg.H_kv)]
     t0 = time.perf_counter()
     W = oracle.hyperplanes(seed, cfg.K * cfg.L, cfg.d)
-    mu = oracle.mean(kh)
-    codes, _ = oracle.encode_keys_parallel(kh, W, cfg.K, cfg.L, mu, threads=threads)
+    k0 = k[0, 0].cpu().double().numpy()
+    mu0 = oracle.mean(k0)
+    codes0, _ = oracle.encode_keys_parallel(k0, W, cfg.K, cfg.L, mu0, threads=threads)
     t_build = time.perf_counter() - t0
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
+    # host copies of every unit (fp64) and the oracle's codes of each: the
+    # codes of unit 0 stand in for the others' in the decode timing (same
+    # sizes, same work)
+    kh = [k[b, h].cpu().double().numpy() for b, h in units]
+    vh = [v[b, h].cpu().double().numpy() for b, h in units]
+    mus = [oracle.mean(x) for x in kh]
+    qh = [q[b].cpu().double().numpy() for b in range(cfg.B)]
+
+    def head(task):
+        u, g = task
+        b, h = units[u]
+        qq = qh[b][h * G + g]
+        qc, _ = oracle.encode(qq, W, cfg.K, cfg.L)
+        S = oracle.select(oracle.collision_counts(codes0, qc), cfg.n_sink, cfg.n_local)
+        oracle.estimate(qq, kh[u], vh[u], mus[u], S, cfg.K, cfg.L, cfg.n_sink, cfg.n_local)
+
+    reps, t0 = 0, time.perf_counter()
+    while True:                       # one thread: unit 0, its G heads
         for g in range(G):
-            qc, _ = oracle.encode(qh[g], W, cfg.K, cfg.L)
-            cnt = oracle.collision_counts(codes, qc)
-            S = oracle.select(cnt, cfg.n_sink, cfg.n_local)
-            oracle.estimate(qh[g], kh, vh, mu, S, cfg.K, cfg.L, cfg.n_sink, cfg.n_local)
+            head((0, g))
         reps += 1
-        el = time.perf_counter() - t0
-        if el > 8.0 or reps >= 50:
+        el1 = time.perf_counter() - t0
+        if el1 > 6.0 or reps >= 50:
             break
-    t_unit = el / reps
-    units = cfg.B * cfg.H_kv
-    return {"value": 1.0 / (t_unit * units), "unit": "decode layer-steps/s", "cores": 1,
+    t_unit1 = el1 / reps
+    tasks = [(u, g) for u in range(len(units)) for g in range(G)]
+    used = min(threads, len(tasks))
+    steps, t0 = 0, time.perf_counter()
+    with ThreadPoolExecutor(used) as ex:   # ctypes drops the GIL in the oracle
+        while True:
+            list(ex.map(head, tasks))
+            steps += 1
+            elN = time.perf_counter() - t0
+            if elN > 6.0 or steps >= 50:
+                break
+    info = cpu_info()
+    return {"value": round(steps / elN, 4), "unit": "decode layer-steps/s", "cores": used,
             "kind": "oracle",
-            "sample": (f"KV head 0 of sequence 0 with its {G} query heads = 1 of {units} "
-                       f"identical units of one layer, decode repeated {reps}x "
-                       f"({t_unit * 1e3:.1f} ms per unit), scaled by {units}; the oracle's "
-                       f"index build of that head took {t_build:.1f} s on {threads} threads "
-                       "and is excluded, as on the GPU")}
+            "sample": (f"one layer of {cfg.name}: every one of the {len(tasks)} (KV unit, query "
+                       f"head) decodes on {used} threads, {steps} layer-steps; the key codes of "
+                       "unit 0 serve every unit (same sizes and work)"),
+            "single_thread": {"value": round(1.0 / (t_unit1 * len(units)), 4),
+                              "unit": "decode layer-steps/s", "cores": 1,
+                              "sample": (f"unit 0 with its {G} query heads, {reps} times "
+                                         f"({t_unit1 * 1e3:.1f} ms each), scaled by the "
+                                         f"{len(units)} units")},
+            "index_build_s_per_layer": round(t_build * len(units), 3),
+            "index_build_sample": (f"hyperplanes, mean and key codes of unit 0 "
+                                   f"({cfg.n} keys) on {threads} threads: {t_build:.2f} s, "
+                                   f"scaled by the {len(units)} units"),
+            **info}
 
 
 def time_steps(step, warmup, steps):
@@ -210,61 +258,144 @@ def time_steps(step, warmup, steps):
     return total_ms, wall, [ev_b[i].elapsed_time(ev_e[i]) for i in range(steps)]
 
 
-def tables_leg(args, cfg, state, layers, sh):
+def measure_workload(cfg, layers, steps, warmup, dev, sh, tables=True, kv_layout="separate",
+                     log=None):
+    """Times `steps` decode steps of one workload on both paths, cycling
+    `layers` seeded layers (each with its own index and caches) so that the
+    code planes and rows come from HBM.  Returns (scan, tables, state) where
+    scan/tables hold the step rate, the dominant kernel's roofline and the
+    algorithmic bytes; state keeps layer 0's tensors for the CPU baseline."""
+    import torch
+    import lsh_sampled_sparse_amd as mp
+    from lsh_sampled_sparse_amd import capi
+    import synth
+    state, build_ms = [], []
+    for l in range(layers):
+        inp = synth.config_inputs(cfg, layer=l, device=dev)
+        k, v, q = inp["k"], inp["v"], inp["q"].contiguous()
+        del inp
+        if kv_layout == "token":
+            kv = torch.empty(cfg.B, cfg.H_kv, cfg.n, 2, cfg.d, dtype=k.dtype, device=dev)
+            kv[:, :, :, 0].copy_(k)
+            kv[:, :, :, 1].copy_(v)
+            k, v = kv[:, :, :, 0], kv[:, :, :, 1]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        idx = mp.build_index(k, cfg.K, cfg.L, cfg.hyperplane_seed(l))
+        e1.record()
+        torch.cuda.synchronize()
+        build_ms.append(e0.elapsed_time(e1))
+        scratch = torch.empty(idx.scratch_bytes(cfg.H_q), dtype=torch.uint8, device=dev)
+        res = mp.decode_debug(q, idx, k, v, cfg.n_sink, cfg.n_local, scratch=scratch)
+        u, mS = union_rows_of(cfg, res, dev)
+        del res
+        state.append(dict(k=k, v=v, q=q, idx=idx, scratch=scratch, out=torch.empty_like(q),
+                          kv_k=mp.kv_view(k), kv_v=mp.kv_view(v), union=u, mean_S=mS))
+        if log:
+            log(f"{cfg.name} layer {l}: build {build_ms[-1]:.2f} ms, mean |S| {mS:.0f}, "
+                f"union rows {u}")
+
+    def step(i, eb=None, ee=None):
+        st = state[i % layers]
+        args = (st["q"].data_ptr(), cfg.H_q, st["idx"].handle, st["kv_k"], st["kv_v"],
+                cfg.n_sink, cfg.n_local, 0.0, st["out"].data_ptr(), st["scratch"].data_ptr(),
+                st["scratch"].numel(), sh)
+        if eb is None:
+            capi.mp_decode_attn(*args)
+        else:
+            capi.mp_decode_attn_timed(*args, eb, ee)
+
+    total_ms, wall, scan_ms = time_steps(step, warmup, steps)
+    lay = [(warmup + i) % layers for i in range(steps)]
+    scan_bytes = sum(scan_bytes_per_launch(cfg, state[l]["union"]) for l in lay)
+    dec_bytes = sum(decode_bytes_per_step(cfg, state[l]["union"]) for l in lay)
+    scan_gbs = scan_bytes / (sum(scan_ms) / 1e3) / 1e9
+    dec_gbs = dec_bytes / (total_ms / 1e3) / 1e9
+    value = steps / (total_ms / 1e3)
+    flops_build = 2.0 * cfg.B * cfg.H_kv * cfg.n * cfg.d * cfg.K * cfg.L
+    build_avg = sum(build_ms[1:]) / (len(build_ms) - 1) if len(build_ms) > 1 else build_ms[0]
+    scan = {
+        "value": round(value, 2), "unit": "decode layer-steps/s",
+        "ms_per_step": round(total_ms / steps, 5),
+        "wall_ms_per_step": round(wall * 1e3 / steps, 5),
+        "keys_scanned_per_s": round(cfg.B * cfg.H_kv * cfg.n * value, 1),
+        "hbm_gbps_decode": round(dec_gbs, 1),
+        "pct_hbm_peak_decode": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
+        "mean_S_per_head": round(sum(st["mean_S"] for st in state) / layers, 1),
+        "mean_union_rows_per_layer": round(sum(st["union"] for st in state) / layers, 1),
+        "roofline": {"kernel": "scan_gather", "bound": "hbm", "achieved": round(scan_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": (measured_traffic("scan_gather")
+                                 if cfg.name == "llama8b_96k" else None),
+                     "avg_launch_us": round(sum(scan_ms) / len(scan_ms) * 1e3, 3),
+                     "algorithmic_bytes_per_launch": round(scan_bytes / steps)},
+        "index_build": {"ms_per_layer": round(build_avg, 3),
+                        "tflops_fp32_mfma": round(flops_build / (build_avg / 1e3) / 1e12, 2),
+                        "frac_fp32_mfma_peak": round(flops_build / (build_avg / 1e3) / 1e12
+                                                     / FP32_MFMA_PEAK_TFLOPS, 4)},
+        "layers_cycled": layers, "steps": steps,
+    }
+    tab = None
+    if tables and capi.mp_tables_workspace_bytes(state[0]["idx"].handle) > 0:
+        tab = tables_leg(cfg, state, layers, steps, warmup, sh, dev)
+        tab["vs_code_scan"] = round(tab["value"] / value, 3)
+    return scan, tab, state
+
+
+def tables_leg(cfg, state, layers, steps, warmup, sh, dev):
     """The bucketed-table path over the same layers and steps."""
     import torch
     import lsh_sampled_sparse_amd as mp
     from lsh_sampled_sparse_amd import capi
-    build_ms, entries, tscr = [], [], []
-    for l in range(layers):
-        k, v, q, idx = state[l][:4]
+    build_ms, entries = [], []
+    for st in state:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        mp.build_tables(idx)
+        mp.build_tables(st["idx"])
         e1.record()
         torch.cuda.synchronize()
         build_ms.append(e0.elapsed_time(e1))
-        scr = torch.empty(idx.scratch_bytes(cfg.H_q, tables=True), dtype=torch.uint8,
-                          device=q.device)
-        res = mp.decode_tables_debug(q, idx, k, v, cfg.n_sink, cfg.n_local, scratch=scr)
-        entries.append(bucket_entries_of(cfg, idx, res["qcodes"]))
+        st["tscratch"] = torch.empty(st["idx"].scratch_bytes(cfg.H_q, tables=True),
+                                     dtype=torch.uint8, device=dev)
+        res = mp.decode_tables_debug(st["q"], st["idx"], st["k"], st["v"], cfg.n_sink,
+                                     cfg.n_local, scratch=st["tscratch"])
+        entries.append(bucket_entries_of(cfg, st["idx"], res["qcodes"]))
         del res
-        tscr.append(scr)
 
     def step(i, eb=None, ee=None):
-        _, _, q, idx, _, out, kv_k, kv_v, _ = state[i % layers]
-        scr = tscr[i % layers]
+        st = state[i % layers]
+        args = (st["q"].data_ptr(), cfg.H_q, st["idx"].handle, st["kv_k"], st["kv_v"],
+                cfg.n_sink, cfg.n_local, 0.0, st["out"].data_ptr(), st["tscratch"].data_ptr(),
+                st["tscratch"].numel(), sh)
         if eb is None:
-            capi.mp_decode_attn_tables(q.data_ptr(), cfg.H_q, idx.handle, kv_k, kv_v,
-                                       cfg.n_sink, cfg.n_local, 0.0, out.data_ptr(),
-                                       scr.data_ptr(), scr.numel(), sh)
+            capi.mp_decode_attn_tables(*args)
         else:
-            capi.mp_decode_attn_tables_timed(q.data_ptr(), cfg.H_q, idx.handle, kv_k, kv_v,
-                                             cfg.n_sink, cfg.n_local, 0.0, out.data_ptr(),
-                                             scr.data_ptr(), scr.numel(), sh, eb, ee)
+            capi.mp_decode_attn_tables_timed(*args, eb, ee)
 
-    total_ms, wall, g_ms = time_steps(step, args.warmup, args.steps)
-    lay = [(args.warmup + i) % layers for i in range(args.steps)]
-    g_bytes = sum(table_gather_bytes_per_launch(cfg, state[l][8]) for l in lay)
+    total_ms, wall, g_ms = time_steps(step, warmup, steps)
+    lay = [(warmup + i) % layers for i in range(steps)]
+    g_bytes = sum(table_gather_bytes_per_launch(cfg, state[l]["union"]) for l in lay)
     g_gbs = g_bytes / (sum(g_ms) / 1e3) / 1e9
-    value = args.steps / (total_ms / 1e3)
+    value = steps / (total_ms / 1e3)
     build_avg = (sum(build_ms[1:]) / (len(build_ms) - 1)) if len(build_ms) > 1 else build_ms[0]
-    n_units = cfg.B * cfg.H_kv * cfg.L
     return {
         "value": round(value, 2), "unit": "decode layer-steps/s",
-        "ms_per_step": round(total_ms / args.steps, 5),
+        "ms_per_step": round(total_ms / steps, 5),
         "vs_code_scan": None,
         "mean_bucket_entries_per_head_table": round(
             sum(entries) / len(entries) / (cfg.B * cfg.H_q * cfg.L), 1),
         "roofline": {"kernel": "table_gather", "bound": "hbm", "achieved": round(g_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(g_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("table_gather"),
+                     "traffic": (measured_traffic("table_gather")
+                                 if cfg.name == "llama8b_96k" else None),
                      "avg_launch_us": round(sum(g_ms) / len(g_ms) * 1e3, 3),
-                     "algorithmic_bytes_per_launch": round(g_bytes / args.steps)},
+                     "algorithmic_bytes_per_launch": round(g_bytes / steps)},
         "table_build": {"ms_per_layer": round(build_avg, 3),
-                        "entries_per_layer": n_units * cfg.n,
-                        "workspace_bytes_per_layer": int(state[0][3].tables.numel())},
+                        "entries_per_layer": cfg.B * cfg.H_kv * cfg.L * cfg.n,
+                        "workspace_bytes_per_layer": int(state[0]["idx"].tables.numel()),
+                        "ms_per_step_with_rebuild": round(total_ms / steps + build_avg, 4)},
     }
 
 
@@ -326,6 +457,11 @@ def estimator_error_256k(device) -> dict:
     return res
 
 
+# The other workloads: (layers cycled, steps); together they cover a few
+# hundred MB to a few GB per step, far beyond the 256 MB last-level cache.
+OTHER_WORKLOADS = {"llama8b_16k": (16, 160), "batch16_32k": (2, 40), "llama70b_256k": (2, 40)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,9 +476,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tables", action="store_true",
                     help="skip the bucketed-table leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 16K, batch-16 and 256K workloads")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the streaming-read reference and the 256K estimator-error sweep")
-    ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--cpu-threads", type=int,
+                    default=int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or 16)
     ap.add_argument("--source-hashes", action="store_true",
                     help="print the source hash of each timed kernel and exit")
     ap.add_argument("--calib-copy", action="store_true",
@@ -359,56 +498,16 @@ def main():
         sys.exit(2)
 
     import torch
-    import lsh_sampled_sparse_amd as mp
-    from lsh_sampled_sparse_amd import capi
     import synth
 
     cfg = synth.CONFIGS[args.config]
     layers = args.layers or cfg.layers
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
-    sh = int(stream.cuda_stream)
+    sh = int(torch.cuda.current_stream().cuda_stream)
 
-    state = []
-    build_ms = []
-    union_rows, mean_S = [], []
-    for l in range(layers):
-        inp = synth.config_inputs(cfg, layer=l, device=dev)
-        k, v, q = inp["k"], inp["v"], inp["q"].contiguous()
-        del inp
-        if args.kv_layout == "token":
-            kv = torch.empty(cfg.B, cfg.H_kv, cfg.n, 2, cfg.d, dtype=k.dtype, device=dev)
-            kv[:, :, :, 0].copy_(k)
-            kv[:, :, :, 1].copy_(v)
-            k, v = kv[:, :, :, 0], kv[:, :, :, 1]
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        idx = mp.build_index(k, cfg.K, cfg.L, cfg.hyperplane_seed(l))
-        e1.record()
-        torch.cuda.synchronize()
-        build_ms.append(e0.elapsed_time(e1))
-        scratch = torch.empty(idx.scratch_bytes(cfg.H_q), dtype=torch.uint8, device=dev)
-        out = torch.empty_like(q)
-        res = mp.decode_debug(q, idx, k, v, cfg.n_sink, cfg.n_local, scratch=scratch)
-        u, s = union_rows_of(cfg, res, dev)
-        del res
-        union_rows.append(u)
-        mean_S.append(s)
-        state.append((k, v, q, idx, scratch, out, mp.kv_view(k), mp.kv_view(v), u))
-        print(f"layer {l}: build {build_ms[-1]:.2f} ms, mean |S| {s:.0f}, union rows {u}",
-              file=sys.stderr, flush=True)
-
-    def step(i, eb=None, ee=None):
-        k, v, q, idx, scratch, out, kv_k, kv_v, _ = state[i % layers]
-        if eb is None:
-            capi.mp_decode_attn(q.data_ptr(), cfg.H_q, idx.handle, kv_k, kv_v, cfg.n_sink,
-                                cfg.n_local, 0.0, out.data_ptr(), scratch.data_ptr(),
-                                scratch.numel(), sh)
-        else:
-            capi.mp_decode_attn_timed(q.data_ptr(), cfg.H_q, idx.handle, kv_k, kv_v,
-                                      cfg.n_sink, cfg.n_local, 0.0, out.data_ptr(),
-                                      scratch.data_ptr(), scratch.numel(), sh, eb, ee)
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
 
     if args.calib_copy:
         # A kernel of known traffic for scaling hardware byte counters: an fp32
@@ -421,48 +520,50 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # Timed region: the production call, K steps cycling the layers; then the
-    # same steps through the timed entry point, whose HIP events on the launch
-    # stream sit right around the scan + gather kernel.
-    total_ms, wall, scan_ms = time_steps(step, args.warmup, args.steps)
-
-    lay = [(args.warmup + i) % layers for i in range(args.steps)]
-    scan_bytes = sum(scan_bytes_per_launch(cfg, union_rows[l]) for l in lay)
-    dec_bytes = sum(decode_bytes_per_step(cfg, union_rows[l]) for l in lay)
-    ms_per_step = total_ms / args.steps
-    value = args.steps / (total_ms / 1e3)
-    scan_avg_ms = sum(scan_ms) / len(scan_ms)
-    scan_gbs = scan_bytes / (sum(scan_ms) / 1e3) / 1e9
-    dec_gbs = dec_bytes / (total_ms / 1e3) / 1e9
-    flops_build = 2.0 * cfg.B * cfg.H_kv * cfg.n * cfg.d * cfg.K * cfg.L
-    build_avg = sum(build_ms[1:]) / max(1, len(build_ms) - 1) if len(build_ms) > 1 else build_ms[0]
-
-    tables = None
-    if not args.no_tables:
-        tables = tables_leg(args, cfg, state, layers, sh)
-        tables["vs_code_scan"] = round(tables["value"] / value, 3)
-
+    # The headline: K production steps through mp_decode_attn cycling the
+    # layers, then the same steps through the timed entry point, whose HIP
+    # events on the launch stream sit right around the scan + gather kernel.
+    scan, tables, state = measure_workload(cfg, layers, args.steps, args.warmup, dev, sh,
+                                           tables=not args.no_tables,
+                                           kv_layout=args.kv_layout, log=log)
     cpu = None
     if not args.no_cpu_baseline:
-        k, v, q = state[0][0], state[0][1], state[0][2]
-        cpu = cpu_baseline(cfg, k, v, q, cfg.hyperplane_seed(0), args.cpu_threads)
+        st0 = state[0]
+        cpu = cpu_baseline(cfg, st0["k"], st0["v"], st0["q"], cfg.hyperplane_seed(0),
+                           args.cpu_threads)
+    del state
+    torch.cuda.empty_cache()
+
+    per_config = None
+    if not args.no_configs:
+        per_config = {}
+        for name, (lay_n, st_n) in OTHER_WORKLOADS.items():
+            c = synth.CONFIGS[name]
+            sc, tb, stt = measure_workload(c, lay_n, st_n, max(4, st_n // 8), dev, sh,
+                                           tables=not args.no_tables, kv_layout=args.kv_layout,
+                                           log=log)
+            del stt
+            torch.cuda.empty_cache()
+            per_config[name] = {
+                "workload": (f"{c.name}: B={c.B} H_q={c.H_q} H_kv={c.H_kv} n={c.n} K={c.K} "
+                             f"L={c.L} T={c.n_sink}+{c.n_local} kv=bf16"),
+                "code_scan": sc, "tables": tb}
 
     # references outside the timed work, after the layers are freed
     stream_peak = err256 = None
     if not args.no_extras:
-        del state, k, v, q
-        torch.cuda.empty_cache()
         stream_peak = stream_read_peak(dev)
         err256 = estimator_error_256k(dev)
 
+    roof = scan.pop("roofline")
     line = {
         "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "decode layer-steps/s",
+        "value": scan.pop("value"),
+        "unit": scan.pop("unit"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": scan.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -470,32 +571,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} "
                                f"n={cfg.n} d={cfg.d} K={cfg.K} L={cfg.L} T={cfg.n_sink}+"
-                               f"{cfg.n_local} kv=bf16, {layers} layers cycled",
+                               f"{cfg.n_local} kv=bf16 ({args.kv_layout} K/V), "
+                               f"{layers} layers cycled",
                    "layers_cycled": layers},
-        "hbm_gbps_decode": round(dec_gbs, 1),
-        "pct_hbm_peak_decode": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
-        "keys_scanned_per_s": round(cfg.B * cfg.H_kv * cfg.n * value, 1),
-        "full_32_layer_steps_per_s": round(value / 32.0, 2),
-        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
-        "mean_S_per_head": round(sum(mean_S) / len(mean_S), 1),
-        "mean_union_rows_per_layer": round(sum(union_rows) / len(union_rows), 1),
-        "roofline": {"kernel": "scan_gather", "bound": "hbm", "achieved": round(scan_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("scan_gather"),
-                     "avg_launch_us": round(scan_avg_ms * 1e3, 3),
-                     "algorithmic_bytes_per_launch": round(scan_bytes / args.steps)},
-        "index_build": {"ms_per_layer": round(build_avg, 3),
-                        "tflops_fp32_mfma": round(flops_build / (build_avg / 1e3) / 1e12, 2),
-                        "frac_fp32_mfma_peak": round(flops_build / (build_avg / 1e3) / 1e12
-                                                     / FP32_MFMA_PEAK_TFLOPS, 4)},
+        "roofline": roof,
+        **{k: v for k, v in scan.items() if k not in ("layers_cycled", "steps")},
+        "full_32_layer_steps_per_s": None,
         "tables": tables,
+        "per_config": per_config,
         "stream_read_peak": stream_peak,
-        "pct_stream_read_peak": (round(100.0 * scan_gbs / stream_peak["gbps"], 1)
+        "pct_stream_read_peak": (round(100.0 * roof["achieved"] / stream_peak["gbps"], 1)
                                  if stream_peak else None),
         "estimator_error_256k": err256,
         "cpu_baseline": cpu,
     }
+    line["full_32_layer_steps_per_s"] = round(line["value"] / 32.0, 2)
     print(json.dumps(line), flush=True)
 
 
