@@ -90,8 +90,14 @@ typedef struct mp_index mp_index;
 /* Keys per chunk of the code layout (see mp_index_views). */
 #define MP_CHUNK 512
 
+/* Most keys per (sequence, KV head) an index or a view may hold (2^30: key
+ * counts padded to whole chunks stay inside int32).  Views with more keys are
+ * MP_E_SHAPE; size queries for more return 0. */
+#define MP_MAX_KEYS (1 << 30)
+
 /* Bytes of device workspace mp_build_index needs for these sizes; 0 if the
- * sizes are invalid (B, H_kv, n >= 1; d == 128; 0 <= K <= 16; 2 <= L <= 255). */
+ * sizes are invalid (B, H_kv >= 1, B * H_kv <= 65535; 1 <= n <= MP_MAX_KEYS;
+ * d == 128; 0 <= K <= 16; 2 <= L <= 255). */
 size_t mp_index_workspace_bytes(int32_t B, int32_t H_kv, int32_t n, int32_t d,
                                 int32_t K, int32_t L);
 

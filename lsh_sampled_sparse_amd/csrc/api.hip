@@ -77,9 +77,6 @@ IndexLayout index_layout(int32_t B, int32_t H_kv, int32_t n, int32_t K, int32_t 
     return y;
 }
 
-size_t collide_lds_bytes(const IndexLayout &lay);   // tables.hip
-int collide_slices();                               // tables.hip
-
 DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables, bool debug)
 {
     DecodeLayout y{};
@@ -96,9 +93,26 @@ DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables, boo
     y.off_seg_cnt = off;
     if (debug) off = align256(off + BHq * lay.n_chunks * 4);
     y.off_bits = off;
-    if (tables) off = align256(off + BHq * collide_slices() * (lay.n_pad / 16) * 4);
+    if (tables) off = align256(off + BHq * kCollideSlices * (lay.n_pad / 16) * 4);
     y.total = off;
     return y;
+}
+
+TablesLayout tables_layout(const IndexLayout &lay)
+{
+    TablesLayout y{};
+    y.nbins = 1 << lay.K;
+    const int64_t BH = int64_t(lay.B) * lay.H_kv;
+    int64_t off = 0;
+    y.off_offsets = off; off = align256(off + BH * lay.L * int64_t(y.nbins + 1) * 4);
+    y.off_entries = off; off = align256(off + BH * lay.L * int64_t(lay.n) * 4);
+    y.total = off;
+    return y;
+}
+
+size_t collide_lds_bytes(const IndexLayout &lay)
+{
+    return size_t(lay.n_pad / 16) * 4 + size_t(2 * lay.L + 1) * 4;
 }
 
 // Why the bucketed tables of an index cannot be used, or NULL.
@@ -112,8 +126,8 @@ static const char *tables_unsupported(const IndexLayout &lay)
 
 static bool sizes_ok(int32_t B, int32_t H, int32_t n, int32_t d, int32_t K, int32_t L)
 {
-    return B >= 1 && H >= 1 && n >= 1 && d == kD && K >= 0 && K <= 16 && L >= 2 && L <= 255 &&
-           int64_t(B) * H <= 65535;
+    return B >= 1 && H >= 1 && n >= 1 && n <= MP_MAX_KEYS && d == kD && K >= 0 && K <= 16 &&
+           L >= 2 && L <= 255 && int64_t(B) * H <= 65535;
 }
 
 static mp_status check_view(const mp_kv_view *v, const char *name)
@@ -125,6 +139,8 @@ static mp_status check_view(const mp_kv_view *v, const char *name)
     if (v->d != kD) return fail(MP_E_SHAPE, "%s: d = %d, only 128 is supported", name, v->d);
     if (v->B < 1 || v->H < 1 || v->n < 1)
         return fail(MP_E_SHAPE, "%s: B, H, n must be >= 1 (got %d, %d, %d)", name, v->B, v->H, v->n);
+    if (v->n > MP_MAX_KEYS)
+        return fail(MP_E_SHAPE, "%s: n = %d exceeds MP_MAX_KEYS (%d)", name, v->n, MP_MAX_KEYS);
     if (v->stride_b < 0 || v->stride_h < 0 || v->stride_n < kD)
         return fail(MP_E_SHAPE, "%s: strides must be >= 0 and stride_n >= 128", name);
     const int64_t elt = v->dtype == MP_F32 ? 4 : 2;

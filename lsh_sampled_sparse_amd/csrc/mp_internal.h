@@ -145,6 +145,9 @@ constexpr int kMaxTableK = 12;   // 2^K bucket counters live in LDS while a tabl
 // Largest dynamic LDS of the bucket walk (a head's collision bitmap and its
 // bucket bounds): a workgroup's 160 KB less room for the static part.
 constexpr size_t kCollideLdsMax = 160 * 1024 - 1024;
+constexpr int kCollideSlices = 4;   // bucket-walk workgroups per query head, each over L / 4 tables
+// Dynamic LDS of the bucket walk of an index: 2 bits per key, 2L + 1 bucket words.
+size_t collide_lds_bytes(const IndexLayout &lay);
 struct TablesLayout {
     int32_t nbins;
     int64_t off_offsets, off_entries, total;

@@ -25,22 +25,10 @@
 
 namespace mp {
 
-TablesLayout tables_layout(const IndexLayout &lay)
-{
-    TablesLayout y{};
-    y.nbins = 1 << lay.K;
-    const int64_t BH = int64_t(lay.B) * lay.H_kv;
-    int64_t off = 0;
-    y.off_offsets = off; off = align256(off + BH * lay.L * int64_t(y.nbins + 1) * 4);
-    y.off_entries = off; off = align256(off + BH * lay.L * int64_t(lay.n) * 4);
-    y.total = off;
-    return y;
-}
-
 namespace {
 
 constexpr int kBuildThreads = 1024;
-constexpr int kSlices = 4;   // collide workgroups per query head, each over L / kSlices tables
+constexpr int kSlices = kCollideSlices;
 
 // Exclusive prefix sum of one value per thread over a workgroup of
 // kBuildThreads (16 waves); every thread gets its own prefix and the total.
@@ -359,14 +347,6 @@ hipError_t launch_table_gather(const DecodeArgs &a, int32_t nwords, hipStream_t 
 }
 
 }  // namespace
-
-// LDS bytes of collide_kernel for an index (the API checks it against the
-// workgroup limit before any launch); also the number of slice bitmaps.
-int collide_slices() { return kSlices; }
-size_t collide_lds_bytes(const IndexLayout &lay)
-{
-    return size_t(lay.n_pad / 16) * 4 + size_t(2 * lay.L + 1) * 4;
-}
 
 // Dynamic LDS of build_tables_kernel: 3 x 2^K bucket words and the staged tile.
 static size_t build_tables_lds(int K) { return (size_t(3) * (size_t(1) << K) + kStageTile) * 4; }

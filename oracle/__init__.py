@@ -23,7 +23,9 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MP_ORACLE_LIB names another build of oracle.c (the sanitized one of
+# build.build(sanitize=True)); the default is the plain build beside this file.
+_LIB_PATH = os.environ.get("MP_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 SCORE_CENTERED = 1
