@@ -93,7 +93,7 @@ DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables, boo
     y.off_seg_cnt = off;
     if (debug) off = align256(off + BHq * lay.n_chunks * 4);
     y.off_bits = off;
-    if (tables) off = align256(off + BHq * kCollideSlices * (lay.n_pad / 16) * 4);
+    if (tables) off = align256(off + BHq * collide_plan(BHq).slices * (lay.n_pad / 16) * 4);
     y.total = off;
     return y;
 }

@@ -72,9 +72,10 @@ __device__ __forceinline__ uint32_t and_xnor(uint32_t acc, uint32_t p, uint32_t 
 // ---------------------------------------------------------------- query codes
 // Block: TB = 64/K whole tables (<= 64 hyperplanes) x kQueryHeads query
 // heads.  Thread = (hyperplane, quarter of the dims): four lanes read one W
-// row together (coalesced) and keep their 32 dims in registers for all the
-// block's heads, whose queries are LDS broadcasts; two shuffles add the
-// quarters.  Sign bits meet in LDS and are packed per (head, table).
+// row together (64 contiguous bytes a load) and keep their 32 dims in
+// registers for all the block's heads, whose queries are LDS broadcasts;
+// two shuffles add the quarters.  Sign bits meet in LDS and are packed per
+// (head, table).
 constexpr int kQueryHeads = 4;
 __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restrict__ q,
                                                            int32_t BHq,
@@ -97,39 +98,19 @@ __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restri
     if (t < nq * (kD / 4)) sQ[t / (kD / 4)][t % (kD / 4)] = q4[t];
     float4 wr[8];
     if (hp < nh) {
-        const float4 *w4 = reinterpret_cast<const float4 *>(W + (int64_t(l0) * K + hp) * kD) + 8 * dq;
+        load_w_quarter(wr, W + (int64_t(l0) * K + hp) * kD, dq);
+    } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) wr[c] = w4[c];
+        for (int c = 0; c < 8; ++c) wr[c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
     __syncthreads();
     if (blockIdx.x == 0) {         // |q| of the block's heads, for the cosines
         const int j = t >> 5, c4 = t & 31;
-        float s2 = 0.0f;
-        if (j < nq) {
-            const float4 v = sQ[j][c4];
-            s2 = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        }
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) s2 += __shfl_xor(s2, off, 32);
-        if (j < nq && c4 == 0) qnorm[q0 + j] = sqrtf(s2);
+        const float nrm = norm32(j < nq ? sQ[j][c4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f));
+        if (j < nq && c4 == 0) qnorm[q0 + j] = nrm;
     }
     for (int j = 0; j < nq; ++j) {
-        float a0 = 0.0f, a1 = 0.0f;   // two chains over the quarter's 32 dims
-#pragma unroll
-        for (int c = 0; c < 8; c += 2) {
-            const float4 qa = sQ[j][8 * dq + c], qb = sQ[j][8 * dq + c + 1];
-            a0 = fmaf(wr[c].x, qa.x, a0);
-            a0 = fmaf(wr[c].y, qa.y, a0);
-            a0 = fmaf(wr[c].z, qa.z, a0);
-            a0 = fmaf(wr[c].w, qa.w, a0);
-            a1 = fmaf(wr[c + 1].x, qb.x, a1);
-            a1 = fmaf(wr[c + 1].y, qb.y, a1);
-            a1 = fmaf(wr[c + 1].z, qb.z, a1);
-            a1 = fmaf(wr[c + 1].w, qb.w, a1);
-        }
-        float sdot = a0 + a1;
-        sdot += __shfl_xor(sdot, 1, 4);
-        sdot += __shfl_xor(sdot, 2, 4);
+        const float sdot = quarter_dot(wr, sQ[j], dq);
         if (dq == 0 && hp < nh) sbit[j][hp] = sdot > 0.0f ? 1 : 0;
     }
     __syncthreads();

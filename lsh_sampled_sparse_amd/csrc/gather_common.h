@@ -83,6 +83,57 @@ template <> struct Row8<uint16_t> {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// ---- query codes (page "MagicPIG: LSH Sampling for Efficient LLM
+// Generation", background: a SimHash bit is the sign of a projection on a
+// random hyperplane).  Both decode paths compute a query's projections with
+// these two routines, so their codes and norms agree bit for bit.
+//
+// q . W_j over a group of four lanes: lane dq holds float4s 4c + dq
+// (c < 8) of row W_j, so that each of the eight loads of a group reads 64
+// contiguous bytes, and reads the same float4s of q (32 float4, in LDS).  Two
+// FMA chains, their sum, then two shuffles over the group; all four lanes of
+// the group must call it together and get the whole sum.
+__device__ __forceinline__ void load_w_quarter(float4 (&wr)[8], const float *row, int dq)
+{
+    const float4 *w4 = reinterpret_cast<const float4 *>(row);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) wr[c] = w4[4 * c + dq];
+}
+
+__device__ __forceinline__ float quarter_dot(const float4 (&wr)[8], const float4 *q4, int dq)
+{
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) {
+        const float4 qa = q4[4 * c + dq], qb = q4[4 * c + 4 + dq];
+        a0 = fmaf(wr[c].x, qa.x, a0);
+        a0 = fmaf(wr[c].y, qa.y, a0);
+        a0 = fmaf(wr[c].z, qa.z, a0);
+        a0 = fmaf(wr[c].w, qa.w, a0);
+        a1 = fmaf(wr[c + 1].x, qb.x, a1);
+        a1 = fmaf(wr[c + 1].y, qb.y, a1);
+        a1 = fmaf(wr[c + 1].z, qb.z, a1);
+        a1 = fmaf(wr[c + 1].w, qb.w, a1);
+    }
+    float sdot = a0 + a1;
+    sdot += __shfl_xor(sdot, 1, 4);
+    sdot += __shfl_xor(sdot, 2, 4);
+    return sdot;
+}
+
+// |q| over a group of 32 lanes, lane c4 holding float4 c4 of the query; all
+// 32 lanes call it together and get the norm.
+__device__ __forceinline__ float norm32(float4 v)
+{
+    float s2 = v.x * v.x;
+    s2 = fmaf(v.y, v.y, s2);
+    s2 = fmaf(v.z, v.z, s2);
+    s2 = fmaf(v.w, v.w, s2);
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) s2 += __shfl_xor(s2, off, 32);
+    return sqrtf(s2);
+}
+
 // log u for u = P[at least 2 of L tables collide], P = p^K (fp32).
 // Closed form 1 - (1-P)^L - L P (1-P)^(L-1) where L*P > 0.05; below that the
 // two subtractions cancel, so u is the binomial tail

@@ -145,7 +145,23 @@ constexpr int kMaxTableK = 12;   // 2^K bucket counters live in LDS while a tabl
 // Largest dynamic LDS of the bucket walk (a head's collision bitmap and its
 // bucket bounds): a workgroup's 160 KB less room for the static part.
 constexpr size_t kCollideLdsMax = 160 * 1024 - 1024;
-constexpr int kCollideSlices = 4;   // bucket-walk workgroups per query head, each over L / 4 tables
+// The bucket walk of the table path: `slices` workgroups per query head, each
+// over L / slices of its tables, and whether they compute the query's codes
+// for their tables themselves (one launch fewer, at the price of reading W
+// once per query head instead of once per four).  Both depend only on the
+// number of query heads B * H_q, so the scratch layout and the launch agree.
+// The gather is compiled for 4 and 8 slices.
+constexpr int kMaxCollideSlices = 8;
+struct CollidePlan {
+    int32_t slices;
+    bool own_codes;
+};
+inline CollidePlan collide_plan(int64_t BHq)
+{
+    if (BHq <= 32) return {8, true};
+    if (BHq <= 64) return {4, true};
+    return {4, false};
+}
 // Dynamic LDS of the bucket walk of an index: 2 bits per key, 2L + 1 bucket words.
 size_t collide_lds_bytes(const IndexLayout &lay);
 struct TablesLayout {

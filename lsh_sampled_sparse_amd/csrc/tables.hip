@@ -11,15 +11,19 @@
 //                  the keys by their code (bucket starts + keys grouped by
 //                  bucket).  Keys within a bucket come in no fixed order;
 //                  nothing downstream depends on it.
-//   collide        per query head and slice of its L tables: the slice's
-//                  buckets, each key marked in an LDS bitmap of 2 bits (seen
-//                  once, seen twice), written out per slice.
+//   collide        per query head and slice of its L tables (collide_plan
+//                  sets the slices): the query's codes for the slice's
+//                  tables unless encode_query has made them, then the
+//                  slice's buckets, each key marked in an LDS bitmap of 2
+//                  bits (seen once, seen twice), written out per slice.
 //   table_gather   per 512-key chunk: the G heads' slice bits of its keys
 //                  (seen twice = in one slice, or once in two) give the
 //                  sampled / exact list; gather-SNIS as in the code scan
 //                  (gather_common.h) writes the chunk's partial softmax, which
 //                  the merge of decode.hip combines.
 #include <hip/hip_ext.h>
+
+#include <algorithm>
 
 #include "gather_common.h"
 
@@ -28,7 +32,9 @@ namespace mp {
 namespace {
 
 constexpr int kBuildThreads = 1024;
-constexpr int kSlices = kCollideSlices;
+// LDS of collide_kernel's code step: q (kD floats) and the sign bits of a
+// slice's hyperplanes (at most 255 tables of kMaxTableK bits).
+constexpr size_t kCollideCodeLds = kD * 4 + 255 * kMaxTableK;
 
 // Exclusive prefix sum of one value per thread over a workgroup of
 // kBuildThreads (16 waves); every thread gets its own prefix and the total.
@@ -185,31 +191,88 @@ __global__ __launch_bounds__(kBuildThreads) void build_tables_kernel(
     }
 }
 
-// Block = one slice of the L tables of one query head (kSlices slices).
-// LDS: the slice's bitmap (2 bits per key: bit 0 = seen in a bucket, bit 1 =
-// seen in two), then per table of the slice the bucket start and the prefix
-// of bucket sizes.  The entries of the slice's buckets are walked as one flat
-// range, four per thread at a time so their loads overlap.  Slice bitmaps go
-// out side by side; the gather combines them.
+// Block = one slice of the L tables of one query head (`slices` slices).
+// With kOwnCodes, first the head's codes for the slice's tables, computed
+// here rather than in a kernel of their own: thread = (hyperplane, quarter of
+// the dims), 256 hyperplanes a pass, with the projection of the code scan's
+// query encoder (quarter_dot), so both paths find the same codes; the sign
+// bits meet in LDS.  The codes also go to qcodes (the debug view) and the
+// first slice writes |q|.  Otherwise the codes come from qcodes.  Then the
+// bucket walk.  LDS: the slice's bitmap (2 bits per
+// key: bit 0 = seen in a bucket, bit 1 = seen in two), then per table of the
+// slice the bucket start and the prefix of bucket sizes; the code step uses
+// the front of that space before the bitmap is cleared.  The entries of the
+// slice's buckets are walked as one flat range, four per thread at a time so
+// their loads overlap.  Slice bitmaps go out side by side; the gather
+// combines them.
+template <bool kOwnCodes>
 __global__ __launch_bounds__(kBuildThreads) void collide_kernel(
-    const uint16_t *__restrict__ qcodes, const uint32_t *__restrict__ off,
-    const uint32_t *__restrict__ ent, int32_t H_q, int32_t H_kv, int32_t n, int32_t nwords,
-    int32_t L, int32_t nbins, uint32_t *__restrict__ bits)
+    const float *__restrict__ q, const float *__restrict__ W, int32_t K,
+    const uint32_t *__restrict__ off, const uint32_t *__restrict__ ent, int32_t H_q, int32_t H_kv,
+    int32_t n, int32_t nwords, int32_t L, int32_t nbins, uint32_t *__restrict__ bits,
+    uint16_t *__restrict__ qcodes, float *__restrict__ qnorm, int32_t slices)
 {
     extern __shared__ uint32_t sm[];
     __shared__ uint32_t wtot[kBuildThreads / 64];
-    const int bhq = blockIdx.x / kSlices, sl = blockIdx.x % kSlices;
-    const int l0 = (sl * L) / kSlices, nl = ((sl + 1) * L) / kSlices - l0;
+    const int bhq = blockIdx.x / slices, sl = blockIdx.x % slices;
+    const int l0 = (sl * L) / slices, nl = ((sl + 1) * L) / slices - l0;
+    const int t = threadIdx.x;
+    uint32_t code = 0u;
+    if (kOwnCodes) {
+        // ---- the slice's query codes (the first W rows are loaded before q is
+        // staged, so that the two loads overlap)
+        float4 *sq4 = reinterpret_cast<float4 *>(sm);              // q: kD / 4 float4
+        uint8_t *sbit = reinterpret_cast<uint8_t *>(sm + kD);      // nl * K sign bits
+        const int nh = nl * K, hp0 = t >> 2, dq = t & 3;
+        constexpr int kPass = kBuildThreads / 4;                   // hyperplanes a pass
+        float4 wr[2][8];
+        auto load_pass = [&](int p0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int hp = p0 + h * kPass + hp0;
+                if (hp < nh) {
+                    load_w_quarter(wr[h], W + (int64_t(l0) * K + hp) * kD, dq);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) wr[h][c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                }
+            }
+        };
+        load_pass(0);
+        if (t < kD / 4) sq4[t] = reinterpret_cast<const float4 *>(q + int64_t(bhq) * kD)[t];
+        __syncthreads();
+        if (sl == 0 && t < 32) {
+            const float nrm = norm32(sq4[t]);
+            if (t == 0) qnorm[bhq] = nrm;
+        }
+        for (int p0 = 0; p0 < nh; p0 += 2 * kPass) {
+            if (p0 > 0) load_pass(p0);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int hp = p0 + h * kPass + hp0;
+                const float sdot = quarter_dot(wr[h], sq4, dq);
+                if (dq == 0 && hp < nh) sbit[hp] = sdot > 0.0f ? 1 : 0;
+            }
+        }
+        __syncthreads();
+        if (t < nl) {
+            for (int bb = 0; bb < K; ++bb) code |= uint32_t(sbit[t * K + bb]) << bb;
+            qcodes[int64_t(bhq) * L + l0 + t] = uint16_t(code);
+        }
+    } else if (t < nl) {
+        code = qcodes[int64_t(bhq) * L + l0 + t];
+    }
+    __syncthreads();   // the code step's LDS is the bitmap's from here on
+
+    // ---- the bucket walk
     uint32_t *bm = sm;
     uint32_t *bstart = sm + nwords;
     uint32_t *bpre = bstart + nl;   // nl + 1 entries
     const int b = bhq / H_q, hq = bhq % H_q, G = H_q / H_kv;
     const int u = b * H_kv + hq / G;
-    const int t = threadIdx.x;
     for (int i = t; i < nwords; i += kBuildThreads) bm[i] = 0u;
     uint32_t size = 0u;
     if (t < nl) {
-        const uint32_t code = qcodes[int64_t(bhq) * L + l0 + t];
         const uint32_t *o = off + (int64_t(u) * L + l0 + t) * (nbins + 1);
         const uint32_t s0 = o[code];
         bstart[t] = s0;
@@ -245,13 +308,24 @@ __global__ __launch_bounds__(kBuildThreads) void collide_kernel(
         }
     }
     __syncthreads();
-    uint32_t *ob = bits + int64_t(bhq) * kSlices * nwords + sl * nwords;
+    uint32_t *ob = bits + int64_t(bhq) * slices * nwords + sl * nwords;
     for (int i = t; i < nwords; i += kBuildThreads) ob[i] = bm[i];
 }
 
-// Block = one 512-key chunk of one unit and its G query heads.
+// Waves per SIMD the register budget is cut for: with bf16 rows 5 up to
+// G = 4 (more chunks resident at once; the second gather round then loads its
+// rows when it starts) and 4 at G = 8 (the second round's rows issued ahead);
+// with fp32 rows what the registers give (LDS holds it to 4 or fewer).
 template <int G, typename T>
-__global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int32_t nwords)
+constexpr int table_occupancy() { return sizeof(T) == 2 ? (G <= 4 ? 5 : 4) : 2; }
+template <int G, typename T>
+constexpr bool table_rows_ahead() { return sizeof(T) == 2 && G > 4; }
+
+// Block = one 512-key chunk of one unit and its G query heads; S slice
+// bitmaps per head (a compile-time count, so that their loads issue together).
+template <int G, typename T, int S>
+__global__ __launch_bounds__(256, (table_occupancy<G, T>())) void table_gather_kernel(DecodeArgs a,
+                                                                                     int32_t nwords)
 {
     __shared__ uint32_t ulist[kChunk];
     __shared__ int wsum[4];
@@ -283,8 +357,8 @@ __global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int3
         // seen twice: in one slice, or once in each of two slices
         uint32_t o = 0u, w2 = 0u;
 #pragma unroll
-        for (int sl = 0; sl < kSlices; ++sl) {
-            const uint32_t f = a.bits[(int64_t(bhq0 + g) * kSlices + sl) * nwords + word] >> sh;
+        for (int sl = 0; sl < S; ++sl) {
+            const uint32_t f = a.bits[(int64_t(bhq0 + g) * S + sl) * nwords + word] >> sh;
             const uint32_t f1 = f & 0x5u, f2 = (f >> 1) & 0x5u;   // 2 keys x 2 bits
             w2 |= f2 | (o & f1);
             o |= f1;
@@ -325,25 +399,33 @@ __global__ __launch_bounds__(256, 2) void table_gather_kernel(DecodeArgs a, int3
     const T *kb, *vb;
     row_bases<T>(a, bkv, li, kb, vb);
     load_rows<T>(a, kb, vb, ulist, 0, min(kRound, total), chunk, gi, kr, vr);
-    // bf16 rows: the second round's rows are issued ahead (fp32 rows would
-    // cost a wave per SIMD)
-    gather_chunk<G, T, sizeof(T) == 2>(a, gl, ulist, total, chunk, bkv, sq, sqn, smu, kr, vr, t,
-                                       gi, li);
+    gather_chunk<G, T, table_rows_ahead<G, T>()>(a, gl, ulist, total, chunk, bkv, sq, sqn, smu, kr,
+                                                  vr, t, gi, li);
 }
 
-template <int G, typename T>
+template <int G, typename T, int S>
 hipError_t launch_table_gather_t(const DecodeArgs &a, int32_t nwords, hipStream_t s)
 {
     const dim3 grid(a.B * a.H_kv * a.n_chunks);
-    return launch_timed(table_gather_kernel<G, T>, grid, dim3(256), 0, s, a.ev_begin, a.ev_end, a,
-                        nwords);
+    return launch_timed(table_gather_kernel<G, T, S>, grid, dim3(256), 0, s, a.ev_begin, a.ev_end,
+                        a, nwords);
+}
+
+template <int G, int S>
+hipError_t launch_table_gather_s(const DecodeArgs &a, int32_t nwords, hipStream_t s)
+{
+    return a.dtype == MP_BF16 ? launch_table_gather_t<G, uint16_t, S>(a, nwords, s)
+                              : launch_table_gather_t<G, float, S>(a, nwords, s);
 }
 
 template <int G>
-hipError_t launch_table_gather(const DecodeArgs &a, int32_t nwords, hipStream_t s)
+hipError_t launch_table_gather(const DecodeArgs &a, int32_t nwords, int32_t slices, hipStream_t s)
 {
-    return a.dtype == MP_BF16 ? launch_table_gather_t<G, uint16_t>(a, nwords, s)
-                              : launch_table_gather_t<G, float>(a, nwords, s);
+    switch (slices) {
+    case 4: return launch_table_gather_s<G, 4>(a, nwords, s);
+    case 8: return launch_table_gather_s<G, 8>(a, nwords, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -369,26 +451,32 @@ hipError_t launch_build_tables(const mp_index_impl &idx, hipStream_t s)
 
 hipError_t launch_decode_tables(const DecodeArgs &a, hipStream_t s)
 {
-    hipError_t e = launch_encode_query(a, s);
+    const CollidePlan plan = collide_plan(int64_t(a.B) * a.H_q);
+    hipError_t e = plan.own_codes ? hipSuccess : launch_encode_query(a, s);
     if (e != hipSuccess) return e;
     static PerDevice attr;
     e = attr.once([](int) {
-        return hipFuncSetAttribute(reinterpret_cast<const void *>(collide_kernel),
+        hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(collide_kernel<true>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           int(kCollideLdsMax));
+        if (r != hipSuccess) return r;
+        return hipFuncSetAttribute(reinterpret_cast<const void *>(collide_kernel<false>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, int(kCollideLdsMax));
     });
     if (e != hipSuccess) return e;
     const int32_t n_pad = a.n_chunks * kChunk, nwords = n_pad / 16;
-    const size_t lds = size_t(nwords) * 4 + size_t(2 * a.L + 1) * 4;   // bounds any slice
-    e = launch(collide_kernel, dim3(a.B * a.H_q * kSlices), dim3(kBuildThreads), lds, s,
-               static_cast<const uint16_t *>(a.qcodes), static_cast<const uint32_t *>(a.tab_off),
-               static_cast<const uint32_t *>(a.tab_ent), a.H_q, a.H_kv, a.n, nwords, a.L,
-               1 << a.K, a.bits);
+    // bounds any slice; at least the code step's q and sign bits
+    const size_t lds = std::max(size_t(nwords) * 4 + size_t(2 * a.L + 1) * 4, kCollideCodeLds);
+    e = launch(plan.own_codes ? collide_kernel<true> : collide_kernel<false>,
+               dim3(a.B * a.H_q * plan.slices), dim3(kBuildThreads), lds, s, a.q, a.W, a.K,
+               static_cast<const uint32_t *>(a.tab_off), static_cast<const uint32_t *>(a.tab_ent),
+               a.H_q, a.H_kv, a.n, nwords, a.L, 1 << a.K, a.bits, a.qcodes, a.qnorm, plan.slices);
     if (e != hipSuccess) return e;
     switch (a.G) {
-    case 1: e = launch_table_gather<1>(a, nwords, s); break;
-    case 2: e = launch_table_gather<2>(a, nwords, s); break;
-    case 4: e = launch_table_gather<4>(a, nwords, s); break;
-    case 8: e = launch_table_gather<8>(a, nwords, s); break;
+    case 1: e = launch_table_gather<1>(a, nwords, plan.slices, s); break;
+    case 2: e = launch_table_gather<2>(a, nwords, plan.slices, s); break;
+    case 4: e = launch_table_gather<4>(a, nwords, plan.slices, s); break;
+    case 8: e = launch_table_gather<8>(a, nwords, plan.slices, s); break;
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

@@ -223,7 +223,7 @@ static void check_decode_args(const DecodeArgs &a, bool tables)
     if (tables) {
         rd(a.tab_off, BH * a.L * ((int64_t(1) << a.K) + 1) * 4);
         rd(a.tab_ent, BH * a.L * int64_t(a.n) * 4);
-        wr(a.bits, BHq * kCollideSlices * (n_pad / 16) * 4);
+        wr(a.bits, BHq * collide_plan(BHq).slices * (n_pad / 16) * 4);
     } else {
         rd(a.planes, BH * a.nc_cap * a.L * a.Kr * 16 * 4);
         EXPECT(a.bits == nullptr);
