@@ -282,6 +282,14 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
     bool pend = false;
     int p_bkv = 0, p_chunk = 0, p_total = 0, p_slot = 0;
     typename Row8<T>::raw kraw[kRowsPerGroup], vraw[kRowsPerGroup];
+    // The run's chunks of one unit fold into one partial softmax, stored as
+    // record run - first run of the unit (the merge reads those records).
+    GatherAcc<G> acc;
+    acc.reset();
+    auto store_unit = [&](int ubkv, int t) {
+        gather_store<G>(a, acc, run - (ubkv * a.n_chunks) / cpb, ubkv, t);
+        acc.reset();
+    };
 
 #pragma unroll 1
     for (int it = 0; it < nrun; ++it) {
@@ -362,18 +370,22 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
             // the masks in seen are complete, and so is the pending chunk's z
             __syncthreads();
             if (pend) {
-                // ---- (c), the rest: c2 of the first round, later rounds,
-                // the partial; then the pending chunk's list and LDS are free
+                // ---- (c), the rest: c2 of the first round, later rounds;
+                // then the pending chunk's list and LDS are free
                 gather_tail<G, T>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot],
-                                  sqn[p_slot], smu[p_slot], t, gi, li);
+                                  sqn[p_slot], smu[p_slot], acc, t, gi, li);
+                if (p_bkv != bkv) store_unit(p_bkv, t);   // its unit ends in this run
                 __syncthreads();
             }
         } else {
-            if (pend)   // ---- (c) gather-SNIS of the pending chunk
-                gather_chunk<G, T, false>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot],
-                                          sqn[p_slot], smu[p_slot], kraw, vraw, t, gi, li);
-            else
+            if (pend) {   // ---- (c) gather-SNIS of the pending chunk
+                gather_chunk_into<G, T, false>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot],
+                                               sqn[p_slot], smu[p_slot], kraw, vraw, acc, t, gi,
+                                               li);
+                if (p_bkv != bkv) store_unit(p_bkv, t);
+            } else {
                 retire_rows<T>(kraw, vraw);   // nothing in flight: returns at once
+            }
             // the masks in seen are complete; the pending chunk's list is no
             // longer read
             __syncthreads();
@@ -431,9 +443,10 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         const int t = threadIdx.x;
         // the plane buffers are dead here: the second round's rows go ahead
         // (bf16 rows; fp32 rows would not fit the registers)
-        gather_chunk<G, T, sizeof(T) == 2>(a, gl, ulist, p_total, p_chunk, p_bkv, sq[p_slot],
-                                           sqn[p_slot], smu[p_slot], kraw, vraw, t, t >> 4,
-                                           t & 15);
+        gather_chunk_into<G, T, sizeof(T) == 2>(a, gl, ulist, p_total, p_chunk, p_bkv,
+                                                sq[p_slot], sqn[p_slot], smu[p_slot], kraw, vraw,
+                                                acc, t, t >> 4, t & 15);
+        store_unit(p_bkv, t);
     }
 }
 
@@ -473,34 +486,39 @@ __global__ __launch_bounds__(256) void counts_kernel(DecodeArgs a)
 
 // ---------------------------------------------------------------- merge
 // Block = one (KV head unit, query head g of its group, kMergeDims dims);
-// thread = (dim c of kMergeDims, chunk lane j of 32).  Lane j folds chunks
-// j, j+32, ... into a running (max, sum, acc) in one pass, loading
-// kMergeBatch chunks before folding them so their loads overlap; the 32 lanes
-// are then combined in lane order, so the result is deterministic.  16 dims
-// a block (256 blocks at 32 query heads) spread the launch over the CUs.
+// thread = (dim c of kMergeDims, record lane j of 32).  A unit's records are
+// its runs of `cpb` chunks (cpb = 1: one record a chunk): the unit's chunks
+// [u n_chunks, (u+1) n_chunks) meet runs floor(u n_chunks / cpb) through
+// floor(((u+1) n_chunks - 1) / cpb).  Lane j folds records j, j+32, ... into
+// a running (max, sum, acc) in one pass, loading kMergeBatch records before
+// folding them so their loads overlap; the 32 lanes are then combined in lane
+// order, so the result is deterministic.  16 dims a block (256 blocks at 32
+// query heads) spread the launch over the CUs.
 constexpr int kMergeBatch = 8;
 constexpr int kMergeDims = 16;
 template <int G>
 __global__ __launch_bounds__(32 * kMergeDims) void merge_kernel(const float *__restrict__ part,
-                                                    int32_t n_chunks, int32_t H_kv, int32_t H_q,
-                                                    float *__restrict__ out)
+                                                    int32_t n_chunks, int32_t cpb, int32_t H_kv,
+                                                    int32_t H_q, float *__restrict__ out)
 {
     __shared__ float sm[32][kMergeDims + 1], sl[32][kMergeDims + 1], sa[32][kMergeDims + 1];
     const int bkv = blockIdx.x / G, g = blockIdx.x % G;
     const int t = threadIdx.x, cl = t % kMergeDims, j = t / kMergeDims;
     const int c = kMergeDims * blockIdx.y + cl;
-    const float *p = part + int64_t(bkv) * n_chunks * (G * kPart) + g * kPart;
+    const int64_t first = int64_t(bkv) * n_chunks;
+    const int nrec = int((first + n_chunks - 1) / cpb - first / cpb + 1);
+    const float *p = part + first * (G * kPart) + g * kPart;
     float m = -INFINITY, l = 0.0f, acc = 0.0f;
-    for (int base = j; base < n_chunks; base += 32 * kMergeBatch) {
+    for (int base = j; base < nrec; base += 32 * kMergeBatch) {
         float mb[kMergeBatch], lb[kMergeBatch], ab[kMergeBatch];
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
             const int ch = base + 32 * u;
-            const float *pc = p + int64_t(min(ch, n_chunks - 1)) * (G * kPart);
+            const float *pc = p + int64_t(min(ch, nrec - 1)) * (G * kPart);
             mb[u] = pc[0];
             lb[u] = pc[1];
             ab[u] = pc[2 + c];
-            if (ch >= n_chunks) mb[u] = -INFINITY;   // past the last chunk: nothing
+            if (ch >= nrec) mb[u] = -INFINITY;   // past the last record: nothing
         }
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
@@ -576,12 +594,12 @@ int resident_workgroups()
 }
 
 template <int G, typename T, int KP>
-hipError_t launch_scan_gather_t(const DecodeArgs &a, hipStream_t s)
+hipError_t launch_scan_gather_t(const DecodeArgs &a, hipStream_t s, int32_t &cpb)
 {
     const int64_t chunks = int64_t(a.B) * a.H_kv * a.n_chunks;
     const int slots = resident_workgroups<G, T, KP>();
     if (slots <= 0) return hipErrorInvalidDevice;
-    const int32_t cpb = ceil_div(chunks, slots);
+    cpb = ceil_div(chunks, slots);
     const dim3 grid(ceil_div(chunks, cpb));
     // timed entry point: the runtime stamps the events at this kernel's own
     // start and end
@@ -590,22 +608,23 @@ hipError_t launch_scan_gather_t(const DecodeArgs &a, hipStream_t s)
 }
 
 template <int G, typename T>
-hipError_t launch_scan_gather_kp(const DecodeArgs &a, hipStream_t s)
+hipError_t launch_scan_gather_kp(const DecodeArgs &a, hipStream_t s, int32_t &cpb)
 {
     switch (plane_rows_class(a.Kr)) {
-    case 4: return launch_scan_gather_t<G, T, 4>(a, s);
-    case 8: return launch_scan_gather_t<G, T, 8>(a, s);
-    case 10: return launch_scan_gather_t<G, T, 10>(a, s);
-    case 12: return launch_scan_gather_t<G, T, 12>(a, s);
-    default: return launch_scan_gather_t<G, T, 16>(a, s);
+    case 4: return launch_scan_gather_t<G, T, 4>(a, s, cpb);
+    case 8: return launch_scan_gather_t<G, T, 8>(a, s, cpb);
+    case 10: return launch_scan_gather_t<G, T, 10>(a, s, cpb);
+    case 12: return launch_scan_gather_t<G, T, 12>(a, s, cpb);
+    default: return launch_scan_gather_t<G, T, 16>(a, s, cpb);
     }
 }
 
+// Launches scan_gather; cpb receives its run length (chunks a workgroup).
 template <int G>
-hipError_t launch_scan_gather(const DecodeArgs &a, hipStream_t s)
+hipError_t launch_scan_gather(const DecodeArgs &a, hipStream_t s, int32_t &cpb)
 {
-    return a.dtype == MP_BF16 ? launch_scan_gather_kp<G, uint16_t>(a, s)
-                              : launch_scan_gather_kp<G, float>(a, s);
+    return a.dtype == MP_BF16 ? launch_scan_gather_kp<G, uint16_t>(a, s, cpb)
+                              : launch_scan_gather_kp<G, float>(a, s, cpb);
 }
 
 }  // namespace
@@ -619,15 +638,16 @@ hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s)
                   dim3(256), 0, s, a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
 }
 
-hipError_t launch_merge(const DecodeArgs &a, hipStream_t s)
+hipError_t launch_merge(const DecodeArgs &a, int32_t cpb, hipStream_t s)
 {
     const dim3 grid(a.B * a.H_kv * a.G, kD / kMergeDims), block(32 * kMergeDims);
     const float *part = a.part;
+    const int32_t nc = a.n_chunks;
     switch (a.G) {
-    case 1: return launch(merge_kernel<1>, grid, block, 0, s, part, a.n_chunks, a.H_kv, a.H_q, a.out);
-    case 2: return launch(merge_kernel<2>, grid, block, 0, s, part, a.n_chunks, a.H_kv, a.H_q, a.out);
-    case 4: return launch(merge_kernel<4>, grid, block, 0, s, part, a.n_chunks, a.H_kv, a.H_q, a.out);
-    case 8: return launch(merge_kernel<8>, grid, block, 0, s, part, a.n_chunks, a.H_kv, a.H_q, a.out);
+    case 1: return launch(merge_kernel<1>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
+    case 2: return launch(merge_kernel<2>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
+    case 4: return launch(merge_kernel<4>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
+    case 8: return launch(merge_kernel<8>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
     default: return hipErrorInvalidValue;
     }
 }
@@ -656,15 +676,16 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
 {
     hipError_t e = launch_encode_query(a, s);
     if (e != hipSuccess) return e;
+    int32_t cpb = 1;
     switch (a.G) {
-    case 1: e = launch_scan_gather<1>(a, s); break;
-    case 2: e = launch_scan_gather<2>(a, s); break;
-    case 4: e = launch_scan_gather<4>(a, s); break;
-    case 8: e = launch_scan_gather<8>(a, s); break;
+    case 1: e = launch_scan_gather<1>(a, s, cpb); break;
+    case 2: e = launch_scan_gather<2>(a, s, cpb); break;
+    case 4: e = launch_scan_gather<4>(a, s, cpb); break;
+    case 8: e = launch_scan_gather<8>(a, s, cpb); break;
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    if ((e = launch_merge(a, s)) != hipSuccess) return e;
+    if ((e = launch_merge(a, cpb, s)) != hipSuccess) return e;
     if ((e = launch_counts(a, s)) != hipSuccess) return e;
     return launch_seg_compact(a, s);
 }

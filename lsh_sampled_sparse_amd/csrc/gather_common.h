@@ -464,7 +464,7 @@ __device__ __forceinline__ void gather_round(const DecodeArgs &a, GatherLds<G, T
 // A chunk's gather in two parts, for a caller that runs the first inside
 // other work.  gather_head: round 0's c1 and z, which touch only LDS of the
 // calling wave and need no barrier; then, after a barrier, gather_tail: round
-// 0's c2, the later rounds, and the chunk's partial.
+// 0's c2 and the later rounds, folded into the caller's accumulator.
 template <int G, typename T>
 __device__ __forceinline__ void gather_head(const DecodeArgs &a, GatherLds<G, T> &s,
                                             const uint32_t *ulist, int total,
@@ -482,16 +482,15 @@ __device__ __forceinline__ void gather_head(const DecodeArgs &a, GatherLds<G, T>
 
 template <int G>
 __device__ __forceinline__ void gather_store(const DecodeArgs &a, const GatherAcc<G> &acc,
-                                             int chunk, int bkv, int t);
+                                             int slot, int bkv, int t);
 
 template <int G, typename T>
 __device__ __forceinline__ void gather_tail(const DecodeArgs &a, GatherLds<G, T> &s,
                                             const uint32_t *ulist, int total, int chunk, int bkv,
                                             const float (*sq)[kD], const float *sqn,
-                                            const float *smu, int t, int gi, int li)
+                                            const float *smu, GatherAcc<G> &acc, int t, int gi,
+                                            int li)
 {
-    GatherAcc<G> acc;
-    acc.reset();
     if (total > 0) gather_c2<G, T>(s, min(kRound, total), acc, t);
     if (total > kRound) {
         __syncthreads();   // round 0's c2 may still read its LDS
@@ -504,16 +503,17 @@ __device__ __forceinline__ void gather_tail(const DecodeArgs &a, GatherLds<G, T>
             gather_round<G, T, true>(a, s, ulist, base, ne, sq, sqn, smu, kr, vr, acc, t, gi, li);
         }
     }
-    gather_store<G>(a, acc, chunk, bkv, t);
 }
 
-// The chunk's partial softmax (max, sum, unnormalised accumulator) per head.
+// A partial softmax (max, sum, unnormalised accumulator) per head, into
+// record `slot` of unit bkv (records are n_chunks apart per unit; a record
+// holds one chunk, or several chunks of one unit folded together).
 template <int G>
 __device__ __forceinline__ void gather_store(const DecodeArgs &a, const GatherAcc<G> &acc,
-                                             int chunk, int bkv, int t)
+                                             int slot, int bkv, int t)
 {
     const int lane = t & 63;
-    float *part0 = a.part + (int64_t(bkv) * a.n_chunks + chunk) * (G * kPart);
+    float *part0 = a.part + (int64_t(bkv) * a.n_chunks + slot) * (G * kPart);
 #pragma unroll
     for (int p = 0; p < GatherAcc<G>::kPairs; ++p) {
         const int g = uniform((t + 256 * p) / (kD / 2)), dp = lane;
@@ -528,22 +528,19 @@ __device__ __forceinline__ void gather_store(const DecodeArgs &a, const GatherAc
     }
 }
 
-// The whole list of one chunk: round 0 from rows already loaded (kr0 / vr0),
-// later rounds load theirs; then the chunk's partial softmax (max, sum,
-// unnormalised accumulator) per head goes to `part`.  kAhead: the second
-// round's rows are issued before the first round runs, so that their
-// latency overlaps it (for callers with the registers to spare).
+// The whole list of one chunk, folded into acc: round 0 from rows already
+// loaded (kr0 / vr0), later rounds load theirs.  kAhead: the second round's
+// rows are issued before the first round runs, so that their latency
+// overlaps it (for callers with the registers to spare).
 template <int G, typename T, bool kAhead>
-__device__ __forceinline__ void gather_chunk(const DecodeArgs &a, GatherLds<G, T> &s,
-                                             const uint32_t *ulist, int total, int chunk,
-                                             int bkv, const float (*sq)[kD], const float *sqn,
-                                             const float *smu,
-                                             const typename Row8<T>::raw (&kr0)[kRowsPerGroup],
-                                             const typename Row8<T>::raw (&vr0)[kRowsPerGroup],
-                                             int t, int gi, int li)
+__device__ __forceinline__ void gather_chunk_into(const DecodeArgs &a, GatherLds<G, T> &s,
+                                                  const uint32_t *ulist, int total, int chunk,
+                                                  int bkv, const float (*sq)[kD],
+                                                  const float *sqn, const float *smu,
+                                                  const typename Row8<T>::raw (&kr0)[kRowsPerGroup],
+                                                  const typename Row8<T>::raw (&vr0)[kRowsPerGroup],
+                                                  GatherAcc<G> &acc, int t, int gi, int li)
 {
-    GatherAcc<G> acc;
-    acc.reset();
     const T *kb, *vb;
     row_bases<T>(a, bkv, li, kb, vb);
     typename Row8<T>::raw kr[kRowsPerGroup], vr[kRowsPerGroup];
@@ -560,6 +557,22 @@ __device__ __forceinline__ void gather_chunk(const DecodeArgs &a, GatherLds<G, T
             gather_round<G, T, true>(a, s, ulist, base, ne, sq, sqn, smu, kr, vr, acc, t, gi, li);
         }
     }
+}
+
+// One chunk's whole list into a record of its own (record = chunk).
+template <int G, typename T, bool kAhead>
+__device__ __forceinline__ void gather_chunk(const DecodeArgs &a, GatherLds<G, T> &s,
+                                             const uint32_t *ulist, int total, int chunk,
+                                             int bkv, const float (*sq)[kD], const float *sqn,
+                                             const float *smu,
+                                             const typename Row8<T>::raw (&kr0)[kRowsPerGroup],
+                                             const typename Row8<T>::raw (&vr0)[kRowsPerGroup],
+                                             int t, int gi, int li)
+{
+    GatherAcc<G> acc;
+    acc.reset();
+    gather_chunk_into<G, T, kAhead>(a, s, ulist, total, chunk, bkv, sq, sqn, smu, kr0, vr0, acc, t,
+                                    gi, li);
     gather_store<G>(a, acc, chunk, bkv, t);
 }
 

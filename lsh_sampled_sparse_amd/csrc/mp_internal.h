@@ -226,7 +226,7 @@ struct DecodeArgs {
     uint16_t *qcodes;        // scratch [BHq][L]
     uint32_t *qq;            // scratch [BHq][L], code | code << 16
     float *qnorm;            // scratch [BHq], |q|
-    float *part;             // scratch [B*H_kv][n_chunks][G][kD + 2] chunk partials
+    float *part;             // scratch [B*H_kv][n_chunks][G][kD + 2] partial records (a chunk, or a run's chunks of one unit)
     int32_t *seg_idx;        // scratch [BHq][n_chunks * kChunk] (debug only)
     int32_t *seg_cnt;        // scratch [BHq][n_chunks] (debug only)
     float *out;              // [BHq][128]
@@ -251,7 +251,9 @@ mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx, const 
 // dead handle or an H_q that does not fit the index.
 int64_t decode_scratch_needed(const mp_index *idx, int32_t H_q);
 hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s);
-hipError_t launch_merge(const DecodeArgs &a, hipStream_t s);
+// The LSE merge of the partial records: a unit's records are its runs of cpb
+// chunks (cpb = 1: a record per chunk).
+hipError_t launch_merge(const DecodeArgs &a, int32_t cpb, hipStream_t s);
 hipError_t launch_counts(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_seg_compact(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_build_tables(const mp_index_impl &idx, hipStream_t s);

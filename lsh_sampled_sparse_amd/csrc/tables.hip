@@ -480,7 +480,7 @@ hipError_t launch_decode_tables(const DecodeArgs &a, hipStream_t s)
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    if ((e = launch_merge(a, s)) != hipSuccess) return e;
+    if ((e = launch_merge(a, 1, s)) != hipSuccess) return e;   // a record per chunk
     return launch_seg_compact(a, s);
 }
 
