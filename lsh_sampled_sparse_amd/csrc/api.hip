@@ -429,13 +429,20 @@ mp_status mp_index_append(mp_index *idx, const mp_kv_view *keys, void *stream)
     if (keys->n == lay.n) return MP_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (lay.K > 0) {
-        // from the 256-key block holding the first new key: its old keys are
-        // encoded again to the same bits, so every plane word is written whole
         const KVRows rows{keys->data, keys->stride_b, keys->stride_h, keys->stride_n, keys->H};
-        const hipError_t e =
-            launch_encode_keys(rows, keys->dtype, lay.B, lay.H_kv, keys->n, lay.nc_cap, idx->mu,
-                               idx->Wp, lay.K, lay.L, lay.R_pad, idx->planes, lay.n / 256,
-                               nullptr, nullptr, nullptr, lay.n_cap, s);
+        hipError_t e;
+        if (keys->n - lay.n <= kAppendMax) {
+            // a few keys: their bits alone, written into the plane words
+            e = launch_append_codes(rows, keys->dtype, lay.B, lay.H_kv, lay.n, keys->n, lay.nc_cap,
+                                    idx->mu, idx->W, lay.K, lay.L, idx->planes, s);
+        } else {
+            // from the 256-key block holding the first new key: its old keys
+            // are encoded again to the same bits, so every plane word is
+            // written whole
+            e = launch_encode_keys(rows, keys->dtype, lay.B, lay.H_kv, keys->n, lay.nc_cap,
+                                   idx->mu, idx->Wp, lay.K, lay.L, lay.R_pad, idx->planes,
+                                   lay.n / 256, nullptr, nullptr, nullptr, lay.n_cap, s);
+        }
         if (e != hipSuccess)
             return fail(MP_E_HIP, "append launch failed: %s", hipGetErrorString(e));
     }

@@ -200,6 +200,12 @@ hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int3
                               const float *wx, const double *xx, const double *r2, int32_t n_cap,
                               hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int64_t count, hipStream_t s);
+// Codes of keys [n0, n1) of every unit written bit by bit into the planes
+// (n1 - n0 <= kAppendMax; K >= 1), with the build's mu and canonical W.
+constexpr int kAppendMax = 64;
+hipError_t launch_append_codes(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n0,
+                               int32_t n1, int32_t nc_cap, const float *mu, const float *W,
+                               int32_t K, int32_t L, uint32_t *planes, hipStream_t s);
 // The lift: wx from the hyperplane stream; xx, r^2 and r of every unit (mu64
 // must hold the fp64 mean).
 hipError_t launch_wgen_extra(uint64_t seed, int32_t R, int32_t R_pad, float *wx, hipStream_t s);

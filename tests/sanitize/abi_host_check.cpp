@@ -198,6 +198,25 @@ hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int3
     return hipSuccess;
 }
 
+hipError_t launch_append_codes(const KVRows &keys, int32_t dtype, int32_t B, int32_t H, int32_t n0,
+                               int32_t n1, int32_t nc_cap, const float *mu, const float *W,
+                               int32_t K, int32_t L, uint32_t *planes, hipStream_t)
+{
+    if (take_forced_failure()) return hipErrorLaunchFailure;
+    EXPECT(K >= 1 && n0 < n1 && n1 - n0 <= kAppendMax && n1 <= int64_t(nc_cap) * 512);
+    const int64_t BH = int64_t(B) * H;
+    rd_rows(keys, dtype, B, H, n0, n1);
+    rd(mu, BH * 128 * 4);
+    rd(W, int64_t(K) * L * 128 * 4);
+    // each row's words holding the new keys, in every unit
+    const int64_t chunk_words = int64_t(L) * K * 16;
+    for (int64_t u = 0; u < BH; ++u)
+        for (int64_t i = n0; i < n1; ++i)
+            for (int64_t r = 0; r < int64_t(K) * L; ++r)
+                wr(planes + (u * nc_cap + i / 512) * chunk_words + r * 16 + (i % 512) / 32, 4);
+    return hipSuccess;
+}
+
 hipError_t launch_fill_u32(uint32_t *p, int64_t count, hipStream_t)
 {
     if (take_forced_failure()) return hipErrorLaunchFailure;
@@ -722,6 +741,9 @@ int main(int argc, char **argv)
             {"mips", MP_BF16, 1, 2, 2000, 10, 60, 4, 0, MP_INDEX_MIPS, 0, 128},
             {"grow", MP_BF16, 1, 2, 1000, 10, 60, 4, 3000, 0, 2900, 128},
             {"grow_K0", MP_BF16, 1, 1, 257, 0, 10, 8, 1200, 0, 1100, 128},
+            {"grow_small", MP_BF16, 1, 2, 1000, 10, 60, 4, 1100, 0, 1003, 128},
+            {"grow_small_across_chunk", MP_F32, 2, 1, 510, 9, 40, 2, 600, 0, 514, 128},
+            {"grow_by_64_then_65", MP_BF16, 1, 2, 700, 10, 30, 4, 900, 0, 829, 128},
             {"llama8b_like_20k", MP_BF16, 1, 8, 20000, 10, 150, 4, 0, 0, 0, 128},
         };
         for (const Case &c : cases) run_case(c);

@@ -118,6 +118,29 @@ def test_grow_from_one_key_gqa8():
         print("from one key", r, flush=True)
 
 
+@pytest.mark.parametrize("dtype,H_q,K,L", [(torch.bfloat16, 8, 10, 60), (torch.float32, 16, 9, 40)])
+def test_small_appends_bit_by_bit(dtype, H_q, K, L):
+    """Appends of at most 64 keys write the new keys' bits alone into the
+    plane words; 65 or more re-encode from the first new key's 256-key block.
+    From 480 keys: steps of 1, 1, 31 (into the second chunk), 32, 64, 65 (the
+    block path), 349, 1, 1 (into the third chunk) and 63 keys."""
+    for r in run_growth(1, H_q, 2, dtype, K, L, 480,
+                        [481, 482, 513, 545, 609, 674, 1023, 1024, 1025, 1088], 4, 32, seed=26):
+        print("small appends", r, flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_grow_96k_key_by_key():
+    """The serving pattern at the timed shape: one key appended per step
+    (a token leaving the local window), three steps."""
+    cfg = synth.CONFIGS["llama8b_96k"]
+    n1 = cfg.n
+    for r in run_growth(1, cfg.H_q, cfg.H_kv, cfg.dtype, cfg.K, cfg.L, n1 - 3,
+                        [n1 - 2, n1 - 1, n1], cfg.n_sink, cfg.n_local,
+                        seed=cfg.hyperplane_seed(4)):
+        print("96k key by key", r, flush=True)
+
+
 def test_grow_K0_every_key_collides():
     for r in run_growth(1, 4, 1, torch.bfloat16, 0, 8, 200, [900], 4, 16, seed=24):
         print("K0 growth", r, flush=True)
