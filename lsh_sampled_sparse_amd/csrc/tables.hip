@@ -340,15 +340,39 @@ __global__ __launch_bounds__(256, (table_occupancy<G, T>())) void table_gather_k
     const int bkv = blockIdx.x % units, chunk = a.n_chunks - 1 - blockIdx.x / units;
     const int bhq0 = (bkv / a.H_kv) * a.H_q + (bkv % a.H_kv) * G;
     const int t = threadIdx.x, gi = t >> 4, li = t & 15;
-    for (int i = t; i < G * kD; i += 256) sq[i / kD][i % kD] = a.q[int64_t(bhq0) * kD + i];
-    if (t < G) sqn[t] = a.qnorm[bhq0 + t];
-    if (t == 0) sqn[2 * G] = a.rnorm ? a.rnorm[bkv] : 0.0f;
-    if (t < kD) smu[t] = a.mu[int64_t(bkv) * kD + t];
-
     // Thread t owns keys 2t and 2t+1: one 4-bit field of a bitmap word.
     const int n = a.n;
     const int64_t key0 = int64_t(chunk) * kChunk + 2 * t;
     const int word = int(key0 >> 4), sh = 2 * int(key0 & 15);
+
+    // Every load of the prologue (queries, norms, lift radius, mean, the
+    // slice bitmaps) is issued before any of them is waited for: one round
+    // trip, not one per LDS store.
+    constexpr int kQ = (G * kD + 255) / 256;
+    float qv[kQ];
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+        const int i = t + 256 * j;
+        qv[j] = i < G * kD ? a.q[int64_t(bhq0) * kD + i] : 0.0f;
+    }
+    const float qn = t < G ? a.qnorm[bhq0 + t] : 0.0f;
+    const float rn = t == 0 && a.rnorm ? a.rnorm[bkv] : 0.0f;
+    const float mv = t < kD ? a.mu[int64_t(bkv) * kD + t] : 0.0f;
+    uint32_t fb[G][S];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int sl = 0; sl < S; ++sl)
+            fb[g][sl] = a.bits[(int64_t(bhq0 + g) * S + sl) * nwords + word];
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+        const int i = t + 256 * j;
+        if (i < G * kD) sq[i / kD][i % kD] = qv[j];
+    }
+    if (t < G) sqn[t] = qn;
+    if (t == 0) sqn[2 * G] = rn;
+    if (t < kD) smu[t] = mv;
+
     uint32_t hm[2] = {0u, 0u}, c2[2][G];
     bool ex[2], fl[2];
     uint32_t once[G], twice[G];
@@ -358,7 +382,7 @@ __global__ __launch_bounds__(256, (table_occupancy<G, T>())) void table_gather_k
         uint32_t o = 0u, w2 = 0u;
 #pragma unroll
         for (int sl = 0; sl < S; ++sl) {
-            const uint32_t f = a.bits[(int64_t(bhq0 + g) * S + sl) * nwords + word] >> sh;
+            const uint32_t f = fb[g][sl] >> sh;
             const uint32_t f1 = f & 0x5u, f2 = (f >> 1) & 0x5u;   // 2 keys x 2 bits
             w2 |= f2 | (o & f1);
             o |= f1;
