@@ -117,6 +117,16 @@ def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref)) / den)
 
 
+def elem_rel_err(got: np.ndarray, ref: np.ndarray, floor: float = 1e-3) -> float:
+    """Largest elementwise error relative to max(|ref_j|, floor * max|ref|):
+    a reported companion to row_rel_err (the bar), which near-zero elements
+    would make unstable without the floor."""
+    top = np.max(np.abs(ref))
+    if top == 0.0:
+        return float(np.max(np.abs(got)))
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), floor * top)))
+
+
 def write_report(name: str, rep: dict):
     path = os.environ.get("MP_PARITY_REPORT")
     if path:
@@ -156,7 +166,7 @@ def run_case(k, v, q, K, L, seed, n_sink, n_local, scale=0.0, name=None, idx=Non
     scl = scale if scale > 0 else 1.0 / math.sqrt(d)
     key_mism = key_band = q_mism = q_band = 0
     s_diff_keys = s_diff_heads = 0
-    errs, errs_own = [], []
+    errs, errs_own, errs_elem = [], [], []
     threads = oracle_threads()
     for b in range(B):
         for h in range(H_kv):
@@ -185,6 +195,7 @@ def run_case(k, v, q, K, L, seed, n_sink, n_local, scale=0.0, name=None, idx=Non
                 ref = oracle.estimate(qh, kh, vh, mu, S, K, L, n_sink, n_local, scl)
                 e = row_rel_err(out[b, hq], ref)
                 errs.append(e)
+                errs_elem.append(elem_rel_err(out[b, hq], ref))
                 assert e <= OUT_TOL, f"output error {e:.3g} at (b={b}, h={hq})"
                 # the oracle's integer steps on its own codes: S may differ
                 # only at keys where a code bit differs (in the band)
@@ -209,6 +220,7 @@ def run_case(k, v, q, K, L, seed, n_sink, n_local, scale=0.0, name=None, idx=Non
                key_band_bits=key_band, heads_checked=B * H_q, query_bits=q_bits,
                query_mismatched_bits=q_mism, query_band_bits=q_band,
                max_out_err=max(errs) if errs else 0.0,
+               max_out_err_elementwise=max(errs_elem) if errs_elem else 0.0,
                s_diff_vs_oracle_codes={"heads": s_diff_heads, "keys": s_diff_keys},
                max_out_err_vs_oracle_own_S=max(errs_own) if errs_own else 0.0,
                mean_S=float(s_len.mean()))

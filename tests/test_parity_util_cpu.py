@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
+import parity_util
 from parity_util import check_unit_codes
 
 
@@ -26,3 +27,12 @@ def test_unit_code_check_accepts_band_flips_only():
     got[l, i] ^= 1                             # outside the band: refused
     with pytest.raises(AssertionError, match="outside the band"):
         check_unit_codes(ref, band, got, "planted")
+
+
+def test_elementwise_error_has_a_floor():
+    ref = np.array([1.0, -2.0, 1e-9, 0.0])
+    got = ref + np.array([1e-3, 0.0, 1e-6, 0.0])
+    # element 2: |1e-6| / max(1e-9, 1e-3 * 2) = 5e-4; element 0: 1e-3 / 1 = 1e-3
+    assert np.isclose(parity_util.elem_rel_err(got, ref), 1e-3)
+    assert parity_util.elem_rel_err(ref, ref) == 0.0
+    assert parity_util.elem_rel_err(np.ones(3), np.zeros(3)) == 1.0
