@@ -161,10 +161,11 @@ __device__ __forceinline__ float log1p_f32(float x)
 // taken in logs.  There c_i r <= L P / 3 <= 0.0175 for every i, so the terms
 // left out after i = 7 add less than 2e-10 relative: far below fp32.  p is
 // floored at 1e-30: p = 0 only for an exactly anti-parallel centered key,
-// which cannot collide in exact arithmetic.  Plain logs and exponentials use
-// the hardware log2/exp2 (about 1 ulp); log1p(-P) and the log1p of the
-// tail use log1p_f32, and the expm1 of the closed form, which carries the
-// cancellation, the full-precision routine.
+// which cannot collide in exact arithmetic.  Plain logs, exponentials,
+// reciprocals and square roots use the hardware instructions (about 1 ulp),
+// the cosine's included; log1p(-P) and the log1p of the tail use log1p_f32,
+// and the expm1 of the closed form, which carries the cancellation, the
+// full-precision routine.
 __device__ __forceinline__ float log_u_f32(float p, int K, int L, const float *uc)
 {
     if (K == 0) return 0.0f;
@@ -178,7 +179,7 @@ __device__ __forceinline__ float log_u_f32(float p, int K, int L, const float *u
         const float u = -expm1f(float(L) * a) - LP * __expf(float(L - 1) * a);
         return __logf(u);
     }
-    const float r = P / (1.0f - P);
+    const float r = P * __builtin_amdgcn_rcpf(1.0f - P);
     float f = fmaf(uc[4] * r, 1.0f, 1.0f);
     f = fmaf(uc[3] * r, f, 1.0f);
     f = fmaf(uc[2] * r, f, 1.0f);
@@ -201,7 +202,7 @@ __device__ __forceinline__ float acos_over_pi(float x)
     r = fmaf(r, ax, 0.0889789874f);
     r = fmaf(r, ax, -0.2145988016f);
     r = fmaf(r, ax, 1.5707963050f);
-    r *= sqrtf(1.0f - ax);
+    r *= __builtin_amdgcn_sqrtf(1.0f - ax);
     const float inv_pi = 0.31830988618379067f;
     return x >= 0.0f ? r * inv_pi : 1.0f - r * inv_pi;
 }
@@ -418,8 +419,9 @@ __device__ __forceinline__ void gather_z(const DecodeArgs &a, GatherLds<G, T> &s
                 z = s.srow[e][g] * a.scale;
                 if (!exact) {
                     // q.(k - mu) = q.k - q.mu; a lifted key has norm r
-                    const float den = sqn[g] * (a.rnorm ? sqn[2 * G] : sqrtf(s.srow[e][G]));
-                    float cs = den > 0.0f ? (s.srow[e][g] - sqn[G + g]) / den : 0.0f;
+                    const float den = sqn[g] * (a.rnorm ? sqn[2 * G] : __builtin_amdgcn_sqrtf(s.srow[e][G]));
+                    float cs = den > 0.0f ? (s.srow[e][g] - sqn[G + g]) * __builtin_amdgcn_rcpf(den)
+                                          : 0.0f;
                     cs = fminf(fmaxf(cs, -1.0f), 1.0f);
                     const float pc = 1.0f - acos_over_pi(cs);
                     z -= log_u_f32(pc, a.K, a.L, a.ucoef);
