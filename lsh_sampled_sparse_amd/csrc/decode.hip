@@ -574,8 +574,12 @@ __global__ __launch_bounds__(256) void seg_compact_kernel(const int32_t *__restr
     if (t == 0 && s_len) s_len[bhq] = int32_t(off);
 }
 
-// Workgroups of scan_gather_kernel<G, T, KP> resident at once on the current
-// device (compute units x workgroups per unit), cached per device.
+// Workgroups the grid of scan_gather_kernel<G, T, KP> is sized for on the
+// current device: compute units x workgroups resident per unit, but at most
+// two per unit up to G = 4, cached per device.  Two with longer runs finish
+// sooner there than three: the oldest-first wave scheduler leaves the third
+// workgroup of a unit to run its last chunk nearly alone.  With G = 8 the
+// gather's arithmetic needs the third workgroup's waves.
 template <int G, typename T, int KP>
 int resident_workgroups()
 {
@@ -588,6 +592,7 @@ int resident_workgroups()
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan_gather_kernel<G, T, KP>, 256,
                                                          0) != hipSuccess)
             return 0;
+        if (G <= 4 && per_cu > 2) per_cu = 2;
         cached[dev] = cus * (per_cu > 0 ? per_cu : 1);
     }
     return cached[dev];
