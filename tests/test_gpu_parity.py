@@ -119,8 +119,8 @@ def test_rejects_mismatched_caches():
 
 
 def test_runs_of_two_chunks_every_head():
-    """8 KV heads x 98 chunks = 784 chunks, more than the 768 workgroups that
-    256 CUs hold at 3 a CU: workgroups take runs of two chunks (the gather of
+    """8 KV heads x 98 chunks = 784 chunks, more than the 512 workgroups of the
+    grid (256 CUs, 2 a CU up to G = 4): workgroups take runs of two chunks (the gather of
     one chunk after the next one's scan), and with runs aligned to the KV
     heads each head's last run goes to the first workgroups.  Every key's codes;
     counts, sets and outputs on every query head."""
