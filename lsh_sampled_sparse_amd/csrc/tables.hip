@@ -378,17 +378,19 @@ __global__ __launch_bounds__(256, (table_occupancy<G, T>())) void table_gather_k
     uint32_t once[G], twice[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        // seen twice: in one slice, or once in each of two slices
-        uint32_t o = 0u, w2 = 0u;
+        // Seen twice: in one slice, or once in each of two slices.  The
+        // slices are merged whole words at a time, 16 keys of (twice, once)
+        // bit pairs: once = once_a | once_b, twice = twice_a | twice_b |
+        // (once_a & once_b), the last term moved up from the once bit.
+        uint32_t m = fb[g][0];
 #pragma unroll
-        for (int sl = 0; sl < S; ++sl) {
-            const uint32_t f = fb[g][sl] >> sh;
-            const uint32_t f1 = f & 0x5u, f2 = (f >> 1) & 0x5u;   // 2 keys x 2 bits
-            w2 |= f2 | (o & f1);
-            o |= f1;
+        for (int sl = 1; sl < S; ++sl) {
+            const uint32_t b = fb[g][sl];
+            m = ((m & b & 0x55555555u) << 1) | (m | b);
         }
-        once[g] = o;
-        twice[g] = w2;
+        const uint32_t f = m >> sh;   // this thread's 2 keys x 2 bits
+        once[g] = f & 0x5u;
+        twice[g] = (f >> 1) & 0x5u;
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
