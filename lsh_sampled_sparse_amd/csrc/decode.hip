@@ -4,8 +4,8 @@
 //                  Sampling for Efficient LLM Generation", algorithm steps:
 //                  the query's code from the shared projector).
 //   scan_gather    a workgroup takes a run of 512-key chunks (each of one KV
-//                  head and its G query heads), as many workgroups as are
-//                  resident at once; per chunk:
+//                  head and its G query heads), no more workgroups than are
+//                  resident at once (at most two a CU up to G = 4); per chunk:
 //                  (a) stream the chunk's code planes and mark, per key and
 //                      query head, whether the key shares the query's bucket
 //                      in at least one and in at least two tables (32 keys per
@@ -144,7 +144,7 @@ inline int plane_rows_class(int Kr)
 // One workgroup takes a run of `cpb` consecutive 512-key chunks (numbered
 // over (sequence, KV head) units, then chunks); runs are as equal as the
 // chunk count allows and the grid is no larger than what is resident at
-// once.  Per chunk:
+// once (resident_workgroups).  Per chunk:
 //   (a) scan: thread t takes the 32-key word t % 16 of the chunk in tables
 //       t / 16, t / 16 + 16, ...  For each table and query head, the key
 //       matches iff its K plane bits equal the query's code bits: an AND of
