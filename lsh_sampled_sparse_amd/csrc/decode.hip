@@ -70,13 +70,15 @@ __device__ __forceinline__ uint32_t and_xnor(uint32_t acc, uint32_t p, uint32_t 
 }
 
 // ---------------------------------------------------------------- query codes
-// Block: TB = 64/K whole tables (<= 64 hyperplanes) x kQueryHeads query
-// heads.  Thread = (hyperplane, quarter of the dims): four lanes read one W
-// row together (64 contiguous bytes a load) and keep their 32 dims in
-// registers for all the block's heads, whose queries are LDS broadcasts;
-// two shuffles add the quarters.  Sign bits meet in LDS and are packed per
-// (head, table).
-constexpr int kQueryHeads = 4;
+// Block: TB = 64/K whole tables (<= 64 hyperplanes) x QH query heads.
+// Thread = (hyperplane, quarter of the dims): four lanes read one W row
+// together (64 contiguous bytes a load) and keep their 32 dims in registers
+// for all the block's heads, whose queries are LDS broadcasts; two shuffles
+// add the quarters.  Sign bits meet in LDS and are packed per (head, table).
+// QH = 2 up to 32 query heads (twice the blocks, each with half the dots:
+// the step 0.2-0.3 us shorter at 16K and 96K), 4 beyond (2 was 2.3 us longer
+// at batch 16, 6,400 blocks).
+template <int QH>
 __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restrict__ q,
                                                            int32_t BHq,
                                                            const float *__restrict__ W, int32_t K,
@@ -85,15 +87,15 @@ __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restri
                                                            uint32_t *__restrict__ qq,
                                                            float *__restrict__ qnorm)
 {
-    __shared__ float4 sQ[kQueryHeads][kD / 4];
-    __shared__ uint8_t sbit[kQueryHeads][64];
+    __shared__ float4 sQ[QH][kD / 4];
+    __shared__ uint8_t sbit[QH][64];
     const int t = threadIdx.x, hp = t >> 2, dq = t & 3;
     const int TB = K > 0 ? 64 / K : 64;
     const int l0 = blockIdx.x * TB;
     const int nt = min(TB, L - l0);
     const int nh = nt * K;
-    const int q0 = blockIdx.y * kQueryHeads;
-    const int nq = min(kQueryHeads, BHq - q0);
+    const int q0 = blockIdx.y * QH;
+    const int nq = min(QH, BHq - q0);
     const float4 *q4 = reinterpret_cast<const float4 *>(q + int64_t(q0) * kD);
     if (t < nq * (kD / 4)) sQ[t / (kD / 4)][t % (kD / 4)] = q4[t];
     float4 wr[8];
@@ -639,8 +641,11 @@ hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s)
 {
     const int BHq = a.B * a.H_q;
     const int TB = a.K > 0 ? 64 / a.K : 64;
-    return launch(encode_query_kernel, dim3(ceil_div(a.L, TB), ceil_div(BHq, kQueryHeads)),
-                  dim3(256), 0, s, a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
+    if (BHq <= 32)
+        return launch(encode_query_kernel<2>, dim3(ceil_div(a.L, TB), ceil_div(BHq, 2)), dim3(256),
+                      0, s, a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
+    return launch(encode_query_kernel<4>, dim3(ceil_div(a.L, TB), ceil_div(BHq, 4)), dim3(256), 0,
+                  s, a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
 }
 
 hipError_t launch_merge(const DecodeArgs &a, int32_t cpb, hipStream_t s)
