@@ -492,13 +492,15 @@ __global__ __launch_bounds__(256) void counts_kernel(DecodeArgs a)
 // its runs of `cpb` chunks (cpb = 1: one record a chunk): the unit's chunks
 // [u n_chunks, (u+1) n_chunks) meet runs floor(u n_chunks / cpb) through
 // floor(((u+1) n_chunks - 1) / cpb).  Lane j folds records j, j+32, ... into
-// a running (max, sum, acc) in one pass, loading kMergeBatch records before
-// folding them so their loads overlap; the 32 lanes are then combined in lane
-// order, so the result is deterministic.  16 dims a block (256 blocks at 32
-// query heads) spread the launch over the CUs.
-constexpr int kMergeBatch = 8;
+// a running (max, sum, acc), loading NB records before folding them so their
+// loads overlap; NB is the smallest of 1, 2, 4, 8 that covers a unit's
+// records in one pass (loads past the last record are wasted: 8 a lane at
+// 64 records took the 96K step 0.7 us longer than 2).  The 32 lanes are then
+// combined by a fixed tree (lanes j and j + 16, then j and j + 8, ...), so
+// the result is deterministic.  16 dims a block (256 blocks at 32 query
+// heads) spread the launch over the CUs.
 constexpr int kMergeDims = 16;
-template <int G>
+template <int G, int NB>
 __global__ __launch_bounds__(32 * kMergeDims) void merge_kernel(const float *__restrict__ part,
                                                     int32_t n_chunks, int32_t cpb, int32_t H_kv,
                                                     int32_t H_q, float *__restrict__ out)
@@ -511,10 +513,10 @@ __global__ __launch_bounds__(32 * kMergeDims) void merge_kernel(const float *__r
     const int nrec = int((first + n_chunks - 1) / cpb - first / cpb + 1);
     const float *p = part + first * (G * kPart) + g * kPart;
     float m = -INFINITY, l = 0.0f, acc = 0.0f;
-    for (int base = j; base < nrec; base += 32 * kMergeBatch) {
-        float mb[kMergeBatch], lb[kMergeBatch], ab[kMergeBatch];
+    for (int base = j; base < nrec; base += 32 * NB) {
+        float mb[NB], lb[NB], ab[NB];
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) {
+        for (int u = 0; u < NB; ++u) {
             const int ch = base + 32 * u;
             const float *pc = p + int64_t(min(ch, nrec - 1)) * (G * kPart);
             mb[u] = pc[0];
@@ -523,7 +525,7 @@ __global__ __launch_bounds__(32 * kMergeDims) void merge_kernel(const float *__r
             if (ch >= nrec) mb[u] = -INFINITY;   // past the last record: nothing
         }
 #pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) {
+        for (int u = 0; u < NB; ++u) {
             const float mc = mb[u], lc = lb[u], ac = ab[u];
             if (mc > m) {
                 const float f = __expf(m - mc);      // 0 while m = -inf
@@ -540,20 +542,25 @@ __global__ __launch_bounds__(32 * kMergeDims) void merge_kernel(const float *__r
     sm[j][cl] = m;
     sl[j][cl] = l;
     sa[j][cl] = acc;
-    __syncthreads();
-    if (t < kMergeDims) {
-        float M = -INFINITY;
-        for (int r = 0; r < 32; ++r) M = fmaxf(M, sm[r][t]);
-        float ls = 0.0f, as = 0.0f;
-        if (M != -INFINITY) {
-            for (int r = 0; r < 32; ++r) {
-                const float f = __expf(sm[r][t] - M);
-                ls = fmaf(sl[r][t], f, ls);
-                as = fmaf(sa[r][t], f, as);
+    for (int half = 16; half >= 1; half >>= 1) {
+        __syncthreads();
+        if (j < half) {
+            const float m2 = sm[j + half][cl], l2 = sl[j + half][cl], a2 = sa[j + half][cl];
+            const float M = fmaxf(m, m2);
+            if (M != -INFINITY) {   // both empty: nothing
+                const float f1 = __expf(m - M), f2 = __expf(m2 - M);
+                l = fmaf(l, f1, l2 * f2);
+                acc = fmaf(acc, f1, a2 * f2);
+                m = M;
             }
+            sm[j][cl] = m;
+            sl[j][cl] = l;
+            sa[j][cl] = acc;
         }
+    }
+    if (j == 0) {
         const int b = bkv / H_kv, h = bkv % H_kv;
-        out[(int64_t(b) * H_q + h * G + g) * kD + c] = ls > 0.0f ? as / ls : 0.0f;
+        out[(int64_t(b) * H_q + h * G + g) * kD + c] = l > 0.0f ? acc / l : 0.0f;
     }
 }
 
@@ -648,16 +655,34 @@ hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s)
                   s, a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
 }
 
-hipError_t launch_merge(const DecodeArgs &a, int32_t cpb, hipStream_t s)
+namespace {
+// The merge with NB records a lane per load batch: the smallest of 1, 2, 4, 8
+// whose 32 NB slots hold a unit's records (n_chunks / cpb where runs align
+// with units, else at most ceil(n_chunks / cpb) + 1).
+template <int G>
+hipError_t launch_merge_g(const DecodeArgs &a, int32_t cpb, hipStream_t s)
 {
-    const dim3 grid(a.B * a.H_kv * a.G, kD / kMergeDims), block(32 * kMergeDims);
+    const dim3 grid(a.B * a.H_kv * G, kD / kMergeDims), block(32 * kMergeDims);
     const float *part = a.part;
     const int32_t nc = a.n_chunks;
+    const int64_t nrec = nc % cpb == 0 ? nc / cpb : (int64_t(nc) + cpb - 1) / cpb + 1;
+    if (nrec <= 32)
+        return launch(merge_kernel<G, 1>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
+    if (nrec <= 64)
+        return launch(merge_kernel<G, 2>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
+    if (nrec <= 128)
+        return launch(merge_kernel<G, 4>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
+    return launch(merge_kernel<G, 8>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
+}
+}  // namespace
+
+hipError_t launch_merge(const DecodeArgs &a, int32_t cpb, hipStream_t s)
+{
     switch (a.G) {
-    case 1: return launch(merge_kernel<1>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
-    case 2: return launch(merge_kernel<2>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
-    case 4: return launch(merge_kernel<4>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
-    case 8: return launch(merge_kernel<8>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
+    case 1: return launch_merge_g<1>(a, cpb, s);
+    case 2: return launch_merge_g<2>(a, cpb, s);
+    case 4: return launch_merge_g<4>(a, cpb, s);
+    case 8: return launch_merge_g<8>(a, cpb, s);
     default: return hipErrorInvalidValue;
     }
 }
