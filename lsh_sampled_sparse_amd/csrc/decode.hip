@@ -20,15 +20,16 @@
 //                      to the centered key, u_i = P[Binomial(L, p^K) >= 2],
 //                      z = q.k*scale - log u (z = q.k*scale on T), and run an
 //                      online softmax per query head (algorithm steps: one
-//                      softmax over [w_S, w_T]/sqrt(d) - log[u, 1]); the
-//                      chunk's partial softmax (max, sum, unnormalised
-//                      accumulator) per head goes to scratch.
+//                      softmax over [w_S, w_T]/sqrt(d) - log[u, 1]) that
+//                      carries on over the run's chunks of one unit; the
+//                      partial softmax (max, sum, unnormalised accumulator)
+//                      per head goes to scratch, one record a run and unit.
 //                  The code stream runs two batches ahead across chunks, and
 //                  (c) runs one chunk late, so a chunk's rows arrive while the
 //                  next chunk is scanned.
 //   counts         (debug only) the exact collision count of every key and
 //                  query head, from the planes.
-//   merge          log-sum-exp merge of the chunk partials of every query head
+//   merge          log-sum-exp merge of the partial records of every query head
 //                  (system co-design: partial attention outputs are merged
 //                  recursively).  A kernel of its own: its launch boundary is
 //                  what makes the partials of blocks on other XCDs visible,
@@ -158,7 +159,8 @@ inline int plane_rows_class(int Kr)
 //   (c) gather-SNIS over the list, run one chunk late, when the rows have
 //       long arrived: with bf16 rows the first round's dots and z inside the
 //       next chunk's scan and the rest after it, with fp32 rows all of it
-//       after the scan.  The chunk's partial softmax goes to `part`.
+//       after the scan.  The chunk folds into the run's partial softmax of its
+//       unit, which goes to `part` when the unit's chunks of the run end.
 // Each thread reads its tables of all chunks of the run as one stream, one
 // table (KP plane words) per batch, in two alternating register buffers
 // issued two batches ahead across chunk boundaries.  Every load on the main

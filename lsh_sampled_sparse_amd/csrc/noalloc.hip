@@ -11,7 +11,7 @@
 // handed to kernels.  Every call on a GPU uses that GPU's one array, so calls
 // that overlap on one GPU (other streams, other threads) race: order them on
 // one stream.  The decode writes every scratch word before it reads it in the
-// same call (query codes, norms, chunk partials), so nothing in the array has
+// same call (query codes, norms, partial records), so nothing in the array has
 // to start at zero; it keeps whatever the last call left.
 #include "mp_internal.h"
 
