@@ -495,7 +495,7 @@ __global__ __launch_bounds__(256) void counts_kernel(DecodeArgs a)
 // [u n_chunks, (u+1) n_chunks) meet runs floor(u n_chunks / cpb) through
 // floor(((u+1) n_chunks - 1) / cpb).  Lane j folds records j, j+32, ... into
 // a running (max, sum, acc), loading NB records before folding them so their
-// loads overlap; NB is the smallest of 1, 2, 4, 8 that covers a unit's
+// loads overlap; NB is the smallest of 1, 2, 3, 4, 6, 8 that covers a unit's
 // records in one pass (loads past the last record are wasted: 8 a lane at
 // 64 records took the 96K step 0.7 us longer than 2).  The 32 lanes are then
 // combined by a fixed tree (lanes j and j + 16, then j and j + 8, ...), so
@@ -658,9 +658,9 @@ hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s)
 }
 
 namespace {
-// The merge with NB records a lane per load batch: the smallest of 1, 2, 4, 8
-// whose 32 NB slots hold a unit's records (n_chunks / cpb where runs align
-// with units, else at most ceil(n_chunks / cpb) + 1).
+// The merge with NB records a lane per load batch: the smallest of 1, 2, 3,
+// 4, 6, 8 whose 32 NB slots hold a unit's records (n_chunks / cpb where runs
+// align with units, else at most ceil(n_chunks / cpb) + 1).
 template <int G>
 hipError_t launch_merge_g(const DecodeArgs &a, int32_t cpb, hipStream_t s)
 {
@@ -672,8 +672,12 @@ hipError_t launch_merge_g(const DecodeArgs &a, int32_t cpb, hipStream_t s)
         return launch(merge_kernel<G, 1>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
     if (nrec <= 64)
         return launch(merge_kernel<G, 2>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
+    if (nrec <= 96)
+        return launch(merge_kernel<G, 3>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
     if (nrec <= 128)
         return launch(merge_kernel<G, 4>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
+    if (nrec <= 192)
+        return launch(merge_kernel<G, 6>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
     return launch(merge_kernel<G, 8>, grid, block, 0, s, part, nc, cpb, a.H_kv, a.H_q, a.out);
 }
 }  // namespace
