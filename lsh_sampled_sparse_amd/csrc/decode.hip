@@ -141,7 +141,7 @@ constexpr int scan_occupancy() { return G <= 2 || (G == 4 && sizeof(T) == 2) ? M
 // (rows past Kr re-read row Kr - 1, which changes nothing).
 inline int plane_rows_class(int Kr)
 {
-    return Kr <= 4 ? 4 : Kr <= 8 ? 8 : Kr <= 10 ? 10 : Kr <= 12 ? 12 : 16;
+    return Kr <= 4 ? 4 : Kr <= 8 ? 8 : Kr <= 9 ? 9 : Kr <= 10 ? 10 : Kr <= 12 ? 12 : 16;
 }
 
 // One workgroup takes a run of `cpb` consecutive 512-key chunks (numbered
@@ -629,6 +629,7 @@ hipError_t launch_scan_gather_kp(const DecodeArgs &a, hipStream_t s, int32_t &cp
     switch (plane_rows_class(a.Kr)) {
     case 4: return launch_scan_gather_t<G, T, 4>(a, s, cpb);
     case 8: return launch_scan_gather_t<G, T, 8>(a, s, cpb);
+    case 9: return launch_scan_gather_t<G, T, 9>(a, s, cpb);
     case 10: return launch_scan_gather_t<G, T, 10>(a, s, cpb);
     case 12: return launch_scan_gather_t<G, T, 12>(a, s, cpb);
     default: return launch_scan_gather_t<G, T, 16>(a, s, cpb);
