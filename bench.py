@@ -347,57 +347,67 @@ def append_leg(cfg, state, steps, warmup, sh, dev):
     """A decode that grows its index every step, as when a token leaves the
     exact local window: per layer an index over the first n - g keys with room
     for n (g = the appends it will see), then each step appends the next key
-    (mp_index_append) and decodes over the longer prefix (mp_decode_attn).
-    Views and arguments are made before the timed region."""
+    and decodes over the longer prefix, in one call (mp_decode_attn_append:
+    the key's codes written by the decode's query-encode launch) and, for
+    comparison, as two (mp_index_append + mp_decode_attn).  Views and
+    arguments are made before the timed region."""
     import torch
     import lsh_sampled_sparse_amd as mp
     from lsh_sampled_sparse_amd import capi
     layers = len(state)
     grow = (warmup + steps + layers - 1) // layers + 1
-    plan, idxs = [], []
-    for l, st in enumerate(state):
-        n0 = cfg.n - grow
-        idx = mp.build_index(st["k"][:, :, :n0], cfg.K, cfg.L, cfg.hyperplane_seed(l),
-                             capacity=cfg.n)
-        idxs.append(idx)
-    torch.cuda.synchronize()
-    count = [0] * layers
-    for i in range(warmup + steps):
-        l = i % layers
-        count[l] += 1
-        n_i = cfg.n - grow + count[l]
-        st = state[l]
-        kv = mp.kv_view(st["k"][:, :, :n_i])
-        vv = mp.kv_view(st["v"][:, :, :n_i])
-        plan.append((idxs[l].handle, kv, vv, st["q"].data_ptr(), st["out"].data_ptr(),
-                     st["scratch"].data_ptr(), st["scratch"].numel()))
 
-    def step(i, eb=None, ee=None):
-        h, kv, vv, q, out, scr, nscr = plan[i]
-        capi.mp_index_append(h, kv, sh)
-        args = (q, cfg.H_q, h, kv, vv, cfg.n_sink, cfg.n_local, 0.0, out, scr, nscr, sh)
-        if eb is None:
-            capi.mp_decode_attn(*args)
-        else:
-            capi.mp_decode_attn_timed(*args, eb, ee)
+    def run(fused):
+        plan, idxs = [], []
+        for l, st in enumerate(state):
+            n0 = cfg.n - grow
+            idx = mp.build_index(st["k"][:, :, :n0], cfg.K, cfg.L, cfg.hyperplane_seed(l),
+                                 capacity=cfg.n)
+            idxs.append(idx)
+        torch.cuda.synchronize()
+        count = [0] * layers
+        for i in range(warmup + steps):
+            l = i % layers
+            count[l] += 1
+            n_i = cfg.n - grow + count[l]
+            st = state[l]
+            kv = mp.kv_view(st["k"][:, :, :n_i])
+            vv = mp.kv_view(st["v"][:, :, :n_i])
+            plan.append((st["q"].data_ptr(), cfg.H_q, idxs[l].handle, kv, vv, cfg.n_sink,
+                         cfg.n_local, 0.0, st["out"].data_ptr(), st["scratch"].data_ptr(),
+                         st["scratch"].numel(), sh))
 
-    # time_steps runs the steps twice (plain, then with events); the index
-    # would grow past its room, so only the plain pass is used here.
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        step(warmup + i)
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1)
-    del idxs, plan
+        def step(i):
+            a = plan[i]
+            if fused:
+                capi.mp_decode_attn_append(*a)
+            else:
+                capi.mp_index_append(a[2], a[3], sh)
+                capi.mp_decode_attn(*a)
+
+        # each index grows as it is stepped: warmup and the timed steps
+        # continue one sequence of appends
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            step(warmup + i)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        del idxs, plan
+        return ms
+
+    ms2 = run(False)
+    ms = run(True)
     return {"value": round(steps / (ms / 1e3), 2), "unit": "decode layer-steps/s",
             "ms_per_step": round(ms / steps, 5), "keys_appended_per_step": 1,
-            "what": "mp_index_append of one key (its bits written into the plane words) + "
-                    "mp_decode_attn"}
+            "what": "mp_decode_attn_append: one key appended (its bits written into the plane "
+                    "words by the query-encode launch) and the decode over the grown index",
+            "two_calls_ms_per_step": round(ms2 / steps, 5),
+            "two_calls": "mp_index_append of the key, then mp_decode_attn"}
 
 
 def tables_leg(cfg, state, layers, steps, warmup, sh, dev):

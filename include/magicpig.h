@@ -171,8 +171,10 @@ mp_status mp_build_index_cap(const mp_kv_view *keys, int32_t K, int32_t L, uint6
  * index built with MP_INDEX_MIPS. */
 mp_status mp_index_append(mp_index *idx, const mp_kv_view *keys, void *stream);
 
-/* Bytes of device scratch one mp_decode_attn / mp_decode_debug call needs
- * for H_q query heads per sequence; 0 if invalid. */
+/* Bytes of device scratch one mp_decode_attn / mp_decode_debug /
+ * mp_decode_attn_append call needs for H_q query heads per sequence, for the
+ * index grown to its capacity n_cap (so one scratch serves every call as the
+ * index grows; n_cap = n for an index built without room); 0 if invalid. */
 size_t mp_decode_scratch_bytes(const mp_index *idx, int32_t H_q);
 
 /* One decode step for every (sequence, query head).
@@ -189,6 +191,30 @@ mp_status mp_decode_attn(const float *q, int32_t H_q, const mp_index *idx,
                          const mp_kv_view *k, const mp_kv_view *v,
                          int32_t n_sink, int32_t n_local, float scale, float *out,
                          void *scratch, size_t scratch_bytes, void *stream);
+
+/* mp_index_append(idx, k, stream) followed by mp_decode_attn over the grown
+ * index, with the new keys' codes written by the decode's first launch: one
+ * kernel launch fewer a step for a decode that appends the token leaving the
+ * exact local window (page "MagicPIG: LSH Sampling for Efficient LLM
+ * Generation", system co-design: the sink and local tokens sit in a static
+ * cache beside the hashed keys).
+ *   k, v   the key and value caches viewed with the new length n_new:
+ *          [B][H_kv][n_new][128]; index's n <= n_new <= n_cap, and the first
+ *          n keys of k must be the ones indexed
+ *   other arguments as mp_decode_attn; scratch >= mp_decode_scratch_bytes.
+ * 1 to 64 new keys ride on the decode's query-encode launch; more keys, or
+ * K = 0, take mp_index_append and then mp_decode_attn.  Either way the
+ * results are bit-identical to the two calls.  Every argument is checked
+ * before anything is enqueued: a refused call (MP_E_HANDLE, MP_E_ARG for a
+ * lifted index or another device, MP_E_DTYPE, MP_E_SHAPE, MP_E_WORKSPACE)
+ * leaves the index unchanged.  MP_E_HIP (a failed launch) may leave the new
+ * keys' bits in plane words past n, which no decode reads, or, on the
+ * two-call route, the index grown.  Like mp_index_append it changes the index
+ * (n, detached tables): no other call on the index may overlap it. */
+mp_status mp_decode_attn_append(const float *q, int32_t H_q, mp_index *idx,
+                                const mp_kv_view *k, const mp_kv_view *v, int32_t n_sink,
+                                int32_t n_local, float scale, float *out, void *scratch,
+                                size_t scratch_bytes, void *stream);
 
 /* Bytes of the static device array behind mp_decode_attn_noalloc. */
 #define MP_NOALLOC_SCRATCH_BYTES (32u << 20)

@@ -235,6 +235,31 @@ def decode_attn(q, index, k, v, n_sink, n_local, scale=0.0, out=None, scratch=No
     return _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, False)
 
 
+def decode_attn_append(q, index, k, v, n_sink, n_local, scale=0.0, out=None, scratch=None,
+                       stream=None):
+    """Grow `index` to the keys of k [B][H_kv][n_new][128] and decode over
+    them in one call (see mp_decode_attn_append): out [B][H_q][128] fp32.
+    Detaches any bucketed tables."""
+    if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3:
+        raise ValueError("q must be a contiguous [B][H_q][128] float32 tensor")
+    B, H_q, d = q.shape
+    if out is None:
+        out = torch.empty(B, H_q, d, dtype=torch.float32, device=q.device)
+    need = index.scratch_bytes(H_q)
+    if need == 0:
+        raise ValueError(f"H_q={H_q} does not fit the index (H_kv={index.H_kv})")
+    if scratch is None:
+        scratch = torch.empty(need, dtype=torch.uint8, device=q.device)
+    kv_k, kv_v = kv_view(k), kv_view(v)
+    _keep_alive_on(_side_stream(stream, q.device), out, scratch, index.workspace)
+    capi.mp_decode_attn_append(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local,
+                               float(scale), out.data_ptr(), scratch.data_ptr(), scratch.numel(),
+                               _stream(stream))
+    index.n = k.shape[2]
+    index.tables = None
+    return out
+
+
 def decode_debug(q, index, k, v, n_sink, n_local, scale=0.0, out=None, scratch=None,
                  stream=None):
     """decode_attn plus qcodes, counts, s_idx, s_len (see mp_decode_debug)."""

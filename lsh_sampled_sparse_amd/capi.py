@@ -25,7 +25,7 @@ EXPORTED = [
     "mp_decode_attn_tables", "mp_decode_attn_tables_timed", "mp_decode_tables_debug",
     "mp_tables_views", "mp_build_index_cap", "mp_index_append", "mp_index_workspace_bytes_ex",
     "mp_build_index_ex", "mp_index_lift_views", "mp_stream_read", "mp_debug_fail_launches",
-    "mp_decode_attn_noalloc",
+    "mp_decode_attn_noalloc", "mp_decode_attn_append",
 ]
 
 
@@ -81,6 +81,8 @@ def lib():
                vp, vp, sz, vp]
         L.mp_decode_attn.restype = C.c_int
         L.mp_decode_attn.argtypes = dec
+        L.mp_decode_attn_append.restype = C.c_int
+        L.mp_decode_attn_append.argtypes = dec
         L.mp_decode_attn_noalloc.restype = C.c_int
         L.mp_decode_attn_noalloc.argtypes = [vp, i32, vp, C.POINTER(mp_kv_view),
                                              C.POINTER(mp_kv_view), i32, i32, C.c_float, vp, vp]
@@ -192,6 +194,14 @@ def mp_decode_attn(q: int, H_q: int, idx: int, k: mp_kv_view, v: mp_kv_view, n_s
     st = lib().mp_decode_attn(q, H_q, idx, C.byref(k), C.byref(v), n_sink, n_local, scale, out,
                               scratch, scratch_bytes, stream)
     _check(st, "mp_decode_attn")
+
+
+def mp_decode_attn_append(q: int, H_q: int, idx: int, k: mp_kv_view, v: mp_kv_view, n_sink: int,
+                          n_local: int, scale: float, out: int, scratch: int, scratch_bytes: int,
+                          stream: int) -> None:
+    st = lib().mp_decode_attn_append(q, H_q, idx, C.byref(k), C.byref(v), n_sink, n_local, scale,
+                                     out, scratch, scratch_bytes, stream)
+    _check(st, "mp_decode_attn_append")
 
 
 def mp_decode_attn_noalloc(q: int, H_q: int, idx: int, k: mp_kv_view, v: mp_kv_view,

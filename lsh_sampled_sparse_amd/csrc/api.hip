@@ -179,11 +179,14 @@ mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx, const 
                         const mp_kv_view *v, int32_t n_sink, int32_t n_local, float scale,
                         float *out, void *scratch, size_t scratch_bytes, void *stream, bool debug,
                         uint16_t *qcodes, uint8_t *counts, int32_t *s_idx, int32_t *s_len,
-                        void *ev_begin, void *ev_end, bool tables)
+                        void *ev_begin, void *ev_end, bool tables, int32_t n_new,
+                        bool check_only)
 {
     g_err[0] = 0;
     if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
-    const IndexLayout &lay = idx->lay;
+    // the layout the decode runs on: the index's, or the index grown to n_new
+    IndexLayout lay = idx->lay;
+    if (n_new >= 0) set_index_keys(lay, n_new);
     if (tables && !idx->tab_off)
         return fail(MP_E_ARG, "the index has no bucketed tables: call mp_build_tables first");
     if (!q || !out) return fail(MP_E_ARG, "q and out must be non-NULL");
@@ -220,6 +223,7 @@ mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx, const 
     if (scratch_bytes < size_t(dl.total))
         return fail(MP_E_WORKSPACE, "scratch holds %zu bytes, %lld needed", scratch_bytes,
                     (long long)dl.total);
+    if (check_only) return MP_OK;
 
     char *sp = static_cast<char *>(scratch);
     DecodeArgs a{};
@@ -249,6 +253,8 @@ mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx, const 
     a.qcodes = reinterpret_cast<uint16_t *>(sp + dl.off_qcodes);
     a.qq = reinterpret_cast<uint32_t *>(sp + dl.off_qq);
     a.qnorm = reinterpret_cast<float *>(sp + dl.off_qnorm);
+    a.app_n0 = n_new >= 0 ? idx->lay.n : lay.n;
+    a.app_planes = idx->planes;
     a.part = reinterpret_cast<float *>(sp + dl.off_part);
     a.seg_idx = reinterpret_cast<int32_t *>(sp + dl.off_seg_idx);
     a.seg_cnt = reinterpret_cast<int32_t *>(sp + dl.off_seg_cnt);
@@ -455,7 +461,9 @@ mp_status mp_index_append(mp_index *idx, const mp_kv_view *keys, void *stream)
 size_t mp_decode_scratch_bytes(const mp_index *idx, int32_t H_q)
 {
     if (!live(idx) || H_q < 1 || H_q % idx->lay.H_kv) return 0;
-    return size_t(decode_layout(idx->lay, H_q, false, true).total);
+    IndexLayout cap = idx->lay;   // grown to its capacity: one scratch serves every size
+    set_index_keys(cap, cap.n_cap);
+    return size_t(decode_layout(cap, H_q, false, true).total);
 }
 
 mp_status mp_decode_attn(const float *q, int32_t H_q, const mp_index *idx, const mp_kv_view *k,
@@ -464,6 +472,47 @@ mp_status mp_decode_attn(const float *q, int32_t H_q, const mp_index *idx, const
 {
     return decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
                          stream, false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false);
+}
+
+mp_status mp_decode_attn_append(const float *q, int32_t H_q, mp_index *idx, const mp_kv_view *k,
+                                const mp_kv_view *v, int32_t n_sink, int32_t n_local, float scale,
+                                float *out, void *scratch, size_t scratch_bytes, void *stream)
+{
+    g_err[0] = 0;
+    if (!live(idx)) return fail(MP_E_HANDLE, "index handle is NULL or not a live index");
+    const IndexLayout &lay = idx->lay;
+    mp_status st = check_view(k, "k");
+    if (st != MP_OK) return st;
+    if (k->n == lay.n)   // nothing to add
+        return mp_decode_attn(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch,
+                              scratch_bytes, stream);
+    if (lay.flags & MP_INDEX_MIPS)
+        return fail(MP_E_ARG, "an index built with MP_INDEX_MIPS does not grow");
+    if (k->n < lay.n)
+        return fail(MP_E_SHAPE, "k holds %d keys, fewer than the %d indexed", k->n, lay.n);
+    if (k->n > lay.n_cap)
+        return fail(MP_E_SHAPE, "%d keys exceed the index capacity %d", k->n, lay.n_cap);
+    // every argument of the decode over the grown index, before anything changes
+    st = decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
+                       stream, false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false,
+                       k->n, true);
+    if (st != MP_OK) return st;
+    if (k->n - lay.n > kAppendMax || lay.K == 0) {
+        // many keys, or no bits to write: the two calls
+        st = mp_index_append(idx, k, stream);
+        if (st != MP_OK) return st;
+        return mp_decode_attn(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch,
+                              scratch_bytes, stream);
+    }
+    // 1 to kAppendMax new keys: their codes ride on the decode's query encode
+    st = decode_common(q, H_q, idx, k, v, n_sink, n_local, scale, out, scratch, scratch_bytes,
+                       stream, false, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, false,
+                       k->n);
+    if (st != MP_OK) return st;
+    set_index_keys(idx->lay, k->n);
+    idx->tab_off = nullptr;    // tables of the old keys no longer describe the index
+    idx->tab_ent = nullptr;
+    return MP_OK;
 }
 
 mp_status mp_decode_attn_timed(const float *q, int32_t H_q, const mp_index *idx,

@@ -38,6 +38,7 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include "append_codes.h"
 #include "gather_common.h"
 
 namespace mp {
@@ -80,22 +81,20 @@ __device__ __forceinline__ uint32_t and_xnor(uint32_t acc, uint32_t p, uint32_t 
 // the step 0.2-0.3 us shorter at 16K and 96K), 4 beyond (2 was 2.3 us longer
 // at batch 16, 6,400 blocks).
 template <int QH>
-__global__ __launch_bounds__(256) void encode_query_kernel(const float *__restrict__ q,
-                                                           int32_t BHq,
-                                                           const float *__restrict__ W, int32_t K,
-                                                           int32_t L,
-                                                           uint16_t *__restrict__ qcodes,
-                                                           uint32_t *__restrict__ qq,
-                                                           float *__restrict__ qnorm)
+__device__ __forceinline__ void encode_query_block(const float *__restrict__ q, int32_t BHq,
+                                                   const float *__restrict__ W, int32_t K,
+                                                   int32_t L, uint16_t *__restrict__ qcodes,
+                                                   uint32_t *__restrict__ qq,
+                                                   float *__restrict__ qnorm, int bx, int by,
+                                                   float4 (*sQ)[kD / 4], uint8_t (*sbit)[64],
+                                                   int t)
 {
-    __shared__ float4 sQ[QH][kD / 4];
-    __shared__ uint8_t sbit[QH][64];
-    const int t = threadIdx.x, hp = t >> 2, dq = t & 3;
+    const int hp = t >> 2, dq = t & 3;
     const int TB = K > 0 ? 64 / K : 64;
-    const int l0 = blockIdx.x * TB;
+    const int l0 = bx * TB;
     const int nt = min(TB, L - l0);
     const int nh = nt * K;
-    const int q0 = blockIdx.y * QH;
+    const int q0 = by * QH;
     const int nq = min(QH, BHq - q0);
     const float4 *q4 = reinterpret_cast<const float4 *>(q + int64_t(q0) * kD);
     if (t < nq * (kD / 4)) sQ[t / (kD / 4)][t % (kD / 4)] = q4[t];
@@ -107,7 +106,7 @@ __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restri
         for (int c = 0; c < 8; ++c) wr[c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
     __syncthreads();
-    if (blockIdx.x == 0) {         // |q| of the block's heads, for the cosines
+    if (bx == 0) {                 // |q| of the block's heads, for the cosines
         const int j = t >> 5, c4 = t & 31;
         const float nrm = norm32(j < nq ? sQ[j][c4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f));
         if (j < nq && c4 == 0) qnorm[q0 + j] = nrm;
@@ -124,6 +123,48 @@ __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restri
         const int64_t o = int64_t(q0 + qj) * L + l0 + tl;
         qcodes[o] = uint16_t(code);
         qq[o] = code | (code << 16);
+    }
+}
+
+template <int QH>
+__global__ __launch_bounds__(256) void encode_query_kernel(const float *__restrict__ q,
+                                                           int32_t BHq,
+                                                           const float *__restrict__ W, int32_t K,
+                                                           int32_t L,
+                                                           uint16_t *__restrict__ qcodes,
+                                                           uint32_t *__restrict__ qq,
+                                                           float *__restrict__ qnorm)
+{
+    __shared__ float4 sQ[QH][kD / 4];
+    __shared__ uint8_t sbit[QH][64];
+    encode_query_block<QH>(q, BHq, W, K, L, qcodes, qq, qnorm, blockIdx.x, blockIdx.y, sQ, sbit,
+                           threadIdx.x);
+}
+
+// The query encode and an append of a few keys (append_codes.h) in one
+// launch, for a decode that first grows its index: blocks [0, n_enc) are the
+// encode blocks (bx = b % nbx, by = b / nbx), the rest the append's blocks
+// (unit, hyperplane block of 256).  The two write disjoint memory; the scan
+// that reads both comes after the launch.
+template <int QH, typename T>
+__global__ __launch_bounds__(256) void encode_append_kernel(
+    const float *__restrict__ q, int32_t BHq, const float *__restrict__ W, int32_t K, int32_t L,
+    uint16_t *__restrict__ qcodes, uint32_t *__restrict__ qq, float *__restrict__ qnorm,
+    int32_t nbx, int32_t n_enc, const T *__restrict__ keys, int64_t sb, int64_t sh, int64_t sn,
+    int32_t H, int32_t n0, int32_t n1, int32_t nc_cap, const float *__restrict__ mu,
+    uint32_t *__restrict__ planes, int32_t nhb)
+{
+    __shared__ __align__(16) float sx[kAppendMax][kD];   // the encode's LDS is carved from it
+    static_assert(QH * (kD / 4) * 16 + QH * 64 <= sizeof(sx), "encode LDS fits");
+    const int b = blockIdx.x, t = threadIdx.x;
+    if (b < n_enc) {
+        float4(*sQ)[kD / 4] = reinterpret_cast<float4(*)[kD / 4]>(&sx[0][0]);
+        uint8_t(*sbit)[64] = reinterpret_cast<uint8_t(*)[64]>(&sx[QH][0]);
+        encode_query_block<QH>(q, BHq, W, K, L, qcodes, qq, qnorm, b % nbx, b / nbx, sQ, sbit, t);
+    } else {
+        const int ab = b - n_enc;
+        append_codes_block<T>(keys, sb, sh, sn, H, n0, n1, nc_cap, mu, W, K, L, planes, ab / nhb,
+                              ab % nhb, t, sx);
     }
 }
 
@@ -647,6 +688,34 @@ hipError_t launch_scan_gather(const DecodeArgs &a, hipStream_t s, int32_t &cpb)
 }  // namespace
 
 // ---- launches shared with the bucketed-table path (tables.hip) ----
+namespace {
+template <int QH, typename T>
+hipError_t launch_encode_append_t(const DecodeArgs &a, hipStream_t s)
+{
+    const int BHq = a.B * a.H_q;
+    const int TB = a.K > 0 ? 64 / a.K : 64;
+    const int nbx = ceil_div(a.L, TB), n_enc = nbx * ceil_div(BHq, QH);
+    const int nhb = ceil_div(int64_t(a.K) * a.L, kAppendRows);
+    const int units = a.B * a.H_kv;
+    return launch(encode_append_kernel<QH, T>, dim3(n_enc + units * nhb), dim3(256), 0, s, a.q, BHq,
+                  a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm, nbx, n_enc,
+                  static_cast<const T *>(a.k.data), a.k.sb, a.k.sh, a.k.sn, a.H_kv, a.app_n0, a.n,
+                  a.nc_cap, a.mu, a.app_planes, nhb);
+}
+
+// The query encode with the append of keys [app_n0, n) (1 to kAppendMax, K > 0).
+hipError_t launch_encode_append(const DecodeArgs &a, hipStream_t s)
+{
+    if (a.n - a.app_n0 < 1 || a.n - a.app_n0 > kAppendMax || a.K <= 0 || !a.app_planes)
+        return hipErrorInvalidValue;
+    const bool small = a.B * a.H_q <= 32;
+    if (a.dtype == MP_BF16)
+        return small ? launch_encode_append_t<2, uint16_t>(a, s)
+                     : launch_encode_append_t<4, uint16_t>(a, s);
+    return small ? launch_encode_append_t<2, float>(a, s) : launch_encode_append_t<4, float>(a, s);
+}
+}  // namespace
+
 hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s)
 {
     const int BHq = a.B * a.H_q;
@@ -716,7 +785,9 @@ hipError_t launch_seg_compact(const DecodeArgs &a, hipStream_t s)
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
 {
-    hipError_t e = launch_encode_query(a, s);
+    // a decode that first appends keys [app_n0, n) writes their codes in the
+    // query encode's launch
+    hipError_t e = a.app_n0 < a.n ? launch_encode_append(a, s) : launch_encode_query(a, s);
     if (e != hipSuccess) return e;
     int32_t cpb = 1;
     switch (a.G) {

@@ -10,6 +10,7 @@
 //                 K x L vectors), stored as bit planes: per 512-key chunk and
 //                 hyperplane j = l*K + b, 16 words whose bit i is bit b of the
 //                 table-l code of key 32w + i.  A code costs its K bits.
+#include "append_codes.h"
 #include "mp_internal.h"
 
 namespace mp {
@@ -423,15 +424,9 @@ hipError_t launch_encode_keys(const KVRows &keys, int32_t dtype, int32_t B, int3
 namespace {
 
 // ---------------------------------------------------------------- small appends
-// Codes of keys [n0, n1) (at most kAppendMax new keys) of unit blockIdx.y;
-// thread = hyperplane r = blockIdx.x * 256 + threadIdx.x.  The new keys'
-// centered rows x = k - mu (fp32, the build's mu) are staged in LDS; each
-// thread forms r's projection of every new key (fp32) and writes the sign
-// bits into the words of its plane row l*K + b, one read-modify-write per
-// word: a word holds one row's bits of 32 keys, so no other thread writes it,
-// and the bits of the keys already indexed are kept.  The work is that of the
-// new keys alone, where re-encoding their 256-key block costs the MFMA work
-// of 256 keys on one workgroup per unit.
+// One block of append_codes_block (append_codes.h) per (hyperplane block,
+// unit).  The work is that of the new keys alone, where re-encoding their
+// 256-key block costs the MFMA work of 256 keys on one workgroup per unit.
 template <typename T>
 __global__ __launch_bounds__(256) void append_codes_kernel(const T *__restrict__ keys, int64_t sb,
                                                            int64_t sh, int64_t sn, int32_t H,
@@ -441,50 +436,8 @@ __global__ __launch_bounds__(256) void append_codes_kernel(const T *__restrict__
                                                            int32_t L, uint32_t *__restrict__ planes)
 {
     __shared__ __align__(16) float sx[kAppendMax][kD];
-    const int u = blockIdx.y, t = threadIdx.x, nk = n1 - n0;
-    const T *kb = keys + (u / H) * sb + (u % H) * sh;
-    const float *mu_u = mu + int64_t(u) * kD;
-    for (int i = t; i < nk * kD; i += 256) {
-        const int e = i / kD, d = i % kD;
-        const T v = kb[int64_t(n0 + e) * sn + d];
-        float f;
-        if constexpr (sizeof(T) == 2) f = bf16_to_f32(v);
-        else f = v;
-        sx[e][d] = f - mu_u[d];
-    }
-    __syncthreads();
-    const int r = blockIdx.x * 256 + t;
-    if (r >= K * L) return;
-    const float4 *w4 = reinterpret_cast<const float4 *>(W + int64_t(r) * kD);
-    uint32_t *row = planes + (int64_t(u) * nc_cap * (L * K) + r) * kWords;
-    const int64_t chunk_stride = int64_t(L) * K * kWords;
-    uint32_t *cur = nullptr, mask = 0u, val = 0u;
-    for (int e = 0; e < nk; ++e) {
-        const float4 *x4 = reinterpret_cast<const float4 *>(sx[e]);
-        float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll 8
-        for (int c = 0; c < kD / 4; c += 2) {
-            const float4 w0 = w4[c], x0 = x4[c], w1 = w4[c + 1], x1 = x4[c + 1];
-            a0 = fmaf(w0.x, x0.x, a0);
-            a0 = fmaf(w0.y, x0.y, a0);
-            a0 = fmaf(w0.z, x0.z, a0);
-            a0 = fmaf(w0.w, x0.w, a0);
-            a1 = fmaf(w1.x, x1.x, a1);
-            a1 = fmaf(w1.y, x1.y, a1);
-            a1 = fmaf(w1.z, x1.z, a1);
-            a1 = fmaf(w1.w, x1.w, a1);
-        }
-        const int i = n0 + e;
-        uint32_t *addr = row + (i / kChunk) * chunk_stride + (i % kChunk) / 32;
-        if (addr != cur) {
-            if (cur) *cur = (*cur & ~mask) | val;
-            cur = addr;
-            mask = val = 0u;
-        }
-        mask |= 1u << (i & 31);
-        if (a0 + a1 > 0.0f) val |= 1u << (i & 31);
-    }
-    if (cur) *cur = (*cur & ~mask) | val;
+    append_codes_block<T>(keys, sb, sh, sn, H, n0, n1, nc_cap, mu, W, K, L, planes, blockIdx.y,
+                          blockIdx.x, threadIdx.x, sx);
 }
 
 }  // namespace
@@ -495,7 +448,7 @@ hipError_t launch_append_codes(const KVRows &keys, int32_t dtype, int32_t B, int
 {
     if (n1 <= n0 || K <= 0) return hipSuccess;
     if (n1 - n0 > kAppendMax) return hipErrorInvalidValue;
-    const dim3 grid(ceil_div(int64_t(K) * L, 256), B * H);
+    const dim3 grid(ceil_div(int64_t(K) * L, kAppendRows), B * H);
     if (dtype == MP_BF16)
         return launch(append_codes_kernel<uint16_t>, grid, dim3(256), 0, s,
                       static_cast<const uint16_t *>(keys.data), keys.sb, keys.sh, keys.sn, H, n0, n1,

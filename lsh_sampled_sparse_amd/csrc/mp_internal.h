@@ -232,6 +232,8 @@ struct DecodeArgs {
     uint16_t *qcodes;        // scratch [BHq][L]
     uint32_t *qq;            // scratch [BHq][L], code | code << 16
     float *qnorm;            // scratch [BHq], |q|
+    int32_t app_n0;          // keys [app_n0, n) are appended by this call (app_n0 = n: none)
+    uint32_t *app_planes;    // the index's planes, written by that append
     float *part;             // scratch [B*H_kv][n_chunks][G][kD + 2] partial records (a chunk, or a run's chunks of one unit)
     int32_t *seg_idx;        // scratch [BHq][n_chunks * kChunk] (debug only)
     int32_t *seg_cnt;        // scratch [BHq][n_chunks] (debug only)
@@ -248,11 +250,16 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 mp_status fail(mp_status s, const char *fmt, ...);
 // Validation and launch of every decode entry point (scratch laid out by
 // decode_layout(..., tables, debug)).
+// n_new >= 0: the call first grows the index from its n to n_new keys (at
+// most kAppendMax more, code scan only); the index itself is not changed here.
+// check_only: every check, then MP_OK without enqueueing anything (any
+// n_new up to the capacity).
 mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx, const mp_kv_view *k,
                         const mp_kv_view *v, int32_t n_sink, int32_t n_local, float scale,
                         float *out, void *scratch, size_t scratch_bytes, void *stream, bool debug,
                         uint16_t *qcodes, uint8_t *counts, int32_t *s_idx, int32_t *s_len,
-                        void *ev_begin, void *ev_end, bool tables);
+                        void *ev_begin, void *ev_end, bool tables, int32_t n_new = -1,
+                        bool check_only = false);
 // Scratch bytes of a code-scan decode without the debug lists, or -1 for a
 // dead handle or an H_q that does not fit the index.
 int64_t decode_scratch_needed(const mp_index *idx, int32_t H_q);

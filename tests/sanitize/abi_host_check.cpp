@@ -247,6 +247,12 @@ static void check_decode_args(const DecodeArgs &a, bool tables)
         rd(a.planes, BH * a.nc_cap * a.L * a.Kr * 16 * 4);
         EXPECT(a.bits == nullptr);
     }
+    // keys [app_n0, n) appended by the call: their words of the index's planes
+    EXPECT(a.app_n0 <= a.n && a.n - a.app_n0 <= kAppendMax);
+    if (a.app_n0 < a.n) {
+        EXPECT(!tables && a.K > 0 && a.app_n0 >= 0 && a.app_planes == a.planes);
+        wr(a.app_planes, BH * a.nc_cap * a.L * a.K * 16 * 4);
+    }
     // scratch and outputs
     wr(a.qcodes, BHq * a.L * 2);
     wr(a.qq, BHq * a.L * 4);
@@ -450,8 +456,38 @@ static void run_case(const Case &c)
         EXPECT_ST(mp_index_append(idx, &km, nullptr), MP_OK);
         kv = keys.prefix(c.grow_to);
         vv = vals.prefix(c.grow_to);
-        EXPECT_ST(mp_index_append(idx, &kv, nullptr), MP_OK);
+        // the second step appended by a decode (at most kAppendMax new keys
+        // with K > 0: their codes written by the query-encode launch; else
+        // the two calls).  A refused call leaves the index as it was.
+        {
+            mp_kv_view kbad = kv;
+            kbad.dtype = c.dtype == MP_BF16 ? MP_F32 : MP_BF16;
+            EXPECT_ST(mp_decode_attn_append(q.as<float>(), H_q, idx, &kbad, &vv, 4, 64, 0.0f,
+                                            out.as<float>(), w.p, ws, nullptr),
+                      MP_E_DTYPE);
+            EXPECT_ST(mp_decode_attn_append(q.as<float>(), H_q, idx, &kv, &vv, 4, 64, 0.0f,
+                                            out.as<float>(), w.p, 64, nullptr),
+                      MP_E_WORKSPACE);
+            EXPECT_ST(mp_decode_attn_append(q.as<float>(), H_q + 1, idx, &kv, &vv, 4, 64, 0.0f,
+                                            out.as<float>(), w.p, ws, nullptr),
+                      MP_E_SHAPE);
+            mp_kv_view vm = vals.prefix(mid);
+            Buf sc(mp_decode_scratch_bytes(idx, H_q));
+            EXPECT_ST(mp_decode_attn(q.as<float>(), H_q, idx, &km, &vm, 4, 64, 0.0f,
+                                     out.as<float>(), sc.p, sc.n, nullptr),
+                      MP_OK);   // still mid keys
+            EXPECT_ST(mp_decode_attn_append(q.as<float>(), H_q, idx, &kv, &vv, 4, 64, 0.0f,
+                                            out.as<float>(), sc.p, sc.n, nullptr),
+                      MP_OK);
+            EXPECT_ST(mp_decode_attn(q.as<float>(), H_q, idx, &km, &vm, 4, 64, 0.0f,
+                                     out.as<float>(), sc.p, sc.n, nullptr),
+                      MP_E_SHAPE);   // grown
+        }
+        EXPECT_ST(mp_index_append(idx, &kv, nullptr), MP_OK);   // nothing more to add
         EXPECT_ST(mp_tables_views(idx, nullptr, nullptr), MP_E_ARG);
+        EXPECT_ST(mp_decode_attn_append(q.as<float>(), H_q, idx, &km, &km, 4, 64, 0.0f,
+                                        out.as<float>(), w.p, ws, nullptr),
+                  MP_E_SHAPE);   // fewer keys
         EXPECT_ST(mp_index_append(idx, &km, nullptr), MP_E_SHAPE);   // fewer keys
         EXPECT_ST(mp_index_views(idx, nullptr, nullptr, nullptr, &n_pad), MP_OK);
         EXPECT(n_pad >= c.grow_to && n_pad - c.grow_to < 512);
@@ -637,6 +673,22 @@ static void error_paths()
     a.dtype = MP_F32;
     EXPECT_ST(mp_index_append(idx, &a, nullptr), MP_E_DTYPE);
     EXPECT_ST(mp_index_append(nullptr, &a, nullptr), MP_E_HANDLE);
+    // append and decode in one call: refused before any launch
+    a = more.prefix(999);
+    EXPECT_ST(mp_decode_attn_append(nullptr, 4, idx, &a, &a, 4, 64, 0.0f, nullptr, nullptr, 0,
+                                    nullptr),
+              MP_E_SHAPE);   // fewer keys
+    a = more.prefix(1001);
+    EXPECT_ST(mp_decode_attn_append(nullptr, 4, idx, &a, &a, 4, 64, 0.0f, nullptr, nullptr, 0,
+                                    nullptr),
+              MP_E_SHAPE);   // beyond capacity
+    a = more.view;
+    EXPECT_ST(mp_decode_attn_append(nullptr, 4, idx, &a, &a, 4, 64, 0.0f, nullptr, nullptr, 0,
+                                    nullptr),
+              MP_E_SHAPE);   // beyond capacity, more than one launch's worth of keys
+    EXPECT_ST(mp_decode_attn_append(nullptr, 4, nullptr, &a, &a, 4, 64, 0.0f, nullptr, nullptr,
+                                    0, nullptr),
+              MP_E_HANDLE);
     mp_index_destroy(idx);
 
     // a lifted index does not grow
@@ -646,6 +698,10 @@ static void error_paths()
               MP_OK);
     if (idx) {
         EXPECT_ST(mp_index_append(idx, &v, nullptr), MP_E_ARG);
+        mp_kv_view a1 = more.prefix(1001);
+        EXPECT_ST(mp_decode_attn_append(nullptr, 4, idx, &a1, &a1, 4, 64, 0.0f, nullptr, nullptr,
+                                        0, nullptr),
+                  MP_E_ARG);
         mp_index_destroy(idx);
     }
 

@@ -192,3 +192,81 @@ def test_append_rejections():
         mp.decode_attn(q, idx, k[:, :, :600], v[:, :, :600], 4, 16)
     with pytest.raises(mp.MPError, match="MP_E_ARG"):
         mp.build_index(k[:, :, :600], 8, 20, 26, capacity=599)
+
+
+def _key_bits_mask(n, nc, device):
+    """int32 mask [nc][1][16] of the plane bits that hold keys < n (bit j of
+    word w of chunk c is key 512c + 32w + j); the words of a chunk past n
+    hold whatever the workspace held."""
+    key0 = torch.arange(nc, device=device)[:, None] * 512 + torch.arange(16, device=device) * 32
+    nv = (n - key0).clamp(0, 32)
+    m = torch.where(nv >= 32, torch.full_like(nv, -1), (1 << nv.clamp(max=31)) - 1)
+    return m.to(torch.int32)[:, None, :]
+
+
+def _twin_steps(B, H_q, H_kv, dtype, K, L, n0, steps, n_sink, n_local, seed, cap=None):
+    """Two indexes built alike over the first n0 keys; each step grows one
+    with mp_index_append + mp_decode_attn and the other with
+    mp_decode_attn_append.  Outputs, n and every key's plane bits must agree
+    bit for bit.  Returns the second index and the cache."""
+    cap = cap or max(steps + [n0])
+    k, v, q = _cache(B, H_q, H_kv, cap, dtype, seed)
+    ia = mp.build_index(k[:, :, :n0], K, L, seed, capacity=cap)
+    ib = mp.build_index(k[:, :, :n0], K, L, seed, capacity=cap)
+    if 0 < K <= 12:
+        mp.build_tables(ib)   # detached by the first step
+    for n in steps:
+        mp.append_index(ia, k[:, :, :n])
+        oa = mp.decode_attn(q, ia, k[:, :, :n], v[:, :, :n], n_sink, n_local)
+        ob = mp.decode_attn_append(q, ib, k[:, :, :n], v[:, :, :n], n_sink, n_local)
+        torch.cuda.synchronize()
+        assert ia.n == ib.n == n
+        assert ib.tables is None
+        assert torch.equal(oa, ob), f"outputs differ at n={n}"
+        pa, pb = ia.views()[2], ib.views()[2]
+        m = _key_bits_mask(n, pa.shape[2], pa.device)
+        assert torch.equal(pa & m, pb & m), f"plane bits of the keys differ at n={n}"
+        print(f"n={n}: outputs and the key bits of {pb.numel()} plane words equal", flush=True)
+    return ib, k, v, q
+
+
+@pytest.mark.parametrize("dtype,H_q,H_kv,K,L", [(torch.bfloat16, 8, 2, 10, 60),
+                                                (torch.float32, 8, 1, 9, 40)])
+def test_decode_attn_append_equals_append_then_decode(dtype, H_q, H_kv, K, L):
+    """From 480 keys: 1 key (inside a word), 30, 1 (the chunk's last key), 1
+    (into the second chunk), 64 (the most one encode launch appends), 65
+    (the two-call route), no new key, 1, and 63 keys; then the grown index
+    against the oracle."""
+    steps = [481, 511, 512, 513, 577, 642, 642, 643, 706]
+    ib, k, v, q = _twin_steps(1, H_q, H_kv, dtype, K, L, 480, steps, 4, 32, seed=27, cap=1100)
+    r = check_index(ib, k, v, q, 706, 480, K, L, 27, 4, 32)
+    print("fused append, oracle", r, flush=True)
+
+
+def test_decode_attn_append_batch2_and_K0():
+    _twin_steps(2, 8, 2, torch.bfloat16, 8, 30, 1000, [1001, 1040, 1600], 4, 16, seed=28)
+    _twin_steps(1, 4, 1, torch.bfloat16, 0, 8, 200, [201, 230], 4, 16, seed=29)
+
+
+def test_decode_attn_append_rejections_leave_the_index():
+    k, v, q = _cache(1, 4, 1, 1000, torch.bfloat16, 30)
+    idx = mp.build_index(k[:, :, :600], 8, 20, 30, capacity=900)
+    with pytest.raises(mp.MPError, match="MP_E_SHAPE"):        # beyond the capacity
+        mp.decode_attn_append(q, idx, k[:, :, :901], v[:, :, :901], 4, 16)
+    with pytest.raises(mp.MPError, match="MP_E_SHAPE"):        # v at another length
+        mp.decode_attn_append(q, idx, k[:, :, :610], v[:, :, :600], 4, 16)
+    with pytest.raises(mp.MPError, match="MP_E_SHAPE"):        # v at another length, many keys
+        mp.decode_attn_append(q, idx, k[:, :, :800], v[:, :, :600], 4, 16)
+    assert idx.n == 600
+    mp.decode_attn(q, idx, k[:, :, :600], v[:, :, :600], 4, 16)   # still 600 keys
+    torch.cuda.synchronize()
+
+
+@pytest.mark.timeout(600)
+def test_decode_attn_append_96k_key_by_key():
+    """The serving pattern at the timed shape: one key appended per decode
+    step, through the fused call and through the two calls."""
+    cfg = synth.CONFIGS["llama8b_96k"]
+    n1 = cfg.n
+    _twin_steps(1, cfg.H_q, cfg.H_kv, cfg.dtype, cfg.K, cfg.L, n1 - 4, [n1 - 3, n1 - 2, n1 - 1, n1],
+                cfg.n_sink, cfg.n_local, seed=cfg.hyperplane_seed(5))
