@@ -323,8 +323,9 @@ constexpr bool table_rows_ahead() { return sizeof(T) == 2 && G > 4; }
 
 // Block = one 512-key chunk of one unit and its G query heads; S slice
 // bitmaps per head (a compile-time count, so that their loads issue together).
-template <int G, typename T, int S, int OCC = table_occupancy<G, T>()>
-__global__ __launch_bounds__(256, OCC) void table_gather_kernel(DecodeArgs a, int32_t nwords)
+template <int G, typename T, int S>
+__global__ __launch_bounds__(256, (table_occupancy<G, T>())) void table_gather_kernel(DecodeArgs a,
+                                                                                     int32_t nwords)
 {
     __shared__ uint32_t ulist[kChunk];
     __shared__ int wsum[4];
@@ -428,39 +429,10 @@ __global__ __launch_bounds__(256, OCC) void table_gather_kernel(DecodeArgs a, in
                                                   vr, t, gi, li);
 }
 
-// Workgroups of `kernel` resident on the current device at once (0 if the
-// runtime cannot say), cached per device.
-template <typename F>
-int resident_of(F kernel, int (&cached)[64])
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
-        int cus = 0, per_cu = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
-            return 0;
-        cached[dev] = cus * per_cu;
-    }
-    return cached[dev];
-}
-
 template <int G, typename T, int S>
 hipError_t launch_table_gather_t(const DecodeArgs &a, int32_t nwords, hipStream_t s)
 {
-    const int chunks = a.B * a.H_kv * a.n_chunks;
-    const dim3 grid(chunks);
-    if constexpr (table_occupancy<G, T>() == 5) {
-        // more chunks than 5 waves a SIMD hold, but no more than 6 do: the
-        // 6-wave build (a small spill) runs them all in one wave of
-        // workgroups instead of leaving a short second one
-        static int r5[64], r6[64];
-        const int n5 = resident_of(table_gather_kernel<G, T, S>, r5);
-        const int n6 = resident_of(table_gather_kernel<G, T, S, 6>, r6);
-        if (n5 > 0 && n6 > n5 && chunks > n5 && chunks <= n6)
-            return launch_timed(table_gather_kernel<G, T, S, 6>, grid, dim3(256), 0, s, a.ev_begin,
-                                a.ev_end, a, nwords);
-    }
+    const dim3 grid(a.B * a.H_kv * a.n_chunks);
     return launch_timed(table_gather_kernel<G, T, S>, grid, dim3(256), 0, s, a.ev_begin, a.ev_end,
                         a, nwords);
 }
