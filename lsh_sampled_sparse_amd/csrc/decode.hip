@@ -126,6 +126,29 @@ __device__ __forceinline__ void encode_query_block(const float *__restrict__ q, 
     }
 }
 
+#ifndef MP_ENC_XCD
+#define MP_ENC_XCD 1
+#endif
+// Encode blocks over a 1-D grid: (table block bx < nbx, head block by < nby)
+// of block b.  Workgroups go to the 8 XCDs round-robin by index, so the
+// blocks of one table block (the same W rows, for every head block) are
+// placed on one XCD, b % 8 = bx % 8, and read those rows into its L2 once
+// instead of on every XCD.  The grid then has 8 nby ceil(nbx / 8) blocks;
+// those with bx >= nbx have nothing to do.
+inline int encode_grid(int nbx, int nby) { return MP_ENC_XCD ? 8 * nby * ((nbx + 7) / 8) : nbx * nby; }
+__device__ __forceinline__ bool encode_coords(int b, int nbx, int nby, int &bx, int &by)
+{
+    if (MP_ENC_XCD) {
+        const int k = b / 8;
+        by = k % nby;
+        bx = 8 * (k / nby) + b % 8;
+        return bx < nbx;
+    }
+    bx = b % nbx;
+    by = b / nbx;
+    return by < nby;
+}
+
 template <int QH>
 __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restrict__ q,
                                                            int32_t BHq,
@@ -133,24 +156,27 @@ __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restri
                                                            int32_t L,
                                                            uint16_t *__restrict__ qcodes,
                                                            uint32_t *__restrict__ qq,
-                                                           float *__restrict__ qnorm)
+                                                           float *__restrict__ qnorm, int32_t nbx,
+                                                           int32_t nby)
 {
     __shared__ float4 sQ[QH][kD / 4];
     __shared__ uint8_t sbit[QH][64];
-    encode_query_block<QH>(q, BHq, W, K, L, qcodes, qq, qnorm, blockIdx.x, blockIdx.y, sQ, sbit,
-                           threadIdx.x);
+    int bx, by;
+    if (!encode_coords(blockIdx.x, nbx, nby, bx, by)) return;   // the whole block
+    encode_query_block<QH>(q, BHq, W, K, L, qcodes, qq, qnorm, bx, by, sQ, sbit, threadIdx.x);
 }
 
 // The query encode and an append of a few keys (append_codes.h) in one
 // launch, for a decode that first grows its index: blocks [0, n_enc) are the
-// encode blocks (bx = b % nbx, by = b / nbx), the rest the append's blocks
-// (unit, hyperplane block of 256).  The two write disjoint memory; the scan
+// encode blocks (encode_coords), the rest the append's blocks (unit,
+// hyperplane block of kAppendRows).  The two write disjoint memory; the scan
 // that reads both comes after the launch.
 template <int QH, typename T>
 __global__ __launch_bounds__(256) void encode_append_kernel(
     const float *__restrict__ q, int32_t BHq, const float *__restrict__ W, int32_t K, int32_t L,
     uint16_t *__restrict__ qcodes, uint32_t *__restrict__ qq, float *__restrict__ qnorm,
-    int32_t nbx, int32_t n_enc, const T *__restrict__ keys, int64_t sb, int64_t sh, int64_t sn,
+    int32_t nbx, int32_t nby, int32_t n_enc, const T *__restrict__ keys, int64_t sb, int64_t sh,
+    int64_t sn,
     int32_t H, int32_t n0, int32_t n1, int32_t nc_cap, const float *__restrict__ mu,
     uint32_t *__restrict__ planes, int32_t nhb)
 {
@@ -160,7 +186,9 @@ __global__ __launch_bounds__(256) void encode_append_kernel(
     if (b < n_enc) {
         float4(*sQ)[kD / 4] = reinterpret_cast<float4(*)[kD / 4]>(&sx[0][0]);
         uint8_t(*sbit)[64] = reinterpret_cast<uint8_t(*)[64]>(&sx[QH][0]);
-        encode_query_block<QH>(q, BHq, W, K, L, qcodes, qq, qnorm, b % nbx, b / nbx, sQ, sbit, t);
+        int bx, by;
+        if (encode_coords(b, nbx, nby, bx, by))   // uniform over the block
+            encode_query_block<QH>(q, BHq, W, K, L, qcodes, qq, qnorm, bx, by, sQ, sbit, t);
     } else {
         const int ab = b - n_enc;
         append_codes_block<T>(keys, sb, sh, sn, H, n0, n1, nc_cap, mu, W, K, L, planes, ab / nhb,
@@ -694,11 +722,11 @@ hipError_t launch_encode_append_t(const DecodeArgs &a, hipStream_t s)
 {
     const int BHq = a.B * a.H_q;
     const int TB = a.K > 0 ? 64 / a.K : 64;
-    const int nbx = ceil_div(a.L, TB), n_enc = nbx * ceil_div(BHq, QH);
+    const int nbx = ceil_div(a.L, TB), nby = ceil_div(BHq, QH), n_enc = encode_grid(nbx, nby);
     const int nhb = ceil_div(int64_t(a.K) * a.L, kAppendRows);
     const int units = a.B * a.H_kv;
     return launch(encode_append_kernel<QH, T>, dim3(n_enc + units * nhb), dim3(256), 0, s, a.q, BHq,
-                  a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm, nbx, n_enc,
+                  a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm, nbx, nby, n_enc,
                   static_cast<const T *>(a.k.data), a.k.sb, a.k.sh, a.k.sn, a.H_kv, a.app_n0, a.n,
                   a.nc_cap, a.mu, a.app_planes, nhb);
 }
@@ -720,11 +748,15 @@ hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s)
 {
     const int BHq = a.B * a.H_q;
     const int TB = a.K > 0 ? 64 / a.K : 64;
-    if (BHq <= 32)
-        return launch(encode_query_kernel<2>, dim3(ceil_div(a.L, TB), ceil_div(BHq, 2)), dim3(256),
-                      0, s, a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
-    return launch(encode_query_kernel<4>, dim3(ceil_div(a.L, TB), ceil_div(BHq, 4)), dim3(256), 0,
-                  s, a.q, BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm);
+    const int nbx = ceil_div(a.L, TB);
+    if (BHq <= 32) {
+        const int nby = ceil_div(BHq, 2);
+        return launch(encode_query_kernel<2>, dim3(encode_grid(nbx, nby)), dim3(256), 0, s, a.q,
+                      BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm, nbx, nby);
+    }
+    const int nby = ceil_div(BHq, 4);
+    return launch(encode_query_kernel<4>, dim3(encode_grid(nbx, nby)), dim3(256), 0, s, a.q, BHq,
+                  a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm, nbx, nby);
 }
 
 namespace {
