@@ -227,8 +227,9 @@ mp_status mp_decode_attn_append(const float *q, int32_t H_q, mp_index *idx,
  * nothing.  Arguments, layouts and the output are those of mp_decode_attn
  * (the same kernels, bit-identical results).  The scratch it needs, 256-byte
  * aligned pieces of B*H_q*L*2 + B*H_q*L*4 + B*H_q*4 + B*H_q*ceil(n/512)*130*4
- * bytes (query codes, their packed form, norms, partial records), must fit the
- * array: MP_E_WORKSPACE otherwise, before anything is enqueued.  All calls on
+ * + B*H_kv*4 bytes (query codes, their packed form, norms, partial records,
+ * per-unit record counts), must fit the array: MP_E_WORKSPACE otherwise,
+ * before anything is enqueued.  All calls on
  * one GPU share that GPU's array, so calls that overlap on one GPU (other
  * streams or threads) race; order them on one stream. */
 mp_status mp_decode_attn_noalloc(const float *q, int32_t H_q, const mp_index *idx,

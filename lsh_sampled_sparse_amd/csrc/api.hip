@@ -88,6 +88,7 @@ DecodeLayout decode_layout(const IndexLayout &lay, int32_t H_q, bool tables, boo
     y.off_qq = off;      off = align256(off + BHq * lay.L * 4);
     y.off_qnorm = off;   off = align256(off + BHq * 4);
     y.off_part = off;    off = align256(off + BHq * lay.n_chunks * int64_t(kD + 2) * 4);
+    y.off_cnt = off;     off = align256(off + int64_t(lay.B) * lay.H_kv * 4);
     y.off_seg_idx = off;
     if (debug) off = align256(off + BHq * lay.n_chunks * int64_t(kChunk) * 4);
     y.off_seg_cnt = off;
@@ -256,6 +257,7 @@ mp_status decode_common(const float *q, int32_t H_q, const mp_index *idx, const 
     a.app_n0 = n_new >= 0 ? idx->lay.n : lay.n;
     a.app_planes = idx->planes;
     a.part = reinterpret_cast<float *>(sp + dl.off_part);
+    a.unit_cnt = reinterpret_cast<int32_t *>(sp + dl.off_cnt);
     a.seg_idx = reinterpret_cast<int32_t *>(sp + dl.off_seg_idx);
     a.seg_cnt = reinterpret_cast<int32_t *>(sp + dl.off_seg_cnt);
     a.tab_off = idx->tab_off;

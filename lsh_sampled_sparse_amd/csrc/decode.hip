@@ -157,10 +157,13 @@ __global__ __launch_bounds__(256) void encode_query_kernel(const float *__restri
                                                            uint16_t *__restrict__ qcodes,
                                                            uint32_t *__restrict__ qq,
                                                            float *__restrict__ qnorm, int32_t nbx,
-                                                           int32_t nby)
+                                                           int32_t nby, int32_t *__restrict__ cnt,
+                                                           int32_t ncnt)
 {
     __shared__ float4 sQ[QH][kD / 4];
     __shared__ uint8_t sbit[QH][64];
+    if (blockIdx.x == 0)   // the scan's per-unit record counts start at zero
+        for (int i = threadIdx.x; i < ncnt; i += 256) cnt[i] = 0;
     int bx, by;
     if (!encode_coords(blockIdx.x, nbx, nby, bx, by)) return;   // the whole block
     encode_query_block<QH>(q, BHq, W, K, L, qcodes, qq, qnorm, bx, by, sQ, sbit, threadIdx.x);
@@ -178,11 +181,13 @@ __global__ __launch_bounds__(256) void encode_append_kernel(
     int32_t nbx, int32_t nby, int32_t n_enc, const T *__restrict__ keys, int64_t sb, int64_t sh,
     int64_t sn,
     int32_t H, int32_t n0, int32_t n1, int32_t nc_cap, const float *__restrict__ mu,
-    uint32_t *__restrict__ planes, int32_t nhb)
+    uint32_t *__restrict__ planes, int32_t nhb, int32_t *__restrict__ cnt, int32_t ncnt)
 {
     __shared__ __align__(16) float sx[kAppendMax][kD];   // the encode's LDS is carved from it
     static_assert(QH * (kD / 4) * 16 + QH * 64 <= sizeof(sx), "encode LDS fits");
     const int b = blockIdx.x, t = threadIdx.x;
+    if (b == 0)   // the scan's per-unit record counts start at zero
+        for (int i = t; i < ncnt; i += 256) cnt[i] = 0;
     if (b < n_enc) {
         float4(*sQ)[kD / 4] = reinterpret_cast<float4(*)[kD / 4]>(&sx[0][0]);
         uint8_t(*sbit)[64] = reinterpret_cast<uint8_t(*)[64]>(&sx[QH][0]);
@@ -194,6 +199,69 @@ __global__ __launch_bounds__(256) void encode_append_kernel(
         append_codes_block<T>(keys, sb, sh, sn, H, n0, n1, nc_cap, mu, W, K, L, planes, ab / nhb,
                               ab % nhb, t, sx);
     }
+}
+
+// ---------------------------------------------------------------- fused merge
+// The merge of one unit's records inside the scan, by the workgroup that
+// stores the unit's last record (runs aligned with units, at most
+// kFusedMergeMax records, G <= 4).  Each record was stored with device-scope
+// stores and counted after they completed (s_waitcnt), so device-scope loads
+// here find every record, whichever XCD wrote it.  Wave w takes head g = w: lane r
+// loads the (max, sum) of record r, the wave forms the head's max M, the
+// weights w_r = exp(m_r - M) (0 past nrec or for an empty record) and
+// their sum with the l_r, and puts the weights in LDS (read back by the same
+// wave: no barrier); thread (g, dp) folds the accumulator pairs of every
+// record, all NR loads issued before the first is used, in record order.
+template <int G, typename T, int NR>
+__device__ __forceinline__ void merge_unit_records(const DecodeArgs &a, int bkv, int nrec,
+                                                   GatherLds<G, T> &s, int t)
+{
+    static_assert(G <= 4 && NR <= kRound, "one (head, pair of dims) a thread, a record a lane");
+    const int lane = t & 63, g = t >> 6;
+    if (g >= G) return;   // the whole wave
+    const float *p0 = a.part + int64_t(bkv) * a.n_chunks * (G * kPart) + g * kPart;
+    uint64_t av[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int rr = min(r, nrec - 1);   // past nrec: re-read the last record, weight 0
+        av[r] = __hip_atomic_load(
+            reinterpret_cast<const uint64_t *>(p0 + int64_t(rr) * (G * kPart) + 2 + 2 * lane),
+            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint64_t ml = __hip_atomic_load(
+        reinterpret_cast<const uint64_t *>(p0 + int64_t(min(lane, nrec - 1)) * (G * kPart)),
+        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float m = lane < nrec ? __uint_as_float(uint32_t(ml)) : -INFINITY;
+    const float l = lane < nrec ? __uint_as_float(uint32_t(ml >> 32)) : 0.0f;
+    const float M = wave_max(m);
+    const float wr = m == -INFINITY ? 0.0f : __expf(m - M);
+    const float Ls = wave_sum(wr * l);
+    if (lane < NR) s.sw[lane][g] = wr;
+    float x0 = 0.0f, x1 = 0.0f;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const float wg = s.sw[r][g];
+        x0 = fmaf(wg, __uint_as_float(uint32_t(av[r])), x0);
+        x1 = fmaf(wg, __uint_as_float(uint32_t(av[r] >> 32)), x1);
+    }
+    const int b = bkv / a.H_kv, h = bkv % a.H_kv;
+    reinterpret_cast<float2 *>(a.out + (int64_t(b) * a.H_q + h * G + g) * kD)[lane] =
+        Ls > 0.0f ? make_float2(x0 / Ls, x1 / Ls) : make_float2(0.0f, 0.0f);
+}
+
+// Records a unit has when its runs align with it and there are at most
+// kFusedMergeMax of them, for the fused merge (0: the separate merge kernel
+// runs instead).  The fused merge reads a unit's records on one workgroup,
+// after that unit's last run: at 32 records (16K context) the step is 0.7-0.9
+// us shorter than with the separate kernel, at 4 (batch 16 x 32K) 4-14 us,
+// but at 64 (96K) the one workgroup's 131 KB of reads made scan_gather 3.3 us
+// longer and the step 0.3-0.9 us longer.
+constexpr int kFusedMergeMax = 32;
+inline int fused_merge_records(const DecodeArgs &a, int G, int cpb)
+{
+    if (G > 4 || !a.unit_cnt || a.n_chunks % cpb != 0) return 0;
+    const int nrec = a.n_chunks / cpb;
+    return nrec <= kFusedMergeMax ? nrec : 0;
 }
 
 // ---------------------------------------------------------------- scan + gather
@@ -238,7 +306,8 @@ inline int plane_rows_class(int Kr)
 // rather than on every load in flight.
 template <int G, typename T, int KP>
 __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_kernel(DecodeArgs a,
-                                                                                    int32_t cpb)
+                                                                                    int32_t cpb,
+                                                                                    int32_t frec)
 {
     __shared__ uint32_t seen[2][G][kWords];  // per head and word: matched once / twice
     __shared__ __align__(16) uint32_t sqq[256][G];   // query codes, code | code << 16
@@ -519,6 +588,25 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         gather_chunk_into<G, T, sizeof(T) == 2>(a, gl, ulist, p_total, p_chunk, p_bkv,
                                                 sq[p_slot], sqn[p_slot], smu[p_slot], kraw, vraw,
                                                 acc, t, t >> 4, t & 15);
+        if constexpr (G <= 4) {
+            if (frec > 0) {
+                // runs aligned with units: this run's one record, counted
+                // once its stores have completed; the unit's last merges
+                gather_store<G, true>(a, acc, run - (p_bkv * a.n_chunks) / cpb, p_bkv, t);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __syncthreads();
+                if (t == 0)
+                    wsum[0] = __hip_atomic_fetch_add(a.unit_cnt + p_bkv, 1, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT) == frec - 1;
+                __syncthreads();
+                if (wsum[0]) {
+                    if (frec <= 8) merge_unit_records<G, T, 8>(a, p_bkv, frec, gl, t);
+                    else if (frec <= 16) merge_unit_records<G, T, 16>(a, p_bkv, frec, gl, t);
+                    else merge_unit_records<G, T, kFusedMergeMax>(a, p_bkv, frec, gl, t);
+                }
+                return;
+            }
+        }
         store_unit(p_bkv, t);
     }
 }
@@ -689,7 +777,7 @@ hipError_t launch_scan_gather_t(const DecodeArgs &a, hipStream_t s, int32_t &cpb
     // timed entry point: the runtime stamps the events at this kernel's own
     // start and end
     return launch_timed(scan_gather_kernel<G, T, KP>, grid, dim3(256), 0, s, a.ev_begin, a.ev_end,
-                        a, cpb);
+                        a, cpb, fused_merge_records(a, G, cpb));
 }
 
 template <int G, typename T>
@@ -728,7 +816,7 @@ hipError_t launch_encode_append_t(const DecodeArgs &a, hipStream_t s)
     return launch(encode_append_kernel<QH, T>, dim3(n_enc + units * nhb), dim3(256), 0, s, a.q, BHq,
                   a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm, nbx, nby, n_enc,
                   static_cast<const T *>(a.k.data), a.k.sb, a.k.sh, a.k.sn, a.H_kv, a.app_n0, a.n,
-                  a.nc_cap, a.mu, a.app_planes, nhb);
+                  a.nc_cap, a.mu, a.app_planes, nhb, a.unit_cnt, a.unit_cnt ? units : 0);
 }
 
 // The query encode with the append of keys [app_n0, n) (1 to kAppendMax, K > 0).
@@ -749,14 +837,15 @@ hipError_t launch_encode_query(const DecodeArgs &a, hipStream_t s)
     const int BHq = a.B * a.H_q;
     const int TB = a.K > 0 ? 64 / a.K : 64;
     const int nbx = ceil_div(a.L, TB);
+    const int ncnt = a.unit_cnt ? a.B * a.H_kv : 0;
     if (BHq <= 32) {
         const int nby = ceil_div(BHq, 2);
         return launch(encode_query_kernel<2>, dim3(encode_grid(nbx, nby)), dim3(256), 0, s, a.q,
-                      BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm, nbx, nby);
+                      BHq, a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm, nbx, nby, a.unit_cnt, ncnt);
     }
     const int nby = ceil_div(BHq, 4);
     return launch(encode_query_kernel<4>, dim3(encode_grid(nbx, nby)), dim3(256), 0, s, a.q, BHq,
-                  a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm, nbx, nby);
+                  a.W, a.K, a.L, a.qcodes, a.qq, a.qnorm, nbx, nby, a.unit_cnt, ncnt);
 }
 
 namespace {
@@ -830,7 +919,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    if ((e = launch_merge(a, cpb, s)) != hipSuccess) return e;
+    // the merge runs inside scan_gather where runs align with units
+    if (fused_merge_records(a, a.G, cpb) == 0 && (e = launch_merge(a, cpb, s)) != hipSuccess)
+        return e;
     if ((e = launch_counts(a, s)) != hipSuccess) return e;
     return launch_seg_compact(a, s);
 }

@@ -502,7 +502,7 @@ __device__ __forceinline__ void gather_head(const DecodeArgs &a, GatherLds<G, T>
     gather_z<G, T>(a, s, ulist, 0, ne, sqn, gi, li);
 }
 
-template <int G>
+template <int G, bool kCoherent = false>
 __device__ __forceinline__ void gather_store(const DecodeArgs &a, const GatherAcc<G> &acc,
                                              int slot, int bkv, int t);
 
@@ -527,10 +527,20 @@ __device__ __forceinline__ void gather_tail(const DecodeArgs &a, GatherLds<G, T>
     }
 }
 
+// Two floats as one 64-bit word, low word first (their order in memory).
+__device__ __forceinline__ uint64_t pack2(float lo, float hi)
+{
+    return uint64_t(__float_as_uint(lo)) | (uint64_t(__float_as_uint(hi)) << 32);
+}
+
 // A partial softmax (max, sum, unnormalised accumulator) per head, into
 // record `slot` of unit bkv (records are n_chunks apart per unit; a record
 // holds one chunk, or several chunks of one unit folded together).
-template <int G>
+// kCoherent: stored with device-scope atomic stores (written through to the
+// level every XCD reads), for a workgroup that reads the record back within
+// the same kernel; every pair of floats is 8-byte aligned (records and
+// heads are whole multiples of 8 bytes apart).
+template <int G, bool kCoherent>
 __device__ __forceinline__ void gather_store(const DecodeArgs &a, const GatherAcc<G> &acc,
                                              int slot, int bkv, int t)
 {
@@ -540,11 +550,21 @@ __device__ __forceinline__ void gather_store(const DecodeArgs &a, const GatherAc
     for (int p = 0; p < GatherAcc<G>::kPairs; ++p) {
         const int g = uniform((t + 256 * p) / (kD / 2)), dp = lane;
         if (g < G) {
-            part0[g * kPart + 2 + 2 * dp] = acc.acc0[p];
-            part0[g * kPart + 3 + 2 * dp] = acc.acc1[p];
-            if (dp == 0) {
-                part0[g * kPart] = acc.m[p];
-                part0[g * kPart + 1] = acc.l[p];
+            if constexpr (kCoherent) {
+                __hip_atomic_store(reinterpret_cast<uint64_t *>(part0 + g * kPart + 2 + 2 * dp),
+                                   pack2(acc.acc0[p], acc.acc1[p]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                if (dp == 0)
+                    __hip_atomic_store(reinterpret_cast<uint64_t *>(part0 + g * kPart),
+                                       pack2(acc.m[p], acc.l[p]), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                part0[g * kPart + 2 + 2 * dp] = acc.acc0[p];
+                part0[g * kPart + 3 + 2 * dp] = acc.acc1[p];
+                if (dp == 0) {
+                    part0[g * kPart] = acc.m[p];
+                    part0[g * kPart + 1] = acc.l[p];
+                }
             }
         }
     }

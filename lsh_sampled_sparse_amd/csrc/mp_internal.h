@@ -173,7 +173,8 @@ TablesLayout tables_layout(const IndexLayout &lay);
 // Decode scratch layout.
 struct DecodeLayout {
     int32_t BHq, n_chunks;
-    int64_t off_qcodes, off_qq, off_qnorm, off_part, off_seg_idx, off_seg_cnt, off_bits, total;
+    int64_t off_qcodes, off_qq, off_qnorm, off_part, off_cnt, off_seg_idx, off_seg_cnt, off_bits,
+        total;
 };
 // `tables`: also the per-head collision bitmaps of the bucketed-table path;
 // `debug`: also the per-chunk sampled lists of the debug entry points.
@@ -235,6 +236,7 @@ struct DecodeArgs {
     int32_t app_n0;          // keys [app_n0, n) are appended by this call (app_n0 = n: none)
     uint32_t *app_planes;    // the index's planes, written by that append
     float *part;             // scratch [B*H_kv][n_chunks][G][kD + 2] partial records (a chunk, or a run's chunks of one unit)
+    int32_t *unit_cnt;       // scratch [B*H_kv]: records stored per unit, zeroed by the query encode
     int32_t *seg_idx;        // scratch [BHq][n_chunks * kChunk] (debug only)
     int32_t *seg_cnt;        // scratch [BHq][n_chunks] (debug only)
     float *out;              // [BHq][128]

@@ -258,6 +258,7 @@ static void check_decode_args(const DecodeArgs &a, bool tables)
     wr(a.qq, BHq * a.L * 4);
     wr(a.qnorm, BHq * 4);
     wr(a.part, BH * a.n_chunks * a.G * (128 + 2) * 4);
+    wr(a.unit_cnt, BH * 4);
     if (a.debug) {
         wr(a.seg_idx, BHq * n_pad * 4);
         wr(a.seg_cnt, BHq * a.n_chunks * 4);
