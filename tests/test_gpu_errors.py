@@ -19,18 +19,16 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _inputs():
-    inp = synth.cone_inputs(B=1, H_q=8, H_kv=2, n=1500, d=128, dtype=torch.bfloat16, seeds=[5],
+def _inputs(n=1500):
+    inp = synth.cone_inputs(B=1, H_q=8, H_kv=2, n=n, d=128, dtype=torch.bfloat16, seeds=[5],
                             device=DEV)
     return inp["k"], inp["v"], inp["q"].contiguous()
 
 
-def test_forced_launch_failure_is_mp_e_hip_and_recoverable():
-    k, v, q = _inputs()
-    idx = mp.build_index(k, 8, 40, 5)
+def _fail_each_launch(q, idx, k, v, launches):
     ref = mp.decode_attn(q, idx, k, v, 4, 64)
     torch.cuda.synchronize()
-    for nth in (0, 1, 2):          # the query encode, the scan, the merge
+    for nth in range(launches):
         mp.capi.mp_debug_fail_launches(nth, 1)
         with pytest.raises(mp.MPError, match="MP_E_HIP"):
             mp.decode_attn(q, idx, k, v, 4, 64)
@@ -38,6 +36,18 @@ def test_forced_launch_failure_is_mp_e_hip_and_recoverable():
         again = mp.decode_attn(q, idx, k, v, 4, 64)
         torch.cuda.synchronize()
         assert torch.equal(again, ref)
+    mp.capi.mp_debug_fail_launches(0, 0)
+
+
+def test_forced_launch_failure_is_mp_e_hip_and_recoverable():
+    # 40 chunks a unit (40 records, one a chunk): the query encode, the scan
+    # and the merge kernel
+    kl, vl, ql = _inputs(40 * 512)
+    _fail_each_launch(ql, mp.build_index(kl, 8, 40, 5), kl, vl, 3)
+    # 3 records a unit: the merge runs inside the scan, two launches
+    k, v, q = _inputs()
+    idx = mp.build_index(k, 8, 40, 5)
+    _fail_each_launch(q, idx, k, v, 2)
     mp.capi.mp_debug_fail_launches(2, 1)                  # W, mean partial sums, then the mean
     with pytest.raises(mp.MPError, match="MP_E_HIP"):
         mp.build_index(k, 8, 40, 5)
