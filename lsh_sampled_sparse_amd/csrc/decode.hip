@@ -201,69 +201,6 @@ __global__ __launch_bounds__(256) void encode_append_kernel(
     }
 }
 
-// ---------------------------------------------------------------- fused merge
-// The merge of one unit's records inside the scan, by the workgroup that
-// stores the unit's last record (runs aligned with units, at most
-// kFusedMergeMax records, G <= 4).  Each record was stored with device-scope
-// stores and counted after they completed (s_waitcnt), so device-scope loads
-// here find every record, whichever XCD wrote it.  Wave w takes head g = w: lane r
-// loads the (max, sum) of record r, the wave forms the head's max M, the
-// weights w_r = exp(m_r - M) (0 past nrec or for an empty record) and
-// their sum with the l_r, and puts the weights in LDS (read back by the same
-// wave: no barrier); thread (g, dp) folds the accumulator pairs of every
-// record, all NR loads issued before the first is used, in record order.
-template <int G, typename T, int NR>
-__device__ __forceinline__ void merge_unit_records(const DecodeArgs &a, int bkv, int nrec,
-                                                   GatherLds<G, T> &s, int t)
-{
-    static_assert(G <= 4 && NR <= kRound, "one (head, pair of dims) a thread, a record a lane");
-    const int lane = t & 63, g = t >> 6;
-    if (g >= G) return;   // the whole wave
-    const float *p0 = a.part + int64_t(bkv) * a.n_chunks * (G * kPart) + g * kPart;
-    uint64_t av[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const int rr = min(r, nrec - 1);   // past nrec: re-read the last record, weight 0
-        av[r] = __hip_atomic_load(
-            reinterpret_cast<const uint64_t *>(p0 + int64_t(rr) * (G * kPart) + 2 + 2 * lane),
-            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    const uint64_t ml = __hip_atomic_load(
-        reinterpret_cast<const uint64_t *>(p0 + int64_t(min(lane, nrec - 1)) * (G * kPart)),
-        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float m = lane < nrec ? __uint_as_float(uint32_t(ml)) : -INFINITY;
-    const float l = lane < nrec ? __uint_as_float(uint32_t(ml >> 32)) : 0.0f;
-    const float M = wave_max(m);
-    const float wr = m == -INFINITY ? 0.0f : __expf(m - M);
-    const float Ls = wave_sum(wr * l);
-    if (lane < NR) s.sw[lane][g] = wr;
-    float x0 = 0.0f, x1 = 0.0f;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const float wg = s.sw[r][g];
-        x0 = fmaf(wg, __uint_as_float(uint32_t(av[r])), x0);
-        x1 = fmaf(wg, __uint_as_float(uint32_t(av[r] >> 32)), x1);
-    }
-    const int b = bkv / a.H_kv, h = bkv % a.H_kv;
-    reinterpret_cast<float2 *>(a.out + (int64_t(b) * a.H_q + h * G + g) * kD)[lane] =
-        Ls > 0.0f ? make_float2(x0 / Ls, x1 / Ls) : make_float2(0.0f, 0.0f);
-}
-
-// Records a unit has when its runs align with it and there are at most
-// kFusedMergeMax of them, for the fused merge (0: the separate merge kernel
-// runs instead).  The fused merge reads a unit's records on one workgroup,
-// after that unit's last run: at 32 records (16K context) the step is 0.7-0.9
-// us shorter than with the separate kernel, at 4 (batch 16 x 32K) 4-14 us,
-// but at 64 (96K) the one workgroup's 131 KB of reads made scan_gather 3.3 us
-// longer and the step 0.3-0.9 us longer.
-constexpr int kFusedMergeMax = 32;
-inline int fused_merge_records(const DecodeArgs &a, int G, int cpb)
-{
-    if (G > 4 || !a.unit_cnt || a.n_chunks % cpb != 0) return 0;
-    const int nrec = a.n_chunks / cpb;
-    return nrec <= kFusedMergeMax ? nrec : 0;
-}
-
 // ---------------------------------------------------------------- scan + gather
 // Waves per SIMD the register budget is cut for: 3 up to G = 4 with bf16 rows
 // (the next chunk's first plane batches stay in registers through a gather),
@@ -588,26 +525,11 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
         gather_chunk_into<G, T, sizeof(T) == 2>(a, gl, ulist, p_total, p_chunk, p_bkv,
                                                 sq[p_slot], sqn[p_slot], smu[p_slot], kraw, vraw,
                                                 acc, t, t >> 4, t & 15);
-        if constexpr (G <= 4) {
-            if (frec > 0) {
-                // runs aligned with units: this run's one record, counted
-                // once its stores have completed; the unit's last merges
-                gather_store<G, true>(a, acc, run - (p_bkv * a.n_chunks) / cpb, p_bkv, t);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                __syncthreads();
-                if (t == 0)
-                    wsum[0] = __hip_atomic_fetch_add(a.unit_cnt + p_bkv, 1, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT) == frec - 1;
-                __syncthreads();
-                if (wsum[0]) {
-                    if (frec <= 8) merge_unit_records<G, T, 8>(a, p_bkv, frec, gl, t);
-                    else if (frec <= 16) merge_unit_records<G, T, 16>(a, p_bkv, frec, gl, t);
-                    else merge_unit_records<G, T, kFusedMergeMax>(a, p_bkv, frec, gl, t);
-                }
-                return;
-            }
-        }
-        store_unit(p_bkv, t);
+        if (frec > 0)   // runs aligned with units: this run's one record, merged here
+            store_count_merge<G, T>(a, acc, run - (p_bkv * a.n_chunks) / cpb, p_bkv, frec, gl,
+                                    wsum, t);
+        else
+            store_unit(p_bkv, t);
     }
 }
 

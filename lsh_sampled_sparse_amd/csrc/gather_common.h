@@ -601,21 +601,93 @@ __device__ __forceinline__ void gather_chunk_into(const DecodeArgs &a, GatherLds
     }
 }
 
-// One chunk's whole list into a record of its own (record = chunk).
-template <int G, typename T, bool kAhead>
-__device__ __forceinline__ void gather_chunk(const DecodeArgs &a, GatherLds<G, T> &s,
-                                             const uint32_t *ulist, int total, int chunk,
-                                             int bkv, const float (*sq)[kD], const float *sqn,
-                                             const float *smu,
-                                             const typename Row8<T>::raw (&kr0)[kRowsPerGroup],
-                                             const typename Row8<T>::raw (&vr0)[kRowsPerGroup],
-                                             int t, int gi, int li)
+// The merge of one unit's records inside the gather kernel (the scan's, or
+// the table path's), by the workgroup that stores the unit's last record
+// (runs aligned with units, at most kFusedMergeMax records, G <= 4).  Each
+// record was stored with device-scope stores and counted after they
+// completed (s_waitcnt), so device-scope loads here find every record,
+// whichever XCD wrote it.  Wave w takes head g = w: lane r loads the (max,
+// sum) of record r, the wave forms the head's max M, the weights
+// w_r = exp(m_r - M) (0 past nrec or for an empty record) and their sum with
+// the l_r, and puts the weights in LDS (read back by the same wave: no
+// barrier); thread (g, dp) folds the accumulator pairs of every record, all
+// NR loads issued before the first is used, in record order.
+template <int G, typename T, int NR>
+__device__ __forceinline__ void merge_unit_records(const DecodeArgs &a, int bkv, int nrec,
+                                                   GatherLds<G, T> &s, int t)
 {
-    GatherAcc<G> acc;
-    acc.reset();
-    gather_chunk_into<G, T, kAhead>(a, s, ulist, total, chunk, bkv, sq, sqn, smu, kr0, vr0, acc, t,
-                                    gi, li);
-    gather_store<G>(a, acc, chunk, bkv, t);
+    static_assert(G <= 4 && NR <= kRound, "one (head, pair of dims) a thread, a record a lane");
+    const int lane = t & 63, g = t >> 6;
+    if (g >= G) return;   // the whole wave
+    const float *p0 = a.part + int64_t(bkv) * a.n_chunks * (G * kPart) + g * kPart;
+    uint64_t av[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int rr = min(r, nrec - 1);   // past nrec: re-read the last record, weight 0
+        av[r] = __hip_atomic_load(
+            reinterpret_cast<const uint64_t *>(p0 + int64_t(rr) * (G * kPart) + 2 + 2 * lane),
+            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint64_t ml = __hip_atomic_load(
+        reinterpret_cast<const uint64_t *>(p0 + int64_t(min(lane, nrec - 1)) * (G * kPart)),
+        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float m = lane < nrec ? __uint_as_float(uint32_t(ml)) : -INFINITY;
+    const float l = lane < nrec ? __uint_as_float(uint32_t(ml >> 32)) : 0.0f;
+    const float M = wave_max(m);
+    const float wr = m == -INFINITY ? 0.0f : __expf(m - M);
+    const float Ls = wave_sum(wr * l);
+    if (lane < NR) s.sw[lane][g] = wr;
+    float x0 = 0.0f, x1 = 0.0f;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const float wg = s.sw[r][g];
+        x0 = fmaf(wg, __uint_as_float(uint32_t(av[r])), x0);
+        x1 = fmaf(wg, __uint_as_float(uint32_t(av[r] >> 32)), x1);
+    }
+    const int b = bkv / a.H_kv, h = bkv % a.H_kv;
+    reinterpret_cast<float2 *>(a.out + (int64_t(b) * a.H_q + h * G + g) * kD)[lane] =
+        Ls > 0.0f ? make_float2(x0 / Ls, x1 / Ls) : make_float2(0.0f, 0.0f);
+}
+
+// Records a unit has when its runs (cpb chunks; 1 on the table path) align
+// with it and there are at most kFusedMergeMax of them, for the fused merge
+// (0: the separate merge kernel runs instead).  The fused merge reads a unit's records on one workgroup,
+// after that unit's last run: at 32 records (16K context) the step is 0.7-0.9
+// us shorter than with the separate kernel, at 4 (batch 16 x 32K) 4-14 us,
+// but at 64 (96K) the one workgroup's 131 KB of reads made scan_gather 3.3 us
+// longer and the step 0.3-0.9 us longer.
+constexpr int kFusedMergeMax = 32;
+inline int fused_merge_records(const DecodeArgs &a, int G, int cpb)
+{
+    if (G > 4 || !a.unit_cnt || a.n_chunks % cpb != 0) return 0;
+    const int nrec = a.n_chunks / cpb;
+    return nrec <= kFusedMergeMax ? nrec : 0;
+}
+
+// A workgroup's record of unit bkv (record rec of nrec), stored so that the
+// workgroup that stores the unit's last record can merge them all in this
+// kernel: device-scope stores, a wait for their completion, then the unit's
+// count (a device-scope add; the counts start at zero).  Every thread calls
+// it; flag is an LDS word.
+template <int G, typename T>
+__device__ __forceinline__ void store_count_merge(const DecodeArgs &a, const GatherAcc<G> &acc,
+                                                  int rec, int bkv, int nrec, GatherLds<G, T> &s,
+                                                  int *flag, int t)
+{
+    if constexpr (G <= 4) {
+        gather_store<G, true>(a, acc, rec, bkv, t);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t == 0)
+            *flag = __hip_atomic_fetch_add(a.unit_cnt + bkv, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == nrec - 1;
+        __syncthreads();
+        if (*flag) {
+            if (nrec <= 8) merge_unit_records<G, T, 8>(a, bkv, nrec, s, t);
+            else if (nrec <= 16) merge_unit_records<G, T, 16>(a, bkv, nrec, s, t);
+            else merge_unit_records<G, T, kFusedMergeMax>(a, bkv, nrec, s, t);
+        }
+    }
 }
 
 // Ascending compaction of a chunk's flagged keys: thread t owns keys 2t and

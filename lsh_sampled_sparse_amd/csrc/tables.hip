@@ -210,10 +210,13 @@ __global__ __launch_bounds__(kBuildThreads) void collide_kernel(
     const float *__restrict__ q, const float *__restrict__ W, int32_t K,
     const uint32_t *__restrict__ off, const uint32_t *__restrict__ ent, int32_t H_q, int32_t H_kv,
     int32_t n, int32_t nwords, int32_t L, int32_t nbins, uint32_t *__restrict__ bits,
-    uint16_t *__restrict__ qcodes, float *__restrict__ qnorm, int32_t slices)
+    uint16_t *__restrict__ qcodes, float *__restrict__ qnorm, int32_t slices,
+    int32_t *__restrict__ cnt, int32_t ncnt)
 {
     extern __shared__ uint32_t sm[];
     __shared__ uint32_t wtot[kBuildThreads / 64];
+    if (blockIdx.x == 0)   // the gather's per-unit record counts start at zero
+        for (int i = threadIdx.x; i < ncnt; i += kBuildThreads) cnt[i] = 0;
     const int bhq = blockIdx.x / slices, sl = blockIdx.x % slices;
     const int l0 = (sl * L) / slices, nl = ((sl + 1) * L) / slices - l0;
     const int t = threadIdx.x;
@@ -325,7 +328,8 @@ constexpr bool table_rows_ahead() { return sizeof(T) == 2 && G > 4; }
 // bitmaps per head (a compile-time count, so that their loads issue together).
 template <int G, typename T, int S>
 __global__ __launch_bounds__(256, (table_occupancy<G, T>())) void table_gather_kernel(DecodeArgs a,
-                                                                                     int32_t nwords)
+                                                                                     int32_t nwords,
+                                                                                     int32_t frec)
 {
     __shared__ uint32_t ulist[kChunk];
     __shared__ int wsum[4];
@@ -425,8 +429,14 @@ __global__ __launch_bounds__(256, (table_occupancy<G, T>())) void table_gather_k
     const T *kb, *vb;
     row_bases<T>(a, bkv, li, kb, vb);
     load_rows<T>(a, kb, vb, ulist, 0, min(kRound, total), chunk, gi, kr, vr);
-    gather_chunk<G, T, table_rows_ahead<G, T>()>(a, gl, ulist, total, chunk, bkv, sq, sqn, smu, kr,
-                                                  vr, t, gi, li);
+    GatherAcc<G> acc;
+    acc.reset();
+    gather_chunk_into<G, T, table_rows_ahead<G, T>()>(a, gl, ulist, total, chunk, bkv, sq, sqn, smu,
+                                                       kr, vr, acc, t, gi, li);
+    if (frec > 0)   // few chunks a unit: the unit's last merges its records here
+        store_count_merge<G, T>(a, acc, chunk, bkv, frec, gl, wsum, t);
+    else
+        gather_store<G>(a, acc, chunk, bkv, t);
 }
 
 template <int G, typename T, int S>
@@ -434,7 +444,7 @@ hipError_t launch_table_gather_t(const DecodeArgs &a, int32_t nwords, hipStream_
 {
     const dim3 grid(a.B * a.H_kv * a.n_chunks);
     return launch_timed(table_gather_kernel<G, T, S>, grid, dim3(256), 0, s, a.ev_begin, a.ev_end,
-                        a, nwords);
+                        a, nwords, fused_merge_records(a, G, 1));
 }
 
 template <int G, int S>
@@ -496,7 +506,8 @@ hipError_t launch_decode_tables(const DecodeArgs &a, hipStream_t s)
     e = launch(plan.own_codes ? collide_kernel<true> : collide_kernel<false>,
                dim3(a.B * a.H_q * plan.slices), dim3(kBuildThreads), lds, s, a.q, a.W, a.K,
                static_cast<const uint32_t *>(a.tab_off), static_cast<const uint32_t *>(a.tab_ent),
-               a.H_q, a.H_kv, a.n, nwords, a.L, 1 << a.K, a.bits, a.qcodes, a.qnorm, plan.slices);
+               a.H_q, a.H_kv, a.n, nwords, a.L, 1 << a.K, a.bits, a.qcodes, a.qnorm, plan.slices,
+               a.unit_cnt, a.unit_cnt ? a.B * a.H_kv : 0);
     if (e != hipSuccess) return e;
     switch (a.G) {
     case 1: e = launch_table_gather<1>(a, nwords, plan.slices, s); break;
@@ -506,7 +517,9 @@ hipError_t launch_decode_tables(const DecodeArgs &a, hipStream_t s)
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    if ((e = launch_merge(a, 1, s)) != hipSuccess) return e;   // a record per chunk
+    // a record per chunk, merged inside table_gather where a unit has few
+    if (fused_merge_records(a, a.G, 1) == 0 && (e = launch_merge(a, 1, s)) != hipSuccess)
+        return e;
     return launch_seg_compact(a, s);
 }
 
