@@ -526,8 +526,8 @@ __global__ __launch_bounds__(256, (scan_occupancy<G, T>())) void scan_gather_ker
                                                 sq[p_slot], sqn[p_slot], smu[p_slot], kraw, vraw,
                                                 acc, t, t >> 4, t & 15);
         if (frec > 0)   // runs aligned with units: this run's one record, merged here
-            store_count_merge<G, T>(a, acc, run - (p_bkv * a.n_chunks) / cpb, p_bkv, frec, gl,
-                                    wsum, t);
+            store_count_merge<G, T, kFusedMergeMax>(a, acc, run - (p_bkv * a.n_chunks) / cpb,
+                                                    p_bkv, frec, gl, wsum, t);
         else
             store_unit(p_bkv, t);
     }
@@ -699,7 +699,7 @@ hipError_t launch_scan_gather_t(const DecodeArgs &a, hipStream_t s, int32_t &cpb
     // timed entry point: the runtime stamps the events at this kernel's own
     // start and end
     return launch_timed(scan_gather_kernel<G, T, KP>, grid, dim3(256), 0, s, a.ev_begin, a.ev_end,
-                        a, cpb, fused_merge_records(a, G, cpb));
+                        a, cpb, fused_merge_records(a, G, cpb, kFusedMergeMax));
 }
 
 template <int G, typename T>
@@ -842,7 +842,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
     }
     if (e != hipSuccess) return e;
     // the merge runs inside scan_gather where runs align with units
-    if (fused_merge_records(a, a.G, cpb) == 0 && (e = launch_merge(a, cpb, s)) != hipSuccess)
+    if (fused_merge_records(a, a.G, cpb, kFusedMergeMax) == 0 &&
+        (e = launch_merge(a, cpb, s)) != hipSuccess)
         return e;
     if ((e = launch_counts(a, s)) != hipSuccess) return e;
     return launch_seg_compact(a, s);

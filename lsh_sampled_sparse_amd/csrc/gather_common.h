@@ -603,7 +603,7 @@ __device__ __forceinline__ void gather_chunk_into(const DecodeArgs &a, GatherLds
 
 // The merge of one unit's records inside the gather kernel (the scan's, or
 // the table path's), by the workgroup that stores the unit's last record
-// (runs aligned with units, at most kFusedMergeMax records, G <= 4).  Each
+// (runs aligned with units, at most kFusedMergeWide records, G <= 4).  Each
 // record was stored with device-scope stores and counted after they
 // completed (s_waitcnt), so device-scope loads here find every record,
 // whichever XCD wrote it.  Wave w takes head g = w: lane r loads the (max,
@@ -617,17 +617,21 @@ __device__ __forceinline__ void merge_unit_records(const DecodeArgs &a, int bkv,
                                                    GatherLds<G, T> &s, int t)
 {
     static_assert(G <= 4 && NR <= kRound, "one (head, pair of dims) a thread, a record a lane");
+    constexpr int kB = NR < 32 ? NR : 32;   // accumulator loads in flight at once
     const int lane = t & 63, g = t >> 6;
     if (g >= G) return;   // the whole wave
     const float *p0 = a.part + int64_t(bkv) * a.n_chunks * (G * kPart) + g * kPart;
-    uint64_t av[NR];
+    uint64_t av[kB];
+    auto load_batch = [&](int r0) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const int rr = min(r, nrec - 1);   // past nrec: re-read the last record, weight 0
-        av[r] = __hip_atomic_load(
-            reinterpret_cast<const uint64_t *>(p0 + int64_t(rr) * (G * kPart) + 2 + 2 * lane),
-            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+        for (int r = 0; r < kB; ++r) {
+            const int rr = min(r0 + r, nrec - 1);   // past nrec: re-read the last, weight 0
+            av[r] = __hip_atomic_load(
+                reinterpret_cast<const uint64_t *>(p0 + int64_t(rr) * (G * kPart) + 2 + 2 * lane),
+                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+    load_batch(0);
     const uint64_t ml = __hip_atomic_load(
         reinterpret_cast<const uint64_t *>(p0 + int64_t(min(lane, nrec - 1)) * (G * kPart)),
         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -638,11 +642,15 @@ __device__ __forceinline__ void merge_unit_records(const DecodeArgs &a, int bkv,
     const float Ls = wave_sum(wr * l);
     if (lane < NR) s.sw[lane][g] = wr;
     float x0 = 0.0f, x1 = 0.0f;
+#pragma unroll 1
+    for (int r0 = 0; r0 < NR; r0 += kB) {   // one batch of loads live at a time
+        if (r0 > 0) load_batch(r0);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const float wg = s.sw[r][g];
-        x0 = fmaf(wg, __uint_as_float(uint32_t(av[r])), x0);
-        x1 = fmaf(wg, __uint_as_float(uint32_t(av[r] >> 32)), x1);
+        for (int r = 0; r < kB; ++r) {
+            const float wg = s.sw[r0 + r][g];
+            x0 = fmaf(wg, __uint_as_float(uint32_t(av[r])), x0);
+            x1 = fmaf(wg, __uint_as_float(uint32_t(av[r] >> 32)), x1);
+        }
     }
     const int b = bkv / a.H_kv, h = bkv % a.H_kv;
     reinterpret_cast<float2 *>(a.out + (int64_t(b) * a.H_q + h * G + g) * kD)[lane] =
@@ -650,18 +658,24 @@ __device__ __forceinline__ void merge_unit_records(const DecodeArgs &a, int bkv,
 }
 
 // Records a unit has when its runs (cpb chunks; 1 on the table path) align
-// with it and there are at most kFusedMergeMax of them, for the fused merge
-// (0: the separate merge kernel runs instead).  The fused merge reads a unit's records on one workgroup,
-// after that unit's last run: at 32 records (16K context) the step is 0.7-0.9
-// us shorter than with the separate kernel, at 4 (batch 16 x 32K) 4-14 us,
-// but at 64 (96K) the one workgroup's 131 KB of reads made scan_gather 3.3 us
-// longer and the step 0.3-0.9 us longer.
-constexpr int kFusedMergeMax = 32;
-inline int fused_merge_records(const DecodeArgs &a, int G, int cpb)
+// with it, for the fused merge, or 0 where the separate merge kernel runs
+// instead.  The fused merge reads a unit's records on one workgroup after
+// that unit's last run.  It takes up to 32 records a unit; at 32 (16K
+// context) the step is 0.7-0.9 us shorter than with the merge kernel, at 4
+// (batch 16 x 32K) 1-3%.  With 64 records and few units (96K: 8) the last
+// workgroups' reads of 131 KB each made scan_gather 3.3 us longer and the
+// step 0.3-0.9 us longer; with 64 and many units (the table path at batch 16:
+// 128) the merges spread over as many CUs and replace a merge kernel of 4,096
+// blocks, so up to 64 are taken there.
+// The code scan takes at most kFusedMergeMax (its runs give more than that
+// only with few units), the table path up to kFusedMergeWide.
+constexpr int kFusedMergeMax = 32, kFusedMergeWide = 64, kFusedWideUnits = 32;
+inline int fused_merge_records(const DecodeArgs &a, int G, int cpb, int max_rec)
 {
     if (G > 4 || !a.unit_cnt || a.n_chunks % cpb != 0) return 0;
     const int nrec = a.n_chunks / cpb;
-    return nrec <= kFusedMergeMax ? nrec : 0;
+    if (nrec <= kFusedMergeMax) return nrec;
+    return nrec <= max_rec && a.B * a.H_kv >= kFusedWideUnits ? nrec : 0;
 }
 
 // A workgroup's record of unit bkv (record rec of nrec), stored so that the
@@ -669,11 +683,12 @@ inline int fused_merge_records(const DecodeArgs &a, int G, int cpb)
 // kernel: device-scope stores, a wait for their completion, then the unit's
 // count (a device-scope add; the counts start at zero).  Every thread calls
 // it; flag is an LDS word.
-template <int G, typename T>
+template <int G, typename T, int kMaxRec>
 __device__ __forceinline__ void store_count_merge(const DecodeArgs &a, const GatherAcc<G> &acc,
                                                   int rec, int bkv, int nrec, GatherLds<G, T> &s,
                                                   int *flag, int t)
 {
+    static_assert(kMaxRec == kFusedMergeMax || kMaxRec == kFusedMergeWide, "a merge width");
     if constexpr (G <= 4) {
         gather_store<G, true>(a, acc, rec, bkv, t);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -685,7 +700,9 @@ __device__ __forceinline__ void store_count_merge(const DecodeArgs &a, const Gat
         if (*flag) {
             if (nrec <= 8) merge_unit_records<G, T, 8>(a, bkv, nrec, s, t);
             else if (nrec <= 16) merge_unit_records<G, T, 16>(a, bkv, nrec, s, t);
-            else merge_unit_records<G, T, kFusedMergeMax>(a, bkv, nrec, s, t);
+            else if (kMaxRec == kFusedMergeMax || nrec <= kFusedMergeMax)
+                merge_unit_records<G, T, kFusedMergeMax>(a, bkv, nrec, s, t);
+            else merge_unit_records<G, T, kMaxRec>(a, bkv, nrec, s, t);
         }
     }
 }

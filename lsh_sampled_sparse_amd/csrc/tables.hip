@@ -434,7 +434,7 @@ __global__ __launch_bounds__(256, (table_occupancy<G, T>())) void table_gather_k
     gather_chunk_into<G, T, table_rows_ahead<G, T>()>(a, gl, ulist, total, chunk, bkv, sq, sqn, smu,
                                                        kr, vr, acc, t, gi, li);
     if (frec > 0)   // few chunks a unit: the unit's last merges its records here
-        store_count_merge<G, T>(a, acc, chunk, bkv, frec, gl, wsum, t);
+        store_count_merge<G, T, kFusedMergeWide>(a, acc, chunk, bkv, frec, gl, wsum, t);
     else
         gather_store<G>(a, acc, chunk, bkv, t);
 }
@@ -444,7 +444,7 @@ hipError_t launch_table_gather_t(const DecodeArgs &a, int32_t nwords, hipStream_
 {
     const dim3 grid(a.B * a.H_kv * a.n_chunks);
     return launch_timed(table_gather_kernel<G, T, S>, grid, dim3(256), 0, s, a.ev_begin, a.ev_end,
-                        a, nwords, fused_merge_records(a, G, 1));
+                        a, nwords, fused_merge_records(a, G, 1, kFusedMergeWide));
 }
 
 template <int G, int S>
@@ -518,7 +518,8 @@ hipError_t launch_decode_tables(const DecodeArgs &a, hipStream_t s)
     }
     if (e != hipSuccess) return e;
     // a record per chunk, merged inside table_gather where a unit has few
-    if (fused_merge_records(a, a.G, 1) == 0 && (e = launch_merge(a, 1, s)) != hipSuccess)
+    if (fused_merge_records(a, a.G, 1, kFusedMergeWide) == 0 &&
+        (e = launch_merge(a, 1, s)) != hipSuccess)
         return e;
     return launch_seg_compact(a, s);
 }

@@ -138,6 +138,9 @@ def test_tiny_config():
     ("K1_L2_min", 1, 4, 1, 520, torch.bfloat16, 1, 2, 4, 16, 0.0),
     ("K0_every_key", 1, 8, 2, 1300, torch.bfloat16, 0, 8, 4, 64, 0.0),
     ("two_level_merge_ragged_group", 1, 8, 2, 17 * 512 + 100, torch.bfloat16, 8, 40, 4, 64, 0.0),
+    # 32 units of 36 chunks: table_gather merges the 36 records of a unit in
+    # the kernel (many units), and the scan its runs' records
+    ("merge_in_kernel_32_units", 2, 32, 16, 35 * 512 + 7, torch.bfloat16, 8, 40, 4, 64, 0.0),
 ])
 def test_small_cases(name, B, H_q, H_kv, n, dtype, K, L, n_sink, n_local, tail):
     print(f"case {name}", flush=True)
