@@ -126,27 +126,19 @@ __device__ __forceinline__ void encode_query_block(const float *__restrict__ q, 
     }
 }
 
-#ifndef MP_ENC_XCD
-#define MP_ENC_XCD 1
-#endif
 // Encode blocks over a 1-D grid: (table block bx < nbx, head block by < nby)
 // of block b.  Workgroups go to the 8 XCDs round-robin by index, so the
 // blocks of one table block (the same W rows, for every head block) are
 // placed on one XCD, b % 8 = bx % 8, and read those rows into its L2 once
 // instead of on every XCD.  The grid then has 8 nby ceil(nbx / 8) blocks;
 // those with bx >= nbx have nothing to do.
-inline int encode_grid(int nbx, int nby) { return MP_ENC_XCD ? 8 * nby * ((nbx + 7) / 8) : nbx * nby; }
+inline int encode_grid(int nbx, int nby) { return 8 * nby * ((nbx + 7) / 8); }
 __device__ __forceinline__ bool encode_coords(int b, int nbx, int nby, int &bx, int &by)
 {
-    if (MP_ENC_XCD) {
-        const int k = b / 8;
-        by = k % nby;
-        bx = 8 * (k / nby) + b % 8;
-        return bx < nbx;
-    }
-    bx = b % nbx;
-    by = b / nbx;
-    return by < nby;
+    const int k = b / 8;
+    by = k % nby;
+    bx = 8 * (k / nby) + b % 8;
+    return bx < nbx;
 }
 
 template <int QH>
@@ -179,8 +171,7 @@ __global__ __launch_bounds__(256) void encode_append_kernel(
     const float *__restrict__ q, int32_t BHq, const float *__restrict__ W, int32_t K, int32_t L,
     uint16_t *__restrict__ qcodes, uint32_t *__restrict__ qq, float *__restrict__ qnorm,
     int32_t nbx, int32_t nby, int32_t n_enc, const T *__restrict__ keys, int64_t sb, int64_t sh,
-    int64_t sn,
-    int32_t H, int32_t n0, int32_t n1, int32_t nc_cap, const float *__restrict__ mu,
+    int64_t sn, int32_t H, int32_t n0, int32_t n1, int32_t nc_cap, const float *__restrict__ mu,
     uint32_t *__restrict__ planes, int32_t nhb, int32_t *__restrict__ cnt, int32_t ncnt)
 {
     __shared__ __align__(16) float sx[kAppendMax][kD];   // the encode's LDS is carved from it
