@@ -138,9 +138,10 @@ def test_tiny_config():
     ("K1_L2_min", 1, 4, 1, 520, torch.bfloat16, 1, 2, 4, 16, 0.0),
     ("K0_every_key", 1, 8, 2, 1300, torch.bfloat16, 0, 8, 4, 64, 0.0),
     ("two_level_merge_ragged_group", 1, 8, 2, 17 * 512 + 100, torch.bfloat16, 8, 40, 4, 64, 0.0),
-    # 32 units of 36 chunks: table_gather merges the 36 records of a unit in
+    # 32 units of 36 and 40 chunks: table_gather merges a unit's records in
     # the kernel (many units), and the scan its runs' records
     ("merge_in_kernel_32_units", 2, 32, 16, 35 * 512 + 7, torch.bfloat16, 8, 40, 4, 64, 0.0),
+    ("merge_in_kernel_32_units_gqa4", 4, 32, 8, 40 * 512 - 3, torch.bfloat16, 8, 40, 4, 64, 0.0),
 ])
 def test_small_cases(name, B, H_q, H_kv, n, dtype, K, L, n_sink, n_local, tail):
     print(f"case {name}", flush=True)
@@ -164,6 +165,31 @@ def test_llama8b_96k_one_layer():
                         cfg.hyperplane_seed(5), cfg.n_sink, cfg.n_local,
                         table_units=[(0, 0), (0, 7)])
     print("llama8b_96k tables", r, flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_batch16_32k_tables_against_the_scan():
+    """The batch-16 workload (128 units of 64 chunks, whose records the
+    table path merges inside table_gather): every head's sampled set and
+    counts capped at 2 equal the code scan's, outputs within 1e-5 of it
+    (the two paths fold the same rows in another order)."""
+    cfg = synth.CONFIGS["batch16_32k"]
+    inp = synth.config_inputs(cfg, device=DEV)
+    k, v, q = inp["k"], inp["v"], inp["q"].contiguous()
+    idx = mp.build_index(k, cfg.K, cfg.L, cfg.hyperplane_seed(0))
+    mp.build_tables(idx)
+    rt = mp.decode_tables_debug(q, idx, k, v, cfg.n_sink, cfg.n_local)
+    rs = mp.decode_debug(q, idx, k, v, cfg.n_sink, cfg.n_local)
+    ot = mp.decode_attn_tables(q, idx, k, v, cfg.n_sink, cfg.n_local)
+    torch.cuda.synchronize()
+    assert torch.equal(rt["out"], ot), "debug and production table decodes differ"
+    assert torch.equal(rt["s_len"], rs["s_len"])
+    assert torch.equal(rt["counts"], torch.minimum(rs["counts"], torch.full_like(rs["counts"], 2)))
+    err = max(row_rel_err(a, b)
+              for a, b in zip(rt["out"].cpu().double().numpy().reshape(-1, 128),
+                              rs["out"].cpu().double().numpy().reshape(-1, 128)))
+    print("batch16 tables vs scan", err, flush=True)
+    assert err <= 1e-5, err
 
 
 @pytest.mark.timeout(600)
