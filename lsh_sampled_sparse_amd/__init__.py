@@ -17,8 +17,8 @@ from . import capi
 from .capi import MPError, MP_CHUNK
 
 __all__ = ["MagicPIGIndex", "build_index", "build_tables", "append_index", "decode_attn",
-           "decode_debug",
-           "decode_attn_tables", "decode_tables_debug", "kv_view", "capi", "MPError", "MP_CHUNK"]
+           "decode_attn_append", "decode_debug", "decode_attn_tables", "decode_tables_debug",
+           "kv_view", "capi", "MPError", "MP_CHUNK"]
 
 _DTYPES = {torch.float32: capi.MP_F32, torch.bfloat16: capi.MP_BF16}
 
@@ -195,7 +195,8 @@ def build_tables(index: MagicPIGIndex, stream=None) -> MagicPIGIndex:
     return index
 
 
-def _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, debug, tables=False):
+def _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, debug, tables=False,
+            append=False):
     if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3:
         raise ValueError("q must be a contiguous [B][H_q][128] float32 tensor")
     B, H_q, d = q.shape
@@ -212,6 +213,15 @@ def _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, debug,
     # must outlive this call's kernels, not just this Python call
     _keep_alive_on(_side_stream(stream, q.device), out, scratch, index.workspace,
                    index.tables if tables else None)
+    if append:
+        capi.mp_decode_attn_append(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local,
+                                   float(scale), out.data_ptr(), scratch.data_ptr(),
+                                   scratch.numel(), s)
+        index.n = k.shape[2]
+        # decodes on other streams may still read the old tables: they were
+        # marked on those streams when the decode was enqueued
+        index.tables = None
+        return out
     if not debug:
         f = capi.mp_decode_attn_tables if tables else capi.mp_decode_attn
         f(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local, float(scale),
@@ -240,24 +250,8 @@ def decode_attn_append(q, index, k, v, n_sink, n_local, scale=0.0, out=None, scr
     """Grow `index` to the keys of k [B][H_kv][n_new][128] and decode over
     them in one call (see mp_decode_attn_append): out [B][H_q][128] fp32.
     Detaches any bucketed tables."""
-    if q.dtype != torch.float32 or not q.is_contiguous() or q.dim() != 3:
-        raise ValueError("q must be a contiguous [B][H_q][128] float32 tensor")
-    B, H_q, d = q.shape
-    if out is None:
-        out = torch.empty(B, H_q, d, dtype=torch.float32, device=q.device)
-    need = index.scratch_bytes(H_q)
-    if need == 0:
-        raise ValueError(f"H_q={H_q} does not fit the index (H_kv={index.H_kv})")
-    if scratch is None:
-        scratch = torch.empty(need, dtype=torch.uint8, device=q.device)
-    kv_k, kv_v = kv_view(k), kv_view(v)
-    _keep_alive_on(_side_stream(stream, q.device), out, scratch, index.workspace)
-    capi.mp_decode_attn_append(q.data_ptr(), H_q, index.handle, kv_k, kv_v, n_sink, n_local,
-                               float(scale), out.data_ptr(), scratch.data_ptr(), scratch.numel(),
-                               _stream(stream))
-    index.n = k.shape[2]
-    index.tables = None
-    return out
+    return _decode(q, index, k, v, n_sink, n_local, scale, out, scratch, stream, False,
+                   append=True)
 
 
 def decode_debug(q, index, k, v, n_sink, n_local, scale=0.0, out=None, scratch=None,
