@@ -1,4 +1,4 @@
-// decode.hip -- one MagicPIG decode step on gfx950: three launches.
+// decode.hip -- one MagicPIG decode step on gfx950: two or three launches.
 //
 //   encode_query   SimHash codes of the raw queries (page "MagicPIG: LSH
 //                  Sampling for Efficient LLM Generation", algorithm steps:
@@ -31,10 +31,14 @@
 //                  query head, from the planes.
 //   merge          log-sum-exp merge of the partial records of every query head
 //                  (system co-design: partial attention outputs are merged
-//                  recursively).  A kernel of its own: its launch boundary is
-//                  what makes the partials of blocks on other XCDs visible,
-//                  which an in-kernel device-scope fence would buy with an L2
-//                  write-back per block.
+//                  recursively).  Where a unit has at most 32 records it runs
+//                  inside scan_gather instead (gather_common.h,
+//                  store_count_merge): records go out with device-scope
+//                  stores and the workgroup that counts a unit's last one
+//                  merges them.  Otherwise a kernel of its own, whose launch
+//                  boundary makes the records of blocks on other XCDs visible
+//                  (one workgroup reading a unit's many records would lengthen
+//                  the scan's tail more than the launch costs).
 #include <hip/hip_ext.h>
 #include <math.h>
 
