@@ -20,7 +20,10 @@
 //                  (seen twice = in one slice, or once in two) give the
 //                  sampled / exact list; gather-SNIS as in the code scan
 //                  (gather_common.h) writes the chunk's partial softmax, which
-//                  the merge of decode.hip combines.
+//                  the merge of decode.hip combines, or, where a unit has few
+//                  chunks (at most 32, or 64 with 32 units or more), the
+//                  workgroup that stores a unit's last one merges in this
+//                  kernel (store_count_merge; collide zeroes the counts).
 #include <hip/hip_ext.h>
 
 #include <algorithm>
