@@ -248,6 +248,20 @@ def test_decode_attn_append_batch2_and_K0():
     _twin_steps(1, 4, 1, torch.bfloat16, 0, 8, 200, [201, 230], 4, 16, seed=29)
 
 
+@pytest.mark.parametrize("n_local,steps", [(0, [701, 702, 703]), (4, [701, 709, 710]),
+                                           (64, [701, 702, 717, 733])])
+def test_decode_attn_append_with_and_without_a_local_window(n_local, steps):
+    """The appended keys' codes must be in the planes before the scan reads
+    them whether or not the new keys are in the exact set T.  From 700 keys:
+    with no local window (every new key is sampled or not by its codes),
+    with 4 local keys (1, then 8 new keys: some outside T), and with 64 (1,
+    1, 15 and 16 new keys, all in T)."""
+    ib, k, v, q = _twin_steps(1, 8, 2, torch.bfloat16, 10, 60, 700, steps, 4, n_local, seed=31,
+                              cap=800)
+    r = check_index(ib, k, v, q, steps[-1], 700, 10, 60, 31, 4, n_local)
+    print("append with n_local", n_local, r, flush=True)
+
+
 def test_decode_attn_append_rejections_leave_the_index():
     k, v, q = _cache(1, 4, 1, 1000, torch.bfloat16, 30)
     idx = mp.build_index(k[:, :, :600], 8, 20, 30, capacity=900)
